@@ -1,0 +1,38 @@
+"""Algorithmic byte counts: the bytes each operator must move, read plus write,
+with every input read once.  Used to turn a kernel time into HBM GB/s.
+
+Fused prologue, per token: q read + written (2 * 2 * H * 512 B), the position
+and the slot index (8 + 8 B), one cos/sin row shared by all heads (64 fp32 =
+256 B); per token whose slot is written: the kv row (1024 B), 448 code bytes,
+the 64 bf16 rotary dims (128 B) and 7 exponent bytes; plus both weight vectors
+once (2 * 1024 B).
+
+Packed Q/K norm+RoPE, per token: the Q and K heads read + written
+(2 * 2 * (Hq + Hk) * D B), the position (8 B) and one cos/sin row (4 * D B);
+the V heads are never touched; plus both weight vectors once (2 * 2 * D B).
+"""
+
+from __future__ import annotations
+
+HEAD_DIM = 512
+ROPE_DIM = 64
+
+
+def dsv4_token_bytes(num_heads: int, slot_written: bool) -> int:
+    b = 4 * num_heads * HEAD_DIM + 8 + 8 + 4 * ROPE_DIM
+    if slot_written:
+        b += 2 * HEAD_DIM + 448 + 2 * ROPE_DIM + 7
+    return b
+
+
+def dsv4_bytes(num_tokens: int, num_heads: int, num_written: int) -> int:
+    return (num_tokens * dsv4_token_bytes(num_heads, False)
+            + num_written * (dsv4_token_bytes(num_heads, True)
+                             - dsv4_token_bytes(num_heads, False))
+            + 2 * 2 * HEAD_DIM)
+
+
+def packed_bytes(num_tokens: int, num_heads_q: int, num_heads_k: int,
+                 head_dim: int) -> int:
+    per_token = 4 * (num_heads_q + num_heads_k) * head_dim + 8 + 4 * head_dim
+    return num_tokens * per_token + 2 * 2 * head_dim

@@ -1,0 +1,133 @@
+"""CPU oracle for the fused attention prologue (test infrastructure only).
+
+Thin ctypes wrapper around ``liboracle.so`` (built from ``oracle.cpp`` by
+``oracle/build.py``).  The oracle is a plain single-threaded double-precision
+statement of the operators; only the tests, the smoke check and the
+CPU-baseline leg of the benchmark may import this package.  It shares no code
+with the GPU library (``fp8_kv_cache_slot_amd``) and never imports it.
+
+Arrays are numpy arrays on the host.  bf16 tensors are passed as ``uint16``
+arrays of their bit patterns; the caller owns every buffer.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "liboracle.so")
+
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        from . import build as _build
+
+        _build.build()
+    lib = ctypes.CDLL(LIB_PATH)
+    P = ctypes.c_void_p
+    I64, I32, D = ctypes.c_int64, ctypes.c_int32, ctypes.c_double
+    lib.oracle_bf16_to_double.argtypes = [ctypes.c_uint16]
+    lib.oracle_bf16_to_double.restype = D
+    lib.oracle_bf16_rne.argtypes = [D]
+    lib.oracle_bf16_rne.restype = ctypes.c_uint16
+    lib.oracle_e4m3_decode.argtypes = [ctypes.c_uint8]
+    lib.oracle_e4m3_decode.restype = D
+    lib.oracle_e4m3_encode.argtypes = [D]
+    lib.oracle_e4m3_encode.restype = ctypes.c_uint8
+    lib.oracle_ue8m0_exponent.argtypes = [D]
+    lib.oracle_ue8m0_exponent.restype = I32
+    lib.oracle_qnorm_rope_kv_quant_insert.argtypes = [
+        P, P, P, P, P, P, P, P, P, I64, I32, I64, D]
+    lib.oracle_qnorm_rope_kv_quant_insert.restype = None
+    lib.oracle_qk_norm_rope_packed.argtypes = [
+        P, I64, I32, I32, I32, I32, D, P, P, P, P]
+    lib.oracle_qk_norm_rope_packed.restype = None
+    _lib = lib
+    return lib
+
+
+def _ptr(a: np.ndarray, dtype, writable=False):
+    if a.dtype != dtype:
+        raise TypeError(f"expected {np.dtype(dtype)}, got {a.dtype}")
+    if not a.flags.c_contiguous:
+        raise ValueError("array must be C-contiguous")
+    if writable and not a.flags.writeable:
+        raise ValueError("array must be writeable")
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+# ---- number formats ---------------------------------------------------------
+
+def bf16_to_double(bits: int) -> float:
+    return _load().oracle_bf16_to_double(int(bits))
+
+
+def bf16_rne(v: float) -> int:
+    return _load().oracle_bf16_rne(float(v))
+
+
+def e4m3_decode(code: int) -> float:
+    return _load().oracle_e4m3_decode(int(code))
+
+
+def e4m3_encode(v: float) -> int:
+    return _load().oracle_e4m3_encode(float(v))
+
+
+def ue8m0_exponent(amax: float) -> int:
+    return _load().oracle_ue8m0_exponent(float(amax))
+
+
+# ---- entry points -----------------------------------------------------------
+
+def qnorm_rope_kv_quant_insert(q, kv, q_weight, kv_weight, cos_sin_cache,
+                               positions, slot_mapping, kv_cache, kv_scale,
+                               eps):
+    """In place on ``q`` (uint16 [T,H,512]), ``kv_cache`` (uint8
+    [pages,64,576]) and ``kv_scale`` (uint8 [pages,64,8])."""
+    T, H, D = q.shape
+    if D != 512 or kv.shape != (T, 512):
+        raise ValueError("q must be [T,H,512] and kv [T,512]")
+    if cos_sin_cache.ndim != 2 or cos_sin_cache.shape[1] != 64:
+        raise ValueError("cos_sin_cache must be [max_position, 64]")
+    if positions.shape != (T,) or slot_mapping.shape != (T,):
+        raise ValueError("positions and slot_mapping must be [T]")
+    pages = kv_cache.shape[0]
+    if kv_cache.shape != (pages, 64, 576) or kv_scale.shape != (pages, 64, 8):
+        raise ValueError("cache must be [pages,64,576], scale [pages,64,8]")
+    if T and (positions.min() < 0 or positions.max() >= cos_sin_cache.shape[0]):
+        raise ValueError("position out of range")
+    _load().oracle_qnorm_rope_kv_quant_insert(
+        _ptr(q, np.uint16, True), _ptr(kv, np.uint16), _ptr(q_weight, np.uint16),
+        _ptr(kv_weight, np.uint16), _ptr(cos_sin_cache, np.float32),
+        _ptr(positions, np.int64), _ptr(slot_mapping, np.int64),
+        _ptr(kv_cache, np.uint8, True), _ptr(kv_scale, np.uint8, True),
+        T, H, pages, float(eps))
+
+
+def qk_norm_rope_packed(qkv, num_heads_q, num_heads_k, num_heads_v, head_dim,
+                        eps, q_weight, k_weight, cos_sin_cache, position_ids):
+    """In place on ``qkv`` (uint16 [T,(Hq+Hk+Hv)*D]); V heads untouched."""
+    T = qkv.shape[0]
+    if qkv.shape[1] != (num_heads_q + num_heads_k + num_heads_v) * head_dim:
+        raise ValueError("qkv width does not match the head counts")
+    if head_dim % 2 or cos_sin_cache.shape[1] != head_dim:
+        raise ValueError("cos_sin_cache must be [max_position, head_dim]")
+    if position_ids.shape != (T,):
+        raise ValueError("position_ids must be [T]")
+    if T and (position_ids.min() < 0
+              or position_ids.max() >= cos_sin_cache.shape[0]):
+        raise ValueError("position out of range")
+    _load().oracle_qk_norm_rope_packed(
+        _ptr(qkv, np.uint16, True), T, num_heads_q, num_heads_k, num_heads_v,
+        head_dim, float(eps), _ptr(q_weight, np.uint16),
+        _ptr(k_weight, np.uint16), _ptr(cos_sin_cache, np.float32),
+        _ptr(position_ids, np.int64))

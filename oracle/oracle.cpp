@@ -1,0 +1,255 @@
+// CPU oracle: TEST INFRASTRUCTURE ONLY (see oracle.h for the sources cited
+// as [P1], [P2], [P3] and for who may load this library).
+//
+// Everything is computed in double; the only roundings are the ones that
+// produce a stored output (bf16 for q and for the rotary part of the cache,
+// E4M3 for the cache codes, an exact integer for the block exponent).
+// No blocking, fusion or reordering: each token, then each head, then each
+// element, in the order the operator is described.
+
+#include "oracle.h"
+
+#include <cfenv>
+#include <cmath>
+#include <cstring>
+
+namespace {
+
+// Geometry of the DeepSeek-V4 prologue.  The head width is fixed by [P1]
+// "Correctness" (16744448 q elements at 511 tokens and 64 heads = 512 per
+// head) and [P2] "What the optimisation does" (64 threads for 512 elements).
+// Rotary width, block width and page size are readings: 64 rotary dims at the
+// end of the head, seven 64-dim quantisation blocks over the first 448 dims
+// ([P1] "Performance": seven per-block exponents per token), 64-slot pages.
+constexpr int kHeadDim = 512;
+constexpr int kRopeDim = 64;
+constexpr int kRopeStart = kHeadDim - kRopeDim;  // 448
+constexpr int kQuantBlock = 64;
+constexpr int kNumBlocks = kRopeStart / kQuantBlock;  // 7
+constexpr int kPageSize = 64;
+constexpr int kRowBytes = kRopeStart + 2 * kRopeDim;  // 576
+constexpr int kScaleBytes = 8;                        // 7 used + 1 reserved
+constexpr double kE4M3Max = 448.0;
+
+// Round a double to the nearest multiple of `quantum` (a power of two), ties
+// to even.  nearbyint honours the current rounding mode, which is forced to
+// round-to-nearest-even around every use.
+double round_to_quantum(double v, double quantum) {
+  return std::nearbyint(v / quantum) * quantum;
+}
+
+struct NearestEven {
+  int saved;
+  NearestEven() : saved(std::fegetround()) { std::fesetround(FE_TONEAREST); }
+  ~NearestEven() { std::fesetround(saved); }
+};
+
+// RMSNorm of one row of n bf16 values with a bf16 weight, all in double:
+//   y_d = x_d / sqrt(mean(x^2) + eps) * w_d
+// Reading: the mean runs over every element of the head (the rotary dims
+// included), eps sits inside the square root and the weight multiplies plainly
+// and before any rotation ([P3] "Summary": the paired element enters the
+// rotation with its own norm weight).
+void rms_norm(const uint16_t* x, const uint16_t* w, int n, double eps,
+              double* y) {
+  double sum_sq = 0.0;
+  for (int d = 0; d < n; ++d) {
+    double v = oracle_bf16_to_double(x[d]);
+    sum_sq += v * v;
+  }
+  double mean_sq = sum_sq / n;
+  double inv_rms = 1.0 / std::sqrt(mean_sq + eps);
+  for (int d = 0; d < n; ++d)
+    y[d] = oracle_bf16_to_double(x[d]) * inv_rms * oracle_bf16_to_double(w[d]);
+}
+
+// Rotation of one pair (a, b) by an angle with cosine c and sine s:
+// a' = a c - b s, b' = b c + a s  (multiplication of a + ib by c + is).
+void rotate_pair(double* a, double* b, double c, double s) {
+  double a0 = *a, b0 = *b;
+  *a = a0 * c - b0 * s;
+  *b = b0 * c + a0 * s;
+}
+
+}  // namespace
+
+extern "C" {
+
+double oracle_bf16_to_double(uint16_t bits) {
+  uint32_t u = static_cast<uint32_t>(bits) << 16;
+  float f;
+  std::memcpy(&f, &u, sizeof f);
+  return static_cast<double>(f);
+}
+
+uint16_t oracle_bf16_rne(double v) {
+  // bf16 keeps 8 significant bits (1 implicit + 7 stored) with the exponent
+  // range of binary32: normals from 2^-126, subnormal spacing 2^-133.
+  if (std::isnan(v)) return 0x7FC0;
+  NearestEven mode;
+  double a = std::fabs(v);
+  double r;
+  if (a == 0.0) {
+    r = 0.0;
+  } else {
+    int k;
+    std::frexp(a, &k);  // a = m * 2^k, m in [0.5, 1): top bit has weight 2^(k-1)
+    int lsb_exp = (k - 1) - 7;
+    if (lsb_exp < -133) lsb_exp = -133;
+    r = round_to_quantum(a, std::ldexp(1.0, lsb_exp));
+  }
+  uint16_t sign = std::signbit(v) ? 0x8000 : 0;
+  if (r >= std::ldexp(1.0, 128)) return sign | 0x7F80;  // overflow to inf
+  float f = static_cast<float>(r);  // exact: r has at most 8 significant bits
+  uint32_t u;
+  std::memcpy(&u, &f, sizeof u);
+  return sign | static_cast<uint16_t>(u >> 16);
+}
+
+double oracle_e4m3_decode(uint8_t code) {
+  // OCP 8-bit floating point, E4M3: sign, 4 exponent bits (bias 7), 3
+  // mantissa bits; exponent field 0 is subnormal; S.1111.111 is NaN.
+  int sign = code >> 7;
+  int exp_field = (code >> 3) & 0xF;
+  int mant = code & 0x7;
+  if (exp_field == 0xF && mant == 0x7) return std::nan("");
+  double mag = exp_field == 0 ? std::ldexp(static_cast<double>(mant), -9)
+                              : std::ldexp(1.0 + mant / 8.0, exp_field - 7);
+  return sign ? -mag : mag;
+}
+
+uint8_t oracle_e4m3_encode(double v) {
+  NearestEven mode;
+  uint8_t sign = std::signbit(v) ? 0x80 : 0x00;
+  double a = std::fabs(v);
+  if (std::isnan(v)) return 0x7F;
+  // Quantum: 2^(E-3) for a normal value in [2^E, 2^(E+1)), E >= -6; the
+  // subnormal range below 2^-6 has the fixed spacing 2^-9.
+  double r;
+  if (a == 0.0) {
+    r = 0.0;
+  } else {
+    int k;
+    std::frexp(a, &k);
+    int top = k - 1;
+    int lsb_exp = (top < -6 ? -6 : top) - 3;
+    r = round_to_quantum(a, std::ldexp(1.0, lsb_exp));
+  }
+  if (r > kE4M3Max) r = kE4M3Max;  // saturate: no infinities in E4M3
+  // Encode the representable magnitude r.
+  uint8_t bits;
+  if (r < std::ldexp(1.0, -6)) {
+    bits = static_cast<uint8_t>(std::ldexp(r, 9));  // subnormal (or zero)
+  } else {
+    int k;
+    double m = std::frexp(r, &k);  // r = m 2^k, m in [0.5, 1)
+    int exp_field = (k - 1) + 7;
+    int mant = static_cast<int>((2.0 * m - 1.0) * 8.0);
+    bits = static_cast<uint8_t>((exp_field << 3) | mant);
+  }
+  return sign | bits;
+}
+
+int32_t oracle_ue8m0_exponent(double amax) {
+  // Smallest integer e with amax <= 448 * 2^e.  Write amax = m 2^k with
+  // m in [0.5, 1) and 448 = 0.875 * 2^9: then amax <= 448 * 2^e exactly when
+  // e >= k - 9 for m <= 0.875 and when e >= k - 8 for m > 0.875.
+  if (amax == 0.0) return -127;
+  int k;
+  double m = std::frexp(amax, &k);
+  int e = k - 9 + (m > 0.875 ? 1 : 0);
+  if (e < -127) e = -127;
+  if (e > 127) e = 127;
+  return e;
+}
+
+void oracle_qnorm_rope_kv_quant_insert(
+    uint16_t* q, const uint16_t* kv, const uint16_t* q_weight,
+    const uint16_t* kv_weight, const float* cos_sin_cache,
+    const int64_t* positions, const int64_t* slot_mapping, uint8_t* kv_cache,
+    uint8_t* kv_scale, int64_t num_tokens, int32_t num_heads,
+    int64_t num_pages, double eps) {
+  const int64_t num_slots = num_pages * kPageSize;
+  double y[kHeadDim];
+  for (int64_t t = 0; t < num_tokens; ++t) {
+    // Interleaved rotary angles of this token's position: pair i rotates
+    // dims (448 + 2i, 449 + 2i) by cos[i], sin[i] (reading: interleaved pairs
+    // on the last 64 dims, cosines before sines in the cache row).
+    const float* row = cos_sin_cache + positions[t] * kRopeDim;
+    const float* cosv = row;
+    const float* sinv = row + kRopeDim / 2;
+
+    // Q: every head is normalised with q_weight, rotated and written back as
+    // bf16 ([P2] "What the optimisation does": a Q slot is normalise and
+    // rotate; [P1] "Correctness": q compared in bf16 ULP).
+    for (int32_t h = 0; h < num_heads; ++h) {
+      uint16_t* qh = q + (t * num_heads + h) * kHeadDim;
+      rms_norm(qh, q_weight, kHeadDim, eps, y);
+      for (int i = 0; i < kRopeDim / 2; ++i)
+        rotate_pair(&y[kRopeStart + 2 * i], &y[kRopeStart + 2 * i + 1],
+                    cosv[i], sinv[i]);
+      for (int d = 0; d < kHeadDim; ++d) qh[d] = oracle_bf16_rne(y[d]);
+    }
+
+    // KV: the single latent head, normalised with kv_weight and rotated the
+    // same way (reading: the norm applies to KV as well as to Q).
+    const int64_t slot = slot_mapping[t];
+    if (slot < 0 || slot >= num_slots) continue;  // skipped token
+    rms_norm(kv + t * kHeadDim, kv_weight, kHeadDim, eps, y);
+    for (int i = 0; i < kRopeDim / 2; ++i)
+      rotate_pair(&y[kRopeStart + 2 * i], &y[kRopeStart + 2 * i + 1], cosv[i],
+                  sinv[i]);
+
+    uint8_t* dst = kv_cache + slot * kRowBytes;
+    uint8_t* scale = kv_scale + slot * kScaleBytes;
+    // Seven UE8M0 power-of-two block scales per token ([P1] "Performance":
+    // the lightop scalar scale "cannot carry seven per-block exponents per
+    // token"), each the smallest power of two that brings the block's
+    // largest magnitude within the E4M3 range.
+    for (int b = 0; b < kNumBlocks; ++b) {
+      double amax = 0.0;
+      for (int d = b * kQuantBlock; d < (b + 1) * kQuantBlock; ++d)
+        amax = std::fmax(amax, std::fabs(y[d]));
+      int32_t e = oracle_ue8m0_exponent(amax);
+      scale[b] = static_cast<uint8_t>(e + 127);
+      for (int d = b * kQuantBlock; d < (b + 1) * kQuantBlock; ++d)
+        dst[d] = oracle_e4m3_encode(std::ldexp(y[d], -e));  // exact scaling
+    }
+    // The rotary dims are kept as bf16 after the codes (reading).
+    for (int j = 0; j < kRopeDim; ++j) {
+      uint16_t bits = oracle_bf16_rne(y[kRopeStart + j]);
+      dst[kRopeStart + 2 * j] = static_cast<uint8_t>(bits & 0xFF);
+      dst[kRopeStart + 2 * j + 1] = static_cast<uint8_t>(bits >> 8);
+    }
+  }
+}
+
+void oracle_qk_norm_rope_packed(
+    uint16_t* qkv, int64_t num_tokens, int32_t num_heads_q,
+    int32_t num_heads_k, int32_t num_heads_v, int32_t head_dim, double eps,
+    const uint16_t* q_weight, const uint16_t* k_weight,
+    const float* cos_sin_cache, const int64_t* position_ids) {
+  const int64_t row_elems =
+      static_cast<int64_t>(num_heads_q + num_heads_k + num_heads_v) * head_dim;
+  const int half = head_dim / 2;
+  double* y = new double[head_dim];
+  for (int64_t t = 0; t < num_tokens; ++t) {
+    const float* row = cos_sin_cache + position_ids[t] * head_dim;
+    const float* cosv = row;
+    const float* sinv = row + half;
+    // Heads are packed [Q heads | K heads | V heads]; Q heads take q_weight
+    // and K heads k_weight; V heads are not touched ([P3] "Summary").
+    for (int32_t h = 0; h < num_heads_q + num_heads_k; ++h) {
+      uint16_t* xh = qkv + t * row_elems + static_cast<int64_t>(h) * head_dim;
+      const uint16_t* w = h < num_heads_q ? q_weight : k_weight;
+      rms_norm(xh, w, head_dim, eps, y);
+      // NeoX pairs (i, i + D/2) over the whole head; each element carries its
+      // own weight into the rotation ([P3] "Summary", paired-weight rule).
+      for (int i = 0; i < half; ++i) rotate_pair(&y[i], &y[i + half], cosv[i], sinv[i]);
+      for (int d = 0; d < head_dim; ++d) xh[d] = oracle_bf16_rne(y[d]);
+    }
+  }
+  delete[] y;
+}
+
+}  // extern "C"

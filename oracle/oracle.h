@@ -1,0 +1,107 @@
+/*
+ * CPU oracle for the fused attention prologue and the packed Q/K norm+RoPE.
+ *
+ * TEST INFRASTRUCTURE ONLY.  This library is a plain, slow, single-threaded
+ * statement of what the two operators compute, evaluated in double precision
+ * with exactly one rounding at every stored output.  Only the test suite, the
+ * smoke check and the CPU-baseline leg of the benchmark may load it.  It shares
+ * no code, header, table or helper with the GPU library and never calls it.
+ *
+ * Sources (cited by page title and section):
+ *   [P1] FlagGems PR #5449 "[KMCompiler][Hygon] Token-tiled
+ *        fused_deepseek_v4_qnorm_rope_kv_rope_quant_insert"
+ *   [P2] FlagGems PR #5321 "[KMCompiler][MetaX][Hygon] Token-tiled
+ *        fused_deepseek_v4_qnorm_rope_kv_rope_quant_insert, plus test and
+ *        benchmark fixes"
+ *   [P3] InfiniOps PR #1019 "FusedQkNormRope"
+ *
+ * The pages name the operator, its inputs and its outputs but never write it
+ * down as formulas; every step below that the pages leave open is marked
+ * "reading" and takes the plainest interpretation consistent with them.
+ *
+ * Every pointer is a host pointer owned by the caller.  bf16 values travel as
+ * their raw 16-bit patterns (uint16_t).  No function allocates, and none
+ * checks its preconditions beyond what is stated.
+ *
+ * Parity pins: every function here is pinned by the CPU test suite against
+ * closed forms, library conversions or brute force; none is "parity unpinned"
+ * except the exact bf16 values of random inputs beyond those properties.
+ */
+#ifndef FP8KV_ORACLE_H
+#define FP8KV_ORACLE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- number formats ---------------------------------------------------- */
+
+/* Exact value of a bf16 bit pattern. */
+double oracle_bf16_to_double(uint16_t bits);
+
+/* bf16 bit pattern nearest to v, ties to even (one rounding from double). */
+uint16_t oracle_bf16_rne(double v);
+
+/* Value of an OCP FP8 E4M3 ("fn": no infinities, 0x7F/0xFF are NaN) code.
+ * NaN codes decode to NaN. */
+double oracle_e4m3_decode(uint8_t code);
+
+/* OCP E4M3 code nearest to v, ties to even, saturating at +-448, sign kept
+ * (a negative value that rounds to zero gives 0x80).  This is the cache's
+ * "fp8e4nv" format named in [P2] "The four test and benchmark fixes". */
+uint8_t oracle_e4m3_encode(double v);
+
+/* UE8M0 block exponent: the smallest integer e with amax <= 448 * 2^e, i.e.
+ * e = ceil(log2(amax / 448)), clamped to [-127, 127]; amax == 0 gives -127
+ * (reading: the closed form is undefined at zero and no epsilon is added).
+ * amax must be >= 0 and finite.  The stored byte is e + 127. */
+int32_t oracle_ue8m0_exponent(double amax);
+
+/* ---- entry 1: fused DeepSeek-V4 attention prologue ----------------------- */
+/*
+ * fused_deepseek_v4_qnorm_rope_kv_rope_quant_insert ([P1], [P2]).
+ *
+ *   q             bf16 [T, H, 512], rewritten in place
+ *   kv            bf16 [T, 512], the single latent KV head of each token
+ *   q_weight      bf16 [512];  kv_weight bf16 [512]
+ *   cos_sin_cache fp32 [max_position, 64]: row p = 32 cosines then 32 sines
+ *   positions     int64 [T], 0 <= positions[t] < max_position (precondition)
+ *   slot_mapping  int64 [T]; a negative slot, or one >= num_pages*64, skips
+ *                 the cache write of that token (q is still rewritten)
+ *   kv_cache      uint8 [num_pages, 64, 576]: 448 E4M3 codes of dims 0..447
+ *                 then dims 448..511 as 64 little-endian bf16
+ *   kv_scale      uint8 [num_pages, 64, 8]: bytes 0..6 = e_b + 127 for the
+ *                 seven 64-dim quantisation blocks; byte 7 is never written
+ *   eps           added to the mean square inside the square root
+ */
+void oracle_qnorm_rope_kv_quant_insert(
+    uint16_t* q, const uint16_t* kv, const uint16_t* q_weight,
+    const uint16_t* kv_weight, const float* cos_sin_cache,
+    const int64_t* positions, const int64_t* slot_mapping, uint8_t* kv_cache,
+    uint8_t* kv_scale, int64_t num_tokens, int32_t num_heads,
+    int64_t num_pages, double eps);
+
+/* ---- entry 2: packed-QKV FusedQkNormRope ([P3] "Summary") ---------------- */
+/*
+ *   qkv           bf16 [T, (Hq + Hk + Hv) * D], Q and K heads rewritten in
+ *                 place, the V heads neither read nor written
+ *   q_weight      bf16 [D] applied to Q heads; k_weight bf16 [D] to K heads
+ *   cos_sin_cache fp32 [max_position, D]: row p = D/2 cosines then D/2 sines
+ *   position_ids  int64 [T], in range (precondition)
+ * Per head: RMSNorm over D with its own weight per element, then NeoX RoPE
+ * over the full head (pairs i, i + D/2), each element entering the rotation
+ * with its own weight already applied.
+ */
+void oracle_qk_norm_rope_packed(
+    uint16_t* qkv, int64_t num_tokens, int32_t num_heads_q,
+    int32_t num_heads_k, int32_t num_heads_v, int32_t head_dim, double eps,
+    const uint16_t* q_weight, const uint16_t* k_weight,
+    const float* cos_sin_cache, const int64_t* position_ids);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FP8KV_ORACLE_H */
