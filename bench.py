@@ -1,0 +1,292 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused DeepSeek-V4 attention prologue on one MI355X.
+
+One step = one call of qnorm_rope_kv_quant_insert over the prefill workload
+(32768 tokens x 64 Q heads x 512, one latent KV head per token, 1024 pages of
+64 slots; 4,356,540,416 algorithmic bytes).  Inputs are seeded synthetic data
+generated on the GPU and resident in HBM before timing starts.
+
+Prints ONE JSON line:
+  value        whole-job HBM throughput in GB/s (algorithmic bytes / time)
+  pct_of_d2d   value as a fraction of a measured 512 MiB device-to-device copy
+               (hipMemcpyAsync, read + write bytes counted)
+  roofline     dominant kernel: algorithmic bytes per launch / mean launch
+               duration (HIP events on the launch stream) against 8 TB/s
+  cpu_baseline the CPU oracle timed on a bounded token slice of the same
+               workload, single-threaded
+  extra        the other workloads (131072 x 64, 32768 x 128, decode and tiny
+               latencies, the packed Q/K norm+RoPE at 8192 tokens)
+
+Usage: python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--quick]
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = ("achieved HBM GB/s & % of measured D2D-copy peak at tokens×heads "
+          "32768×64")
+HBM_PEAK_GBPS = 8000.0
+PROFILE_COUNTERS = os.path.join(ROOT, "profiles",
+                                "dsv4_prologue_prefill_32768x64_counters.json")
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "fp8_kv_cache_slot_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they were
+    taken on the current kernel sources; else None."""
+    try:
+        with open(PROFILE_COUNTERS) as f:
+            c = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if c.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return c.get("traffic_bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--quick", action="store_true",
+                    help="headline workload only (no extras, no CPU baseline)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="target CPU time of the oracle sample")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: the fused prologue is per-token "
+              f"independent and has no cross-GPU step, so --gpus {args.gpus} is "
+              f"not a configuration of this benchmark", file=sys.stderr)
+        sys.exit(2)
+    if args.steps < 1:
+        sys.exit("--steps must be >= 1")
+
+    import torch
+
+    import fp8_kv_cache_slot_amd as K
+    from fp8_kv_cache_slot_amd import accounting as A
+    from fp8_kv_cache_slot_amd import inputs as I
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+    props = torch.cuda.get_device_properties(dev)
+    log(f"device {props.name} {getattr(props, 'gcnArchName', '')}")
+
+    # ---- ceiling: 512 MiB device-to-device copy -----------------------------
+    n = 512 * 2 ** 20
+    src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    times = []
+    for _ in range(20):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        dst.copy_(src)
+        e1.record(stream)
+        e1.synchronize()
+        times.append(e0.elapsed_time(e1) / 1e3)
+    d2d_gbps = 2 * n / statistics.median(times) / 1e9
+    del src, dst
+    log(f"D2D copy ceiling {d2d_gbps:.1f} GB/s")
+
+    def call(x, q, cache, scale):
+        K.qnorm_rope_kv_quant_insert(q, x["kv"], x["q_weight"], x["kv_weight"],
+                                     x["cos_sin_cache"], x["positions"],
+                                     x["slot_mapping"], cache, scale, x["eps"])
+
+    def workload_bytes(w, x):
+        sm = x["slot_mapping"]
+        written = int(((sm >= 0) & (sm < w.num_pages * 64)).sum().item())
+        return A.dsv4_bytes(w.num_tokens, w.num_heads, written)
+
+    def time_launches(fn, steps, warmup):
+        """Run warmup untimed launches, then `steps` launches bracketed by a
+        synchronize on both sides; each launch between its own pair of events
+        on the launch stream.  Returns (total seconds, per-launch seconds)."""
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(steps)]
+        t0 = time.perf_counter()
+        for a, b in ev:
+            a.record(stream)
+            fn()
+            b.record(stream)
+        torch.cuda.synchronize()
+        total = time.perf_counter() - t0
+        per = [a.elapsed_time(b) / 1e3 for a, b in ev]
+        return total, per
+
+    # ---- headline: prefill 32768 x 64 ---------------------------------------
+    w = I.DSV4_WORKLOADS["prefill"]
+    x = I.make_dsv4(w, dev)
+    q, cache, scale = x["q"].clone(), x["kv_cache"].clone(), x["kv_scale"].clone()
+    nbytes = workload_bytes(w, x)
+    total, per = time_launches(lambda: call(x, q, cache, scale), args.steps,
+                               args.warmup)
+    value = nbytes * args.steps / total / 1e9
+    mean_launch = sum(per) / len(per)
+    achieved = nbytes / mean_launch / 1e9
+    log(f"prefill: {value:.1f} GB/s whole-job, kernel {achieved:.1f} GB/s "
+        f"({mean_launch * 1e6:.1f} us/launch), {value / d2d_gbps:.3f} of D2D")
+    traffic = measured_traffic()
+
+    result = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(total / args.steps * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": "fused DeepSeek-V4 prologue, prefill: 32768 tokens x 64 "
+                        "Q heads x 512 (bf16 in/out) + 1 latent KV head -> FP8 "
+                        "E4M3 + 7 UE8M0 exponents into 1024 pages x 64 slots",
+            "tokens": w.num_tokens, "heads": w.num_heads, "head_dim": 512,
+            "rope_dim": 64, "page_size": 64, "num_pages": w.num_pages,
+            "algorithmic_bytes": nbytes, "io_dtype": "bf16 -> bf16 q, fp8 e4m3 kv",
+            "tiling": list(K.get_tiling()),
+            "dispatch_threshold_programs": K.get_dispatch_threshold(),
+        },
+        "pct_of_d2d": round(value / d2d_gbps, 4),
+        "d2d_copy_gbps": round(d2d_gbps, 1),
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBPS, 4),
+            "traffic": traffic,
+            "kernel": "dsv4_prologue_kernel (tiled)",
+            "mean_launch_us": round(mean_launch * 1e6, 2),
+            "median_launch_us": round(statistics.median(per) * 1e6, 2),
+        },
+    }
+    del q, cache, scale
+
+    # ---- CPU baseline: the oracle on a bounded slice of the same workload --
+    if not (args.quick or args.no_cpu_baseline):
+        import numpy as np
+
+        import oracle as O
+
+        def oracle_on(tokens):
+            sl = slice(0, tokens)
+            h = dict(q=I.bits(x["q"][sl]).copy(), kv=I.bits(x["kv"][sl]).copy(),
+                     qw=I.bits(x["q_weight"]), kw=I.bits(x["kv_weight"]),
+                     cs=I.bits(x["cos_sin_cache"]),
+                     pos=I.bits(x["positions"][sl]).copy(),
+                     sm=I.bits(x["slot_mapping"][sl]).copy())
+            c = np.full((w.num_pages, 64, 576), I.CACHE_CANARY, np.uint8)
+            s = np.full((w.num_pages, 64, 8), I.SCALE_CANARY, np.uint8)
+            t0 = time.perf_counter()
+            O.qnorm_rope_kv_quant_insert(h["q"], h["kv"], h["qw"], h["kw"], h["cs"],
+                                         h["pos"], h["sm"], c, s, w.eps)
+            return time.perf_counter() - t0
+
+        probe = 256
+        dt = oracle_on(probe)
+        tokens = int(min(w.num_tokens, max(probe, probe * args.cpu_seconds / dt)))
+        tokens = max(64, tokens // 64 * 64)
+        dt = oracle_on(tokens)
+        sbytes = A.dsv4_bytes(tokens, w.num_heads, tokens)
+        result["cpu_baseline"] = {
+            "value": round(sbytes / dt / 1e9, 4),
+            "unit": "GB/s",
+            "cores": 1,
+            "kind": "oracle",
+            "sample": f"first {tokens} of the 32768 prefill tokens (all 64 heads "
+                      f"+ KV), {dt:.1f} s single-threaded double-precision C++",
+            "seconds": round(dt, 2),
+            "host_cpus": os.cpu_count(),
+        }
+        log(f"cpu oracle: {tokens} tokens in {dt:.1f} s")
+
+    del x
+    torch.cuda.empty_cache()
+
+    # ---- the other workloads -------------------------------------------------
+    if not args.quick:
+        extra = {}
+        for name in ("long64", "wide128"):
+            wl = I.DSV4_WORKLOADS[name]
+            xx = I.make_dsv4(wl, dev)
+            qq, cc, ss = xx["q"].clone(), xx["kv_cache"].clone(), xx["kv_scale"].clone()
+            nb = workload_bytes(wl, xx)
+            tot, per = time_launches(lambda: call(xx, qq, cc, ss), 20, 3)
+            m = statistics.median(per)
+            extra[name] = {"tokens": wl.num_tokens, "heads": wl.num_heads,
+                           "bytes": nb, "median_us": round(m * 1e6, 1),
+                           "gbps": round(nb / m / 1e9, 1),
+                           "pct_of_d2d": round(nb / m / 1e9 / d2d_gbps, 4)}
+            log(f"{name}: {extra[name]}")
+            del xx, qq, cc, ss
+            torch.cuda.empty_cache()
+        for name in ("tiny", "decode"):
+            wl = I.DSV4_WORKLOADS[name]
+            xx = I.make_dsv4(wl, dev)
+            qq, cc, ss = xx["q"].clone(), xx["kv_cache"].clone(), xx["kv_scale"].clone()
+            nb = workload_bytes(wl, xx)
+            tot, per = time_launches(lambda: call(xx, qq, cc, ss), 50, 10)
+            m = statistics.median(per)
+            extra[name] = {"tokens": wl.num_tokens, "heads": wl.num_heads,
+                           "bytes": nb, "median_us": round(m * 1e6, 2),
+                           "gbps": round(nb / m / 1e9, 1)}
+            log(f"{name}: {extra[name]}")
+        pw = I.PACKED_WORKLOADS["packed_t8192"]
+        px = I.make_packed(pw, dev)
+        qkv = px["qkv"].clone()
+
+        def pcall():
+            K.qk_norm_rope_packed(qkv, pw.num_heads_q, pw.num_heads_k,
+                                  pw.num_heads_v, pw.head_dim, pw.eps,
+                                  px["q_weight"], px["k_weight"],
+                                  px["cos_sin_cache"], True, px["position_ids"])
+        tot, per = time_launches(pcall, 50, 10)
+        m = statistics.median(per)
+        nb = A.packed_bytes(pw.num_tokens, pw.num_heads_q, pw.num_heads_k, pw.head_dim)
+        extra["packed_t8192"] = {"tokens": pw.num_tokens, "heads": "16q/8k/8v x 128",
+                                 "bytes": nb, "median_us": round(m * 1e6, 2),
+                                 "gbps": round(nb / m / 1e9, 1)}
+        log(f"packed_t8192: {extra['packed_t8192']}")
+        result["extra"] = extra
+
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,189 @@
+"""fp8_kv_cache_slot_amd — fused DeepSeek-V4 attention prologue (Q/KV RMSNorm,
+RoPE, FP8 E4M3 + UE8M0 blockwise quantisation and paged-cache insert) and the
+packed-QKV Q/K norm+RoPE, as hand-written HIP kernels for MI355X (gfx950).
+
+This module is the thin Python binding of ``libfp8kv.so``: it checks that the
+torch tensors it is given are device tensors of the right dtype and shape,
+passes their device pointers, sizes and the current HIP stream to the C ABI
+declared in ``include/fp8kv.h``, and raises on a non-zero status.  Every step
+of the computation runs in the library's kernels; there is no fallback.  If
+the library has not been built the first call raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libfp8kv.so")
+
+HEAD_DIM = 512
+ROPE_DIM = 64
+PAGE_SIZE = 64
+ROW_BYTES = 576
+SCALE_BYTES = 8
+PACKED_HEAD_DIM = 128
+
+STATUS = {0: "FP8KV_OK", 1: "FP8KV_ERR_NULL", 2: "FP8KV_ERR_SHAPE",
+          3: "FP8KV_ERR_UNSUPPORTED", 4: "FP8KV_ERR_ALIGN",
+          5: "FP8KV_ERR_DEVICE", 6: "FP8KV_ERR_LAUNCH"}
+
+EXPORTED = ["qnorm_rope_kv_quant_insert", "qk_norm_rope_packed",
+            "fp8kv_status_string", "fp8kv_abi_version",
+            "fp8kv_set_dispatch_threshold", "fp8kv_get_dispatch_threshold",
+            "fp8kv_set_tiling", "fp8kv_get_tiling"]
+
+
+class Fp8kvError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {STATUS.get(status, status)} "
+                         f"({lib().fp8kv_status_string(status).decode()})")
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded ``libfp8kv.so`` with argument types declared."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(
+            f"{LIB_PATH} is not built; run `python -m fp8_kv_cache_slot_amd.build`"
+            " (the HIP kernels are the only implementation)")
+    L = ctypes.CDLL(LIB_PATH)
+    P, I32, I64, F = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float
+    L.qnorm_rope_kv_quant_insert.argtypes = [
+        P, P, P, P, P, P, P, P, P, I64, I32, I32, I32, I64, I64, I32, F, P]
+    L.qnorm_rope_kv_quant_insert.restype = ctypes.c_int
+    L.qk_norm_rope_packed.argtypes = [
+        P, I64, I32, I32, I32, I32, F, P, P, P, I32, P, I32, I64, P]
+    L.qk_norm_rope_packed.restype = ctypes.c_int
+    L.fp8kv_status_string.argtypes = [ctypes.c_int]
+    L.fp8kv_status_string.restype = ctypes.c_char_p
+    L.fp8kv_abi_version.argtypes = []
+    L.fp8kv_abi_version.restype = ctypes.c_int
+    L.fp8kv_set_dispatch_threshold.argtypes = [I64]
+    L.fp8kv_set_dispatch_threshold.restype = ctypes.c_int
+    L.fp8kv_get_dispatch_threshold.argtypes = []
+    L.fp8kv_get_dispatch_threshold.restype = I64
+    L.fp8kv_set_tiling.argtypes = [I32, I32]
+    L.fp8kv_set_tiling.restype = ctypes.c_int
+    L.fp8kv_get_tiling.argtypes = [ctypes.POINTER(I32), ctypes.POINTER(I32)]
+    L.fp8kv_get_tiling.restype = None
+    _lib = L
+    return L
+
+
+def _check(t: torch.Tensor, name: str, dtype, shape=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a device tensor, got {t.device}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+def qnorm_rope_kv_quant_insert(q, kv, q_weight, kv_weight, cos_sin_cache,
+                               positions, slot_mapping, kv_cache, kv_scale,
+                               eps: float = 1e-6, stream=None) -> None:
+    """Fused DeepSeek-V4 prologue, in place on ``q`` (bf16 [T,H,512]),
+    ``kv_cache`` (uint8 [pages,64,576]) and ``kv_scale`` (uint8
+    [pages,64,8]).  See ``include/fp8kv.h`` for the exact semantics."""
+    if q.dim() != 3:
+        raise ValueError("q must be [T, H, 512]")
+    T, H, D = q.shape
+    _check(q, "q", torch.bfloat16)
+    _check(kv, "kv", torch.bfloat16, (T, D))
+    _check(q_weight, "q_weight", torch.bfloat16, (D,))
+    _check(kv_weight, "kv_weight", torch.bfloat16, (D,))
+    _check(cos_sin_cache, "cos_sin_cache", torch.float32)
+    if cos_sin_cache.dim() != 2:
+        raise ValueError("cos_sin_cache must be [max_position, rope_dim]")
+    _check(positions, "positions", torch.int64, (T,))
+    _check(slot_mapping, "slot_mapping", torch.int64, (T,))
+    _check(kv_cache, "kv_cache", torch.uint8)
+    if kv_cache.dim() != 3:
+        raise ValueError("kv_cache must be [num_pages, page_size, 576]")
+    pages, page_size, row = kv_cache.shape
+    if row != ROW_BYTES:
+        raise ValueError("kv_cache rows must be 576 bytes")
+    _check(kv_scale, "kv_scale", torch.uint8, (pages, page_size, SCALE_BYTES))
+    st = lib().qnorm_rope_kv_quant_insert(
+        q.data_ptr(), kv.data_ptr(), q_weight.data_ptr(), kv_weight.data_ptr(),
+        cos_sin_cache.data_ptr(), positions.data_ptr(), slot_mapping.data_ptr(),
+        kv_cache.data_ptr(), kv_scale.data_ptr(), T, H, D,
+        cos_sin_cache.shape[1], cos_sin_cache.shape[0], pages, page_size,
+        float(eps), _stream(stream))
+    if st:
+        raise Fp8kvError(st, "qnorm_rope_kv_quant_insert")
+
+
+def qk_norm_rope_packed(qkv, num_heads_q: int, num_heads_k: int,
+                        num_heads_v: int, head_dim: int, eps: float, q_weight,
+                        k_weight, cos_sin_cache, is_neox: bool, position_ids,
+                        forced_token_heads_per_warp: int = -1,
+                        stream=None) -> None:
+    """Packed-QKV Q/K RMSNorm + NeoX RoPE in place on ``qkv`` (bf16
+    [T,(Hq+Hk+Hv)*D]); V heads untouched.  Parameter order as vLLM's
+    fused_qk_norm_rope."""
+    if qkv.dim() != 2:
+        raise ValueError("qkv must be [T, (Hq+Hk+Hv)*D]")
+    T = qkv.shape[0]
+    _check(qkv, "qkv", torch.bfloat16,
+           (T, (num_heads_q + num_heads_k + num_heads_v) * head_dim))
+    _check(q_weight, "q_weight", torch.bfloat16, (head_dim,))
+    _check(k_weight, "k_weight", torch.bfloat16, (head_dim,))
+    _check(cos_sin_cache, "cos_sin_cache", torch.float32)
+    if cos_sin_cache.dim() != 2 or cos_sin_cache.shape[1] != head_dim:
+        raise ValueError("cos_sin_cache must be [max_position, head_dim]")
+    _check(position_ids, "position_ids", torch.int64, (T,))
+    st = lib().qk_norm_rope_packed(
+        qkv.data_ptr(), T, num_heads_q, num_heads_k, num_heads_v, head_dim,
+        float(eps), q_weight.data_ptr(), k_weight.data_ptr(),
+        cos_sin_cache.data_ptr(), int(bool(is_neox)), position_ids.data_ptr(),
+        int(forced_token_heads_per_warp), cos_sin_cache.shape[0],
+        _stream(stream))
+    if st:
+        raise Fp8kvError(st, "qk_norm_rope_packed")
+
+
+def set_dispatch_threshold(programs: int) -> None:
+    lib().fp8kv_set_dispatch_threshold(int(programs))
+
+
+def get_dispatch_threshold() -> int:
+    return lib().fp8kv_get_dispatch_threshold()
+
+
+def set_tiling(waves_per_block: int, slots_per_wave: int) -> None:
+    st = lib().fp8kv_set_tiling(int(waves_per_block), int(slots_per_wave))
+    if st:
+        raise Fp8kvError(st, "set_tiling")
+
+
+def get_tiling():
+    w, s = ctypes.c_int32(), ctypes.c_int32()
+    lib().fp8kv_get_tiling(ctypes.byref(w), ctypes.byref(s))
+    return w.value, s.value
+
+
+def abi_version() -> int:
+    return lib().fp8kv_abi_version()

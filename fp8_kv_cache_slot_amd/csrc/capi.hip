@@ -1,0 +1,159 @@
+// C ABI of libfp8kv.so (declared in include/fp8kv.h): argument validation on
+// the host, a cached gfx950 device check, the program-count dispatch between
+// the small-batch and the tiled prologue kernels, and the launches.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstdint>
+#include <cstring>
+
+#include "fp8kv.h"
+#include "prologue_launch.hpp"
+#include "validate.hpp"
+
+#define FP8KV_API extern "C" __attribute__((visibility("default")))
+
+namespace fp8kv {
+namespace {
+
+// Programs = num_tokens * (num_heads + 1) below which the small-batch kernel
+// runs (the quantity FlagGems PR #5449 "Dispatch threshold" dispatches on);
+// the value is the crossover measured on MI355X.
+constexpr int64_t kDefaultThreshold = 4096;
+constexpr int kDefaultWaves = 4;
+constexpr int kDefaultSlots = 4;
+
+std::atomic<int64_t> g_threshold{kDefaultThreshold};
+std::atomic<int32_t> g_tiling{(kDefaultWaves << 16) | kDefaultSlots};
+
+constexpr int kMaxDevices = 64;
+std::atomic<int8_t> g_device_ok[kMaxDevices];  // 0 unknown, 1 gfx950, 2 other
+
+int check_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+    return FP8KV_ERR_DEVICE;
+  int8_t state = g_device_ok[dev].load(std::memory_order_relaxed);
+  if (state == 0) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return FP8KV_ERR_DEVICE;
+    state = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+    g_device_ok[dev].store(state, std::memory_order_relaxed);
+  }
+  return state == 1 ? FP8KV_OK : FP8KV_ERR_DEVICE;
+}
+
+}  // namespace
+}  // namespace fp8kv
+
+FP8KV_API int qnorm_rope_kv_quant_insert(
+    void* q, const void* kv, const void* q_weight, const void* kv_weight,
+    const float* cos_sin_cache, const int64_t* positions,
+    const int64_t* slot_mapping, uint8_t* kv_cache, uint8_t* kv_scale,
+    int64_t num_tokens, int32_t num_heads, int32_t head_dim, int32_t rope_dim,
+    int64_t max_position, int64_t num_pages, int32_t page_size, float eps,
+    void* stream) {
+  using namespace fp8kv;
+  int st = validate_prologue(q, kv, q_weight, kv_weight, cos_sin_cache,
+                             positions, slot_mapping, kv_cache, kv_scale,
+                             num_tokens, num_heads, head_dim, rope_dim,
+                             max_position, num_pages, page_size);
+  if (st != FP8KV_OK || num_tokens == 0) return st;
+  st = check_device();
+  if (st != FP8KV_OK) return st;
+
+  PrologueArgs a;
+  a.q = static_cast<uint16_t*>(q);
+  a.kv = static_cast<const uint16_t*>(kv);
+  a.q_weight = static_cast<const uint16_t*>(q_weight);
+  a.kv_weight = static_cast<const uint16_t*>(kv_weight);
+  a.cos_sin = cos_sin_cache;
+  a.positions = positions;
+  a.slot_mapping = slot_mapping;
+  a.kv_cache = kv_cache;
+  a.kv_scale = kv_scale;
+  a.num_tokens = static_cast<int32_t>(num_tokens);
+  a.num_heads = num_heads;
+  a.num_cache_slots = num_pages * kPageSize;
+  a.max_position = max_position;
+  a.eps = eps;
+
+  const int64_t programs = num_tokens * (static_cast<int64_t>(num_heads) + 1);
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (programs < g_threshold.load(std::memory_order_relaxed))
+    return launch_prologue(a, 1, 1, s);
+  const int32_t tiling = g_tiling.load(std::memory_order_relaxed);
+  return launch_prologue(a, tiling >> 16, tiling & 0xFFFF, s);
+}
+
+FP8KV_API int qk_norm_rope_packed(
+    void* qkv, int64_t num_tokens, int32_t num_heads_q, int32_t num_heads_k,
+    int32_t num_heads_v, int32_t head_dim, float eps, const void* q_weight,
+    const void* k_weight, const float* cos_sin_cache, int32_t is_neox,
+    const int64_t* position_ids, int32_t forced_token_heads_per_warp,
+    int64_t max_position, void* stream) {
+  using namespace fp8kv;
+  int st = validate_packed(qkv, num_tokens, num_heads_q, num_heads_k,
+                           num_heads_v, head_dim, q_weight, k_weight,
+                           cos_sin_cache, is_neox, position_ids,
+                           forced_token_heads_per_warp, max_position);
+  if (st != FP8KV_OK || num_tokens == 0) return st;
+  st = check_device();
+  if (st != FP8KV_OK) return st;
+  PackedArgs a;
+  a.qkv = static_cast<uint16_t*>(qkv);
+  a.q_weight = static_cast<const uint16_t*>(q_weight);
+  a.k_weight = static_cast<const uint16_t*>(k_weight);
+  a.cos_sin = cos_sin_cache;
+  a.position_ids = position_ids;
+  a.num_tokens = static_cast<int32_t>(num_tokens);
+  a.num_heads_q = num_heads_q;
+  a.num_heads_k = num_heads_k;
+  a.row_elems = (num_heads_q + num_heads_k + num_heads_v) * kPackedHeadDim;
+  a.max_position = max_position;
+  a.eps = eps;
+  return launch_packed(a, static_cast<hipStream_t>(stream));
+}
+
+FP8KV_API const char* fp8kv_status_string(int status) {
+  switch (status) {
+    case FP8KV_OK: return "ok";
+    case FP8KV_ERR_NULL: return "a required pointer is NULL";
+    case FP8KV_ERR_SHAPE: return "invalid or too large size argument";
+    case FP8KV_ERR_UNSUPPORTED: return "unsupported layout parameter";
+    case FP8KV_ERR_ALIGN: return "pointer not aligned as required";
+    case FP8KV_ERR_DEVICE: return "no current HIP device or device is not gfx950";
+    case FP8KV_ERR_LAUNCH: return "kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+FP8KV_API int fp8kv_abi_version(void) { return FP8KV_ABI_VERSION; }
+
+FP8KV_API int fp8kv_set_dispatch_threshold(int64_t programs) {
+  fp8kv::g_threshold.store(programs < 0 ? fp8kv::kDefaultThreshold : programs,
+                           std::memory_order_relaxed);
+  return FP8KV_OK;
+}
+
+FP8KV_API int64_t fp8kv_get_dispatch_threshold(void) {
+  return fp8kv::g_threshold.load(std::memory_order_relaxed);
+}
+
+FP8KV_API int fp8kv_set_tiling(int32_t waves_per_block, int32_t slots_per_wave) {
+  if (waves_per_block == 0 && slots_per_wave == 0) {
+    waves_per_block = fp8kv::kDefaultWaves;
+    slots_per_wave = fp8kv::kDefaultSlots;
+  }
+  if (!fp8kv::prologue_shape_built(waves_per_block, slots_per_wave))
+    return FP8KV_ERR_UNSUPPORTED;
+  fp8kv::g_tiling.store((waves_per_block << 16) | slots_per_wave,
+                        std::memory_order_relaxed);
+  return FP8KV_OK;
+}
+
+FP8KV_API void fp8kv_get_tiling(int32_t* waves_per_block, int32_t* slots_per_wave) {
+  const int32_t t = fp8kv::g_tiling.load(std::memory_order_relaxed);
+  if (waves_per_block) *waves_per_block = t >> 16;
+  if (slots_per_wave) *slots_per_wave = t & 0xFFFF;
+}

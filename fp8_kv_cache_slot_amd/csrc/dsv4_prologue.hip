@@ -1,0 +1,232 @@
+// Fused DeepSeek-V4 attention prologue for gfx950:
+//   Q heads:  RMSNorm (q_weight) + interleaved RoPE on dims 448..511, in place
+//   KV head:  RMSNorm (kv_weight) + RoPE, dims 0..447 quantised to FP8 E4M3 in
+//             seven 64-dim blocks with UE8M0 exponents, dims 448..511 kept as
+//             bf16, written to the paged cache row slot_mapping[t]
+// (FlagGems PR #5449 / #5321, "Performance" and "What the optimisation does").
+//
+// Layout of the work.  A 512-element bf16 head is exactly one 16-byte vector
+// per lane of a 64-lane wave, so every load and store is a fully coalesced
+// 1 KiB wave access.  Blocks are uniformly KV or Q, as in the pages' tiled
+// design (no divergence between the two paths):
+//   blocks [0, kv_blocks)       one KV row per wave
+//   blocks [kv_blocks, ...)     one wave = QS consecutive heads of one token
+// Each Q wave issues its QS head loads before any arithmetic so QS KiB are in
+// flight per wave, reads the token's position and its cos/sin row once, and
+// reduces the sum of squares across the wave with DPP row steps and four
+// v_readlane of the row totals.  The rotary dims 448..511 sit in lanes 56..63, eight values (four
+// interleaved pairs) per lane, so rotation never leaves the register file.
+// The KV quantisation block of dims 64b..64b+63 is the lane group 8b..8b+7:
+// its absolute maximum is three DPP steps.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "prologue_launch.hpp"
+#include "wave_ops.hpp"
+
+namespace fp8kv {
+namespace {
+
+constexpr int kRopeLane0 = 56;  // first lane holding a rotary dim (448 / 8)
+
+// Normalise one head held as 8 bf16 per lane: y = x / rms(x) * w (fp32).
+__device__ __forceinline__ void rms_normalise(u32x4_t x, const float* w,
+                                              float eps, float* y) {
+  float f[8];
+  unpack8(x, f);
+  const float ss = wave64_sum(sum_sq8(f));
+  const float r = __builtin_amdgcn_rsqf(fmaf(ss, 1.0f / 512.0f, eps));
+#pragma unroll
+  for (int j = 0; j < 8; ++j) y[j] = f[j] * r * w[j];
+}
+
+// Interleaved rotation of the four pairs a lane of 56..63 holds.
+__device__ __forceinline__ void rotate4(float* y, f32x4_t c, f32x4_t s) {
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const float a = y[2 * k], b = y[2 * k + 1];
+    y[2 * k] = a * c[k] - b * s[k];
+    y[2 * k + 1] = b * c[k] + a * s[k];
+  }
+}
+
+// Smallest e with amax <= 448 * 2^e, clamped to [-127, 127]; 0 -> -127.
+// Exact: amax = m 2^k with m in [0.5, 1) and 448 = 0.875 2^9.
+__device__ __forceinline__ int ue8m0_exponent(float amax) {
+  if (!(amax > 0.0f)) return -127;
+  const int k = __builtin_amdgcn_frexp_expf(amax);
+  const float m = __builtin_amdgcn_frexp_mantf(amax);
+  int e = k - 9 + (m > 0.875f ? 1 : 0);
+  e = e < -127 ? -127 : e;
+  return e > 127 ? 127 : e;
+}
+
+template <bool NT>
+__device__ __forceinline__ void kv_row(
+    int32_t t, const uint16_t* __restrict__ kv,
+    const uint16_t* __restrict__ kv_weight, const float* __restrict__ cos_sin,
+    const int64_t* __restrict__ positions,
+    const int64_t* __restrict__ slot_mapping, uint8_t* __restrict__ kv_cache,
+    uint8_t* __restrict__ kv_scale, int64_t num_cache_slots,
+    int64_t max_position, float eps) {
+  const int lane = lane_id();
+  const int64_t slot = slot_mapping[t];
+  if (slot < 0 || slot >= num_cache_slots) return;  // skipped token
+  const int64_t pos = positions[t];
+  if (pos < 0 || pos >= max_position) return;
+
+  const u32x4_t x = load16<NT>(kv + static_cast<int64_t>(t) * 512 + lane * 8);
+  float w[8];
+  unpack8(load16<false>(kv_weight + lane * 8), w);
+  f32x4_t c = {1.f, 1.f, 1.f, 1.f}, s = {0.f, 0.f, 0.f, 0.f};
+  if (lane >= kRopeLane0) {
+    const float* row = cos_sin + pos * 64 + (lane - kRopeLane0) * 4;
+    c = load16f(row);
+    s = load16f(row + 32);
+  }
+  float y[8];
+  rms_normalise(x, w, eps, y);
+  if (lane >= kRopeLane0) rotate4(y, c, s);
+
+  float amax = 0.0f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(y[j]));
+  amax = group8_max(amax);
+  const int e = ue8m0_exponent(amax);
+
+  uint8_t* row = kv_cache + slot * 576;
+  if (lane < kRopeLane0) {
+    float v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = __builtin_ldexpf(y[j], -e);  // exact
+    uint32_t lo = __builtin_amdgcn_cvt_pk_fp8_f32(v[0], v[1], 0, false);
+    lo = __builtin_amdgcn_cvt_pk_fp8_f32(v[2], v[3], lo, true);
+    uint32_t hi = __builtin_amdgcn_cvt_pk_fp8_f32(v[4], v[5], 0, false);
+    hi = __builtin_amdgcn_cvt_pk_fp8_f32(v[6], v[7], hi, true);
+    *reinterpret_cast<u32x2_t*>(row + lane * 8) = u32x2_t{lo, hi};
+    if ((lane & 7) == 0)
+      kv_scale[slot * 8 + (lane >> 3)] = static_cast<uint8_t>(e + 127);
+  } else {
+    u32x4_t o = {pack_bf16(y[0], y[1]), pack_bf16(y[2], y[3]),
+                 pack_bf16(y[4], y[5]), pack_bf16(y[6], y[7])};
+    store16<false>(row + 448 + (lane - kRopeLane0) * 16, o);
+  }
+}
+
+template <int WAVES, int QS, bool NT>
+__global__ void __launch_bounds__(WAVES * 64) dsv4_prologue_kernel(
+    uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
+    const uint16_t* __restrict__ q_weight,
+    const uint16_t* __restrict__ kv_weight, const float* __restrict__ cos_sin,
+    const int64_t* __restrict__ positions,
+    const int64_t* __restrict__ slot_mapping, uint8_t* __restrict__ kv_cache,
+    uint8_t* __restrict__ kv_scale, int32_t num_tokens, int32_t num_heads,
+    int32_t waves_per_token, int32_t kv_blocks, int64_t num_cache_slots,
+    int64_t max_position, float eps) {
+  const int lane = lane_id();
+  const int wave = wave_id();
+  int32_t b = blockIdx.x;
+  if (b < kv_blocks) {
+    const int32_t t = b * WAVES + wave;
+    if (t < num_tokens)
+      kv_row<NT>(t, kv, kv_weight, cos_sin, positions, slot_mapping, kv_cache,
+                 kv_scale, num_cache_slots, max_position, eps);
+    return;
+  }
+  b -= kv_blocks;
+  const int32_t qwave = b * WAVES + wave;
+  const int32_t t = qwave / waves_per_token;
+  if (t >= num_tokens) return;
+  const int32_t h0 = (qwave - t * waves_per_token) * QS;
+  const int64_t pos = positions[t];
+  if (pos < 0 || pos >= max_position) return;
+
+  // Issue every load of this wave before any arithmetic.
+  uint16_t* base = q + (static_cast<int64_t>(t) * num_heads + h0) * 512 + lane * 8;
+  u32x4_t x[QS];
+#pragma unroll
+  for (int s = 0; s < QS; ++s) {
+    // heads past the last one re-read head h0 (in bounds) and are not stored
+    const int off = (h0 + s < num_heads) ? s * 512 : 0;
+    x[s] = load16<NT>(base + off);
+  }
+  float w[8];
+  unpack8(load16<false>(q_weight + lane * 8), w);
+  f32x4_t c = {1.f, 1.f, 1.f, 1.f}, sn = {0.f, 0.f, 0.f, 0.f};
+  if (lane >= kRopeLane0) {
+    const float* row = cos_sin + pos * 64 + (lane - kRopeLane0) * 4;
+    c = load16f(row);
+    sn = load16f(row + 32);
+  }
+
+#pragma unroll
+  for (int s = 0; s < QS; ++s) {
+    if (h0 + s >= num_heads) break;
+    float y[8];
+    rms_normalise(x[s], w, eps, y);
+    if (lane >= kRopeLane0) rotate4(y, c, sn);
+    u32x4_t o = {pack_bf16(y[0], y[1]), pack_bf16(y[2], y[3]),
+                 pack_bf16(y[4], y[5]), pack_bf16(y[6], y[7])};
+    store16<NT>(base + s * 512, o);
+  }
+}
+
+template <int WAVES, int QS, bool NT>
+int launch(const PrologueArgs& a, hipStream_t stream) {
+  const int32_t waves_per_token = (a.num_heads + QS - 1) / QS;
+  const int64_t kv_blocks = (static_cast<int64_t>(a.num_tokens) + WAVES - 1) / WAVES;
+  const int64_t q_waves = static_cast<int64_t>(a.num_tokens) * waves_per_token;
+  const int64_t q_blocks = (q_waves + WAVES - 1) / WAVES;
+  const int64_t blocks = kv_blocks + q_blocks;
+  if (blocks > 0x7FFFFFFF) return FP8KV_ERR_SHAPE;
+  int32_t kvb = static_cast<int32_t>(kv_blocks);
+  void* args[] = {
+      const_cast<uint16_t**>(&a.q),          const_cast<const uint16_t**>(&a.kv),
+      const_cast<const uint16_t**>(&a.q_weight),
+      const_cast<const uint16_t**>(&a.kv_weight),
+      const_cast<const float**>(&a.cos_sin),
+      const_cast<const int64_t**>(&a.positions),
+      const_cast<const int64_t**>(&a.slot_mapping),
+      const_cast<uint8_t**>(&a.kv_cache),    const_cast<uint8_t**>(&a.kv_scale),
+      const_cast<int32_t*>(&a.num_tokens),   const_cast<int32_t*>(&a.num_heads),
+      const_cast<int32_t*>(&waves_per_token), &kvb,
+      const_cast<int64_t*>(&a.num_cache_slots),
+      const_cast<int64_t*>(&a.max_position), const_cast<float*>(&a.eps)};
+  hipError_t err = hipLaunchKernel(
+      reinterpret_cast<const void*>(&dsv4_prologue_kernel<WAVES, QS, NT>),
+      dim3(static_cast<uint32_t>(blocks)), dim3(WAVES * 64), args, 0, stream);
+  return err == hipSuccess ? FP8KV_OK : FP8KV_ERR_LAUNCH;
+}
+
+}  // namespace
+
+// Instantiated (waves per block, Q heads per wave) shapes.  (1, 1) is the
+// small-batch kernel: one head per 64-lane block.
+int launch_prologue(const PrologueArgs& a, int waves, int qs, hipStream_t stream) {
+#define FP8KV_SHAPE(W, S)                                            \
+  if (waves == W && qs == S) return launch<W, S, false>(a, stream);
+  FP8KV_SHAPE(1, 1)
+  FP8KV_SHAPE(1, 2)
+  FP8KV_SHAPE(1, 4)
+  FP8KV_SHAPE(2, 2)
+  FP8KV_SHAPE(2, 4)
+  FP8KV_SHAPE(4, 1)
+  FP8KV_SHAPE(4, 2)
+  FP8KV_SHAPE(4, 4)
+  FP8KV_SHAPE(4, 8)
+  FP8KV_SHAPE(8, 2)
+  FP8KV_SHAPE(8, 4)
+#undef FP8KV_SHAPE
+  return FP8KV_ERR_UNSUPPORTED;
+}
+
+bool prologue_shape_built(int waves, int qs) {
+  static const int shapes[][2] = {{1, 1}, {1, 2}, {1, 4}, {2, 2}, {2, 4}, {4, 1},
+                                  {4, 2}, {4, 4}, {4, 8}, {8, 2}, {8, 4}};
+  for (const auto& s : shapes)
+    if (s[0] == waves && s[1] == qs) return true;
+  return false;
+}
+
+}  // namespace fp8kv

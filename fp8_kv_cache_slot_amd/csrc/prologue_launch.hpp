@@ -1,0 +1,50 @@
+// Internal launch interface between the C ABI (capi.hip) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "fp8kv.h"
+
+namespace fp8kv {
+
+struct PrologueArgs {
+  uint16_t* q;
+  const uint16_t* kv;
+  const uint16_t* q_weight;
+  const uint16_t* kv_weight;
+  const float* cos_sin;
+  const int64_t* positions;
+  const int64_t* slot_mapping;
+  uint8_t* kv_cache;
+  uint8_t* kv_scale;
+  int32_t num_tokens;
+  int32_t num_heads;
+  int64_t num_cache_slots;  // num_pages * 64
+  int64_t max_position;
+  float eps;
+};
+
+struct PackedArgs {
+  uint16_t* qkv;
+  const uint16_t* q_weight;
+  const uint16_t* k_weight;
+  const float* cos_sin;
+  const int64_t* position_ids;
+  int32_t num_tokens;
+  int32_t num_heads_q;
+  int32_t num_heads_k;
+  int32_t row_elems;  // (Hq + Hk + Hv) * 128
+  int64_t max_position;
+  float eps;
+};
+
+// Launch the fused prologue with `waves` 64-lane waves per block and `qs`
+// Q heads per wave.  Returns FP8KV_ERR_UNSUPPORTED for a shape not built.
+int launch_prologue(const PrologueArgs& a, int waves, int qs, hipStream_t stream);
+bool prologue_shape_built(int waves, int qs);
+
+int launch_packed(const PackedArgs& a, hipStream_t stream);
+
+}  // namespace fp8kv

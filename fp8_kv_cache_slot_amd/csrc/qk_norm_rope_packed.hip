@@ -1,0 +1,121 @@
+// Packed-QKV FusedQkNormRope for gfx950 (InfiniOps PR #1019 "FusedQkNormRope",
+// "Summary"): in qkv[T, (Hq+Hk+Hv)*128], every Q head (q_weight) and K head
+// (k_weight) is RMS-normalised and rotated with full-head NeoX RoPE in place;
+// V heads are never read or written.
+//
+// Layout of the work.  One wave per token.  A 128-element bf16 head is one
+// 16-byte vector per lane of a 16-lane row, so a wave covers four heads per
+// access (rows 0..3 take heads g, g+4, g+8, ... of the token).  The token's
+// position and cos/sin row are loaded once per wave and reused for all of its
+// heads.  Lane l of a row holds dims 8l..8l+7; its NeoX partner dims
+// (i +- 64) sit in lane l +- 8 of the same row, which DPP row_ror:8 delivers
+// in one register move, so the update is in place without any workspace and
+// without a read/write hazard (each lane reads and writes only its own 16
+// bytes).  The row's sum of squares is four DPP steps.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "prologue_launch.hpp"
+#include "wave_ops.hpp"
+
+namespace fp8kv {
+namespace {
+
+template <int WAVES, int U>
+__global__ void __launch_bounds__(WAVES * 64) qk_norm_rope_packed_kernel(
+    uint16_t* __restrict__ qkv, const uint16_t* __restrict__ q_weight,
+    const uint16_t* __restrict__ k_weight, const float* __restrict__ cos_sin,
+    const int64_t* __restrict__ position_ids, int32_t num_tokens,
+    int32_t num_heads_q, int32_t num_heads_k, int32_t row_elems,
+    int64_t max_position, float eps) {
+  const int lane = lane_id();
+  const int32_t t = static_cast<int32_t>(blockIdx.x) * WAVES + wave_id();
+  if (t >= num_tokens) return;
+  const int64_t pos = position_ids[t];
+  if (pos < 0 || pos >= max_position) return;
+  const int g = lane >> 4;   // head slot within the row group
+  const int l16 = lane & 15;
+  const int32_t nh = num_heads_q + num_heads_k;
+
+  float wq[8], wk[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) wq[j] = wk[j] = 0.0f;
+  if (num_heads_q > 0) unpack8(load16<false>(q_weight + l16 * 8), wq);
+  if (num_heads_k > 0) unpack8(load16<false>(k_weight + l16 * 8), wk);
+
+  // cos_i, sin_i for the pair index i = 8 (l16 mod 8) + j of this lane.  The
+  // first half of the head takes  n_i c - n_{i+64} s, the second half
+  // n_{i+64} c + n_i s: fold the sign into the sine once.
+  const float* row = cos_sin + pos * 128 + (l16 & 7) * 8;
+  const f32x4_t c0 = load16f(row), c1 = load16f(row + 4);
+  f32x4_t s0 = load16f(row + 64), s1 = load16f(row + 68);
+  if (l16 < 8) {
+    s0 = -s0;
+    s1 = -s1;
+  }
+  const float c[8] = {c0[0], c0[1], c0[2], c0[3], c1[0], c1[1], c1[2], c1[3]};
+  const float s[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
+
+  uint16_t* base = qkv + static_cast<int64_t>(t) * row_elems + l16 * 8;
+  for (int32_t h0 = 0; h0 < nh; h0 += 4 * U) {
+    u32x4_t x[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int32_t h = h0 + 4 * u + g;
+      x[u] = load16<false>(base + (h < nh ? h : 0) * 128);  // in bounds
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int32_t h = h0 + 4 * u + g;
+      float f[8], n[8];
+      unpack8(x[u], f);
+      const float ss = row16_sum(sum_sq8(f));
+      const float r = __builtin_amdgcn_rsqf(fmaf(ss, 1.0f / 128.0f, eps));
+      const bool is_q = h < num_heads_q;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) n[j] = f[j] * r * (is_q ? wq[j] : wk[j]);
+      float o[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float p = dpp<kDppRowRor8>(n[j]);  // partner element, own weight
+        o[j] = n[j] * c[j] + p * s[j];
+      }
+      if (h < nh) {
+        u32x4_t v = {pack_bf16(o[0], o[1]), pack_bf16(o[2], o[3]),
+                     pack_bf16(o[4], o[5]), pack_bf16(o[6], o[7])};
+        store16<false>(base + h * 128, v);
+      }
+    }
+  }
+}
+
+constexpr int kPackedWaves = 4;
+constexpr int kPackedUnroll = 6;  // 24 heads (16 Q + 8 K) in one batch of loads
+
+}  // namespace
+
+int launch_packed(const PackedArgs& a, hipStream_t stream) {
+  const int64_t blocks = (static_cast<int64_t>(a.num_tokens) + kPackedWaves - 1) /
+                         kPackedWaves;
+  if (blocks > 0x7FFFFFFF) return FP8KV_ERR_SHAPE;
+  void* args[] = {const_cast<uint16_t**>(&a.qkv),
+                  const_cast<const uint16_t**>(&a.q_weight),
+                  const_cast<const uint16_t**>(&a.k_weight),
+                  const_cast<const float**>(&a.cos_sin),
+                  const_cast<const int64_t**>(&a.position_ids),
+                  const_cast<int32_t*>(&a.num_tokens),
+                  const_cast<int32_t*>(&a.num_heads_q),
+                  const_cast<int32_t*>(&a.num_heads_k),
+                  const_cast<int32_t*>(&a.row_elems),
+                  const_cast<int64_t*>(&a.max_position),
+                  const_cast<float*>(&a.eps)};
+  hipError_t err = hipLaunchKernel(
+      reinterpret_cast<const void*>(
+          &qk_norm_rope_packed_kernel<kPackedWaves, kPackedUnroll>),
+      dim3(static_cast<uint32_t>(blocks)), dim3(kPackedWaves * 64), args, 0,
+      stream);
+  return err == hipSuccess ? FP8KV_OK : FP8KV_ERR_LAUNCH;
+}
+
+}  // namespace fp8kv

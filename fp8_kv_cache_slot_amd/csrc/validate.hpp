@@ -1,0 +1,85 @@
+// Host-side argument checks of the two entry points.  Pure C++ (no HIP
+// types or calls), so every error path is reachable without a GPU.
+#pragma once
+
+#include <cstdint>
+
+#include "fp8kv.h"
+
+namespace fp8kv {
+
+constexpr int kHeadDim = 512;
+constexpr int kRopeDim = 64;
+constexpr int kPageSize = 64;
+constexpr int kRowBytes = 576;   // 448 E4M3 codes + 64 bf16
+constexpr int kScaleBytes = 8;   // 7 UE8M0 exponents + 1 reserved byte
+constexpr int kPackedHeadDim = 128;
+
+inline bool aligned(const void* p, uintptr_t a) {
+  return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0;
+}
+
+inline int validate_prologue(const void* q, const void* kv,
+                             const void* q_weight, const void* kv_weight,
+                             const float* cos_sin_cache,
+                             const int64_t* positions,
+                             const int64_t* slot_mapping,
+                             const uint8_t* kv_cache, const uint8_t* kv_scale,
+                             int64_t num_tokens, int32_t num_heads,
+                             int32_t head_dim, int32_t rope_dim,
+                             int64_t max_position, int64_t num_pages,
+                             int32_t page_size) {
+  if (num_tokens < 0 || num_heads < 1 || max_position < 1 || num_pages < 0)
+    return FP8KV_ERR_SHAPE;
+  if (head_dim != kHeadDim || rope_dim != kRopeDim || page_size != kPageSize)
+    return FP8KV_ERR_UNSUPPORTED;
+  // Every slot index (token * (heads + 1)) and every token index fits in
+  // 31 bits; byte offsets are formed in 64 bits.
+  if (num_tokens > 0 &&
+      num_tokens > (int64_t{1} << 31) / (static_cast<int64_t>(num_heads) + 1) - 1)
+    return FP8KV_ERR_SHAPE;
+  if (num_pages > (int64_t{1} << 40)) return FP8KV_ERR_SHAPE;
+  if (num_tokens == 0) return FP8KV_OK;
+  if (!q || !kv || !q_weight || !kv_weight || !cos_sin_cache || !positions ||
+      !slot_mapping)
+    return FP8KV_ERR_NULL;
+  if (num_pages > 0 && (!kv_cache || !kv_scale)) return FP8KV_ERR_NULL;
+  if (!aligned(q, 16) || !aligned(kv, 16) || !aligned(q_weight, 16) ||
+      !aligned(kv_weight, 16) || !aligned(cos_sin_cache, 16) ||
+      !aligned(positions, 8) || !aligned(slot_mapping, 8) ||
+      (kv_cache && !aligned(kv_cache, 16)))
+    return FP8KV_ERR_ALIGN;
+  return FP8KV_OK;
+}
+
+inline int validate_packed(const void* qkv, int64_t num_tokens,
+                           int32_t num_heads_q, int32_t num_heads_k,
+                           int32_t num_heads_v, int32_t head_dim,
+                           const void* q_weight, const void* k_weight,
+                           const float* cos_sin_cache, int32_t is_neox,
+                           const int64_t* position_ids,
+                           int32_t forced_token_heads_per_warp,
+                           int64_t max_position) {
+  if (num_tokens < 0 || num_heads_q < 0 || num_heads_k < 0 ||
+      num_heads_v < 0 || num_heads_q + num_heads_k < 1 || max_position < 1)
+    return FP8KV_ERR_SHAPE;
+  if (head_dim != kPackedHeadDim || is_neox != 1 ||
+      forced_token_heads_per_warp != -1)
+    return FP8KV_ERR_UNSUPPORTED;
+  const int64_t heads = static_cast<int64_t>(num_heads_q) + num_heads_k;
+  if (num_tokens > 0 && (num_tokens > ((int64_t{1} << 31) - 1) / heads ||
+                         static_cast<int64_t>(num_heads_q) + num_heads_k +
+                                 num_heads_v > (1 << 20)))
+    return FP8KV_ERR_SHAPE;
+  if (num_tokens == 0) return FP8KV_OK;
+  if (!qkv || !cos_sin_cache || !position_ids) return FP8KV_ERR_NULL;
+  if ((num_heads_q > 0 && !q_weight) || (num_heads_k > 0 && !k_weight))
+    return FP8KV_ERR_NULL;
+  if (!aligned(qkv, 16) || !aligned(cos_sin_cache, 16) ||
+      !aligned(position_ids, 8) || (q_weight && !aligned(q_weight, 16)) ||
+      (k_weight && !aligned(k_weight, 16)))
+    return FP8KV_ERR_ALIGN;
+  return FP8KV_OK;
+}
+
+}  // namespace fp8kv

@@ -1,0 +1,184 @@
+/*
+ * fp8kv — fused attention prologue for AMD Instinct MI355X (gfx950).
+ *
+ * C ABI of libfp8kv.so.  Two operators, both single-launch, stream-ordered and
+ * asynchronous, both bandwidth-bound (no matrix cores):
+ *
+ *   qnorm_rope_kv_quant_insert — the DeepSeek-V4 attention prologue that the
+ *     pages call fused_deepseek_v4_qnorm_rope_kv_rope_quant_insert
+ *     (FlagGems PR #5449 "[KMCompiler][Hygon] Token-tiled
+ *     fused_deepseek_v4_qnorm_rope_kv_rope_quant_insert", and FlagGems PR #5321
+ *     "… plus test and benchmark fixes", sections "Performance" and "What the
+ *     optimisation does"): per token, every Q head is RMS-normalised and
+ *     rotated in place; the single latent KV head is normalised, rotated,
+ *     quantised to FP8 E4M3 with seven UE8M0 (power-of-two) block exponents
+ *     and inserted into a paged cache through slot_mapping.
+ *
+ *   qk_norm_rope_packed — the packed-QKV FusedQkNormRope (InfiniOps PR #1019
+ *     "FusedQkNormRope", section "Summary"): per-head Q and K RMSNorm followed
+ *     by full-head NeoX RoPE, in place in qkv[T, (Hq+Hk+Hv)*D]; V untouched.
+ *     Argument order follows that page's "Open-Source Alignment" list.
+ *
+ * Conventions shared by every call:
+ *   - Every buffer pointer is a DEVICE pointer owned by the caller.  The
+ *     library never allocates, frees or synchronises, and keeps no state
+ *     besides the two tuning knobs below.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     Work is enqueued on it; the call returns before the kernel runs.
+ *   - Return value: FP8KV_OK (0) or a positive fp8kv_status.  On any argument
+ *     error nothing is launched and no buffer is touched.  num_tokens == 0
+ *     returns FP8KV_OK without touching the device.  A launch failure returns
+ *     FP8KV_ERR_LAUNCH.  A fault inside a kernel surfaces, as with any HIP
+ *     kernel, at the caller's next synchronising call.
+ *   - Tensors are dense and row-major (contiguous).  bf16 data is passed as
+ *     void*; the library reads and writes it as 16-bit bf16 patterns.
+ *   - Calls that write overlapping buffers race unless stream-ordered.
+ */
+#ifndef FP8KV_H
+#define FP8KV_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FP8KV_ABI_VERSION 1
+
+enum fp8kv_status {
+  FP8KV_OK = 0,
+  FP8KV_ERR_NULL = 1,        /* a required pointer is NULL                     */
+  FP8KV_ERR_SHAPE = 2,       /* a size is negative, zero where it must not be,
+                                or too large for the kernels' index range      */
+  FP8KV_ERR_UNSUPPORTED = 3, /* a layout parameter other than the supported one */
+  FP8KV_ERR_ALIGN = 4,       /* a pointer is not aligned as documented          */
+  FP8KV_ERR_DEVICE = 5,      /* no current HIP device, or it is not gfx950      */
+  FP8KV_ERR_LAUNCH = 6       /* the kernel launch itself failed                 */
+};
+
+/*
+ * Fused DeepSeek-V4 attention prologue.
+ *
+ * Shapes: T = num_tokens, H = num_heads, D = head_dim = 512 (the pages count
+ * 16744448 q elements at 511 tokens and 64 heads: FlagGems PR #5449,
+ * "Correctness"), R = rope_dim = 64, page_size = 64.
+ *
+ *   q              bf16 [T, H, 512], read and rewritten in place.  16-byte
+ *                  aligned.
+ *   kv             bf16 [T, 512], the one latent KV head per token (the
+ *                  program count is num_tokens * (num_heads + 1): FlagGems
+ *                  PR #5449, "Dispatch threshold").  Read only.  16-byte
+ *                  aligned.
+ *   q_weight       bf16 [512], RMSNorm weight of every Q head.  16-B aligned.
+ *   kv_weight      bf16 [512], RMSNorm weight of the KV head.  16-B aligned.
+ *   cos_sin_cache  fp32 [max_position, 64]; row p holds cos(p f_i) for
+ *                  i = 0..31 followed by sin(p f_i).  16-byte aligned.
+ *   positions      int64 [T].  A token whose position is outside
+ *                  [0, max_position) is skipped entirely: its q heads and its
+ *                  cache slot are left as they were (no read out of bounds).
+ *   slot_mapping   int64 [T].  Flat cache slot (page * page_size + offset) of
+ *                  each token's KV row.  A negative slot, or one >=
+ *                  num_pages * page_size, skips the cache write of that token;
+ *                  its q heads are still processed.  Slots of distinct tokens
+ *                  must differ (precondition, not checked).
+ *   kv_cache       uint8 [num_pages, page_size, 576], 16-byte aligned.  Row of
+ *                  a written slot: bytes 0..447 = FP8 E4M3 (OCP, finite-only)
+ *                  codes of dims 0..447; bytes 448..575 = dims 448..511 as 64
+ *                  little-endian bf16.  Rows of other slots are not touched.
+ *   kv_scale       uint8 [num_pages, page_size, 8].  Bytes 0..6 of a written
+ *                  slot = e_b + 127, where 2^e_b is the UE8M0 scale of the
+ *                  64-dim block b (dims 64b..64b+63) and e_b is the smallest
+ *                  integer with amax_b <= 448 * 2^e_b, clamped to [-127, 127]
+ *                  (amax 0 gives -127).  Byte 7 is never written.  "Seven
+ *                  per-block exponents per token": FlagGems PR #5449,
+ *                  "Performance".
+ *   eps            added to the mean square inside the square root.
+ *
+ * Per token t, for each Q head and then for the KV head x (with its weight w):
+ *   y_d = x_d / sqrt(mean_d(x_d^2) + eps) * w_d            (fp32)
+ *   pairs (448 + 2i, 449 + 2i), i < 32, rotate by row positions[t]:
+ *     y_a' = y_a cos_i - y_b sin_i,  y_b' = y_b cos_i + y_a sin_i
+ *   Q: q[t, h, :] = bf16_rne(y).
+ *   KV: codes_d = e4m3_rne(y_d * 2^-e_b) for d < 448; dims 448.. as bf16_rne.
+ *
+ * Errors: NULL pointer -> FP8KV_ERR_NULL; num_tokens < 0, num_heads < 1,
+ * max_position < 1, num_pages < 0 or num_tokens * (num_heads + 1) >= 2^31 ->
+ * FP8KV_ERR_SHAPE; head_dim != 512, rope_dim != 64, page_size != 64 ->
+ * FP8KV_ERR_UNSUPPORTED; misaligned pointer -> FP8KV_ERR_ALIGN.
+ */
+int qnorm_rope_kv_quant_insert(
+    void* q, const void* kv, const void* q_weight, const void* kv_weight,
+    const float* cos_sin_cache, const int64_t* positions,
+    const int64_t* slot_mapping, uint8_t* kv_cache, uint8_t* kv_scale,
+    int64_t num_tokens, int32_t num_heads, int32_t head_dim, int32_t rope_dim,
+    int64_t max_position, int64_t num_pages, int32_t page_size, float eps,
+    void* stream);
+
+/*
+ * Packed-QKV FusedQkNormRope (InfiniOps PR #1019, "Summary").
+ *
+ *   qkv           bf16 [T, (Hq + Hk + Hv) * D], heads packed as
+ *                 [Q heads | K heads | V heads].  Q and K heads are rewritten
+ *                 in place; the V heads are neither read nor written.  16-B
+ *                 aligned.
+ *   num_heads_q/k/v  Hq >= 0, Hk >= 0, Hv >= 0, Hq + Hk >= 1.
+ *   head_dim      D = 128 (the page's guarded fast path; others ->
+ *                 FP8KV_ERR_UNSUPPORTED).
+ *   eps           added inside the square root.
+ *   q_weight      bf16 [D] for Q heads; k_weight bf16 [D] for K heads;
+ *                 separate one-dimensional tensors as on the page.  16-B
+ *                 aligned.
+ *   cos_sin_cache fp32 [max_position, D]; row p = D/2 cosines then D/2 sines.
+ *                 16-byte aligned.
+ *   is_neox       must be 1 (NeoX pairs (i, i + D/2)); else UNSUPPORTED.
+ *   position_ids  int64 [T]; a token whose position is outside
+ *                 [0, max_position) is left untouched.
+ *   forced_token_heads_per_warp  must be -1 (automatic scheduling, as on the
+ *                 page); anything else -> FP8KV_ERR_UNSUPPORTED.
+ *
+ * Per Q or K head x with weight w:
+ *   n_d = x_d / sqrt(mean(x^2) + eps) * w_d
+ *   out_i = n_i cos_i - n_{i+D/2} sin_i,  out_{i+D/2} = n_{i+D/2} cos_i + n_i sin_i
+ * so the partner element enters the rotation with its own weight (the page's
+ * paired-weight rule).  Outputs are rounded to bf16 (nearest even).
+ */
+int qk_norm_rope_packed(
+    void* qkv, int64_t num_tokens, int32_t num_heads_q, int32_t num_heads_k,
+    int32_t num_heads_v, int32_t head_dim, float eps, const void* q_weight,
+    const void* k_weight, const float* cos_sin_cache, int32_t is_neox,
+    const int64_t* position_ids, int32_t forced_token_heads_per_warp,
+    int64_t max_position, void* stream);
+
+/* Static text for a status code (never NULL). */
+const char* fp8kv_status_string(int status);
+
+/* Library ABI version (FP8KV_ABI_VERSION of the build). */
+int fp8kv_abi_version(void);
+
+/*
+ * Dispatch threshold of the fused prologue, in programs = num_tokens *
+ * (num_heads + 1) (the quantity FlagGems PR #5449 "Dispatch threshold" finds
+ * both head counts agree on).  Calls below it use the small-batch kernel
+ * (one (token, head) slot per 64-lane block); calls at or above it the tiled
+ * kernel.  programs < 0 restores the built-in default; 0 sends everything to
+ * the tiled kernel; INT64_MAX everything to the small-batch kernel.
+ * Process-wide; returns FP8KV_OK.
+ */
+int fp8kv_set_dispatch_threshold(int64_t programs);
+int64_t fp8kv_get_dispatch_threshold(void);
+
+/*
+ * Tiling of the tiled prologue kernel: waves (of 64 lanes) per block and
+ * Q slots per wave.  The built-in default is the measured best on MI355X;
+ * other instantiated shapes exist for measurement.  (0, 0) restores the
+ * default.  Returns FP8KV_ERR_UNSUPPORTED, and changes nothing, for a shape
+ * that is not built.  Process-wide.
+ */
+int fp8kv_set_tiling(int32_t waves_per_block, int32_t slots_per_wave);
+void fp8kv_get_tiling(int32_t* waves_per_block, int32_t* slots_per_wave);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FP8KV_H */

@@ -47,6 +47,8 @@ def _load():
     lib.oracle_qnorm_rope_kv_quant_insert.argtypes = [
         P, P, P, P, P, P, P, P, P, I64, I32, I64, D]
     lib.oracle_qnorm_rope_kv_quant_insert.restype = None
+    lib.oracle_kv_normalised.argtypes = [P, P, P, P, I64, D, P]
+    lib.oracle_kv_normalised.restype = None
     lib.oracle_qk_norm_rope_packed.argtypes = [
         P, I64, I32, I32, I32, I32, D, P, P, P, P]
     lib.oracle_qk_norm_rope_packed.restype = None
@@ -111,6 +113,21 @@ def qnorm_rope_kv_quant_insert(q, kv, q_weight, kv_weight, cos_sin_cache,
         _ptr(positions, np.int64), _ptr(slot_mapping, np.int64),
         _ptr(kv_cache, np.uint8, True), _ptr(kv_scale, np.uint8, True),
         T, H, pages, float(eps))
+
+
+def kv_normalised(kv, kv_weight, cos_sin_cache, positions, eps):
+    """Unrounded normalised + rotated KV rows, float64 [T, 512]."""
+    T = kv.shape[0]
+    if kv.shape != (T, 512) or positions.shape != (T,):
+        raise ValueError("kv must be [T,512], positions [T]")
+    if T and (positions.min() < 0 or positions.max() >= cos_sin_cache.shape[0]):
+        raise ValueError("position out of range")
+    y = np.empty((T, 512), np.float64)
+    _load().oracle_kv_normalised(
+        _ptr(kv, np.uint16), _ptr(kv_weight, np.uint16),
+        _ptr(cos_sin_cache, np.float32), _ptr(positions, np.int64), T,
+        float(eps), _ptr(y, np.float64, True))
+    return y
 
 
 def qk_norm_rope_packed(qkv, num_heads_q, num_heads_k, num_heads_v, head_dim,

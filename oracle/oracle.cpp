@@ -71,6 +71,16 @@ void rotate_pair(double* a, double* b, double c, double s) {
   *b = b0 * c + a0 * s;
 }
 
+// The KV head of one token, normalised with kv_weight and rotated like a Q
+// head (reading: the norm applies to KV as well as to Q).
+void kv_head(const uint16_t* x, const uint16_t* w, const float* cosv,
+             const float* sinv, double eps, double* y) {
+  rms_norm(x, w, kHeadDim, eps, y);
+  for (int i = 0; i < kRopeDim / 2; ++i)
+    rotate_pair(&y[kRopeStart + 2 * i], &y[kRopeStart + 2 * i + 1], cosv[i],
+                sinv[i]);
+}
+
 }  // namespace
 
 extern "C" {
@@ -191,14 +201,10 @@ void oracle_qnorm_rope_kv_quant_insert(
       for (int d = 0; d < kHeadDim; ++d) qh[d] = oracle_bf16_rne(y[d]);
     }
 
-    // KV: the single latent head, normalised with kv_weight and rotated the
-    // same way (reading: the norm applies to KV as well as to Q).
+    // KV: the single latent head.
     const int64_t slot = slot_mapping[t];
     if (slot < 0 || slot >= num_slots) continue;  // skipped token
-    rms_norm(kv + t * kHeadDim, kv_weight, kHeadDim, eps, y);
-    for (int i = 0; i < kRopeDim / 2; ++i)
-      rotate_pair(&y[kRopeStart + 2 * i], &y[kRopeStart + 2 * i + 1], cosv[i],
-                  sinv[i]);
+    kv_head(kv + t * kHeadDim, kv_weight, cosv, sinv, eps, y);
 
     uint8_t* dst = kv_cache + slot * kRowBytes;
     uint8_t* scale = kv_scale + slot * kScaleBytes;
@@ -221,6 +227,16 @@ void oracle_qnorm_rope_kv_quant_insert(
       dst[kRopeStart + 2 * j] = static_cast<uint8_t>(bits & 0xFF);
       dst[kRopeStart + 2 * j + 1] = static_cast<uint8_t>(bits >> 8);
     }
+  }
+}
+
+void oracle_kv_normalised(const uint16_t* kv, const uint16_t* kv_weight,
+                          const float* cos_sin_cache, const int64_t* positions,
+                          int64_t num_tokens, double eps, double* y_out) {
+  for (int64_t t = 0; t < num_tokens; ++t) {
+    const float* row = cos_sin_cache + positions[t] * kRopeDim;
+    kv_head(kv + t * kHeadDim, kv_weight, row, row + kRopeDim / 2, eps,
+            y_out + t * kHeadDim);
   }
 }
 

@@ -83,6 +83,13 @@ void oracle_qnorm_rope_kv_quant_insert(
     uint8_t* kv_scale, int64_t num_tokens, int32_t num_heads,
     int64_t num_pages, double eps);
 
+/* The KV head of each token after RMSNorm and rotation, before any rounding
+ * (double [T, 512]): the values entry 1 quantises.  Exposed so that tests can
+ * tell how close a block maximum sits to a power-of-two exponent boundary. */
+void oracle_kv_normalised(const uint16_t* kv, const uint16_t* kv_weight,
+                          const float* cos_sin_cache, const int64_t* positions,
+                          int64_t num_tokens, double eps, double* y_out);
+
 /* ---- entry 2: packed-QKV FusedQkNormRope ([P3] "Summary") ---------------- */
 /*
  *   qkv           bf16 [T, (Hq + Hk + Hv) * D], Q and K heads rewritten in

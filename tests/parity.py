@@ -1,0 +1,130 @@
+"""Comparison of the GPU library's outputs with the CPU oracle's.
+
+Acceptance rules (floating point decided per element; integer and byte results
+bit-exact):
+  * bf16 outputs (q, the rotary part of the cache, packed Q/K):
+        |got - ref| <= 2^-7 |ref| + 1e-3
+    and at most ``MAX_MISMATCH`` of the elements may differ in their bits at
+    all (fp32 kernel arithmetic vs double oracle only flips a rounding when the
+    value sits next to a bf16 midpoint; a wrong rounding mode would flip ~50%).
+  * E4M3 codes: at most one step apart on the signed integer line
+    (sign-magnitude, +0 == -0), and at most ``MAX_MISMATCH`` differ.
+  * UE8M0 exponent bytes: bit-exact, except in a block whose oracle maximum A
+    lies within 2^-18 of an exponent boundary (A / (448 2^e) > 1 - 2^-18 or
+    < (1 + 2^-18) / 2): there the two exponents may differ by one and the
+    block's codes are checked by dequantised value against the oracle's
+    unrounded values instead.
+  * Everything the operator must not write: bit-exact (canary bytes, byte 7
+    of every scale row, the V section of packed qkv).
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+import oracle as O
+
+MAX_MISMATCH = 1e-3
+BAND = 2.0 ** -18
+
+_E4M3 = np.array([O.e4m3_decode(c) for c in range(256)], np.float64)
+
+
+def bf16_val(bits):
+    return (np.asarray(bits, np.uint16).astype(np.uint32) << 16).view(
+        np.float32).astype(np.float64)
+
+
+def check_bf16(got, ref, what=""):
+    got = np.asarray(got, np.uint16)
+    ref = np.asarray(ref, np.uint16)
+    assert got.shape == ref.shape, (what, got.shape, ref.shape)
+    g, r = bf16_val(got), bf16_val(ref)
+    bad = ~(np.abs(g - r) <= 2.0 ** -7 * np.abs(r) + 1e-3)
+    if bad.any():
+        i = np.flatnonzero(bad.ravel())[:5]
+        raise AssertionError(
+            f"{what}: {bad.sum()} bf16 values out of tolerance, e.g. at {i}: "
+            f"got {g.ravel()[i]} ref {r.ravel()[i]}")
+    frac = float(np.mean(got != ref)) if got.size else 0.0
+    assert frac <= MAX_MISMATCH, f"{what}: {frac:.2e} of bf16 values differ in bits"
+    return frac
+
+
+def _signed_code(c):
+    c = np.asarray(c, np.int32)
+    mag = c & 0x7F
+    return np.where(c & 0x80, -mag, mag)
+
+
+def check_cache(got_cache, got_scale, ref_cache, ref_scale, slots, y_ref,
+                canary_cache, canary_scale, what=""):
+    """Compare the rows of ``slots`` (the valid slots of the tokens whose
+    unrounded oracle KV values are ``y_ref[i]``) and return a dict of
+    statistics.  Rows outside ``slots`` are not looked at here."""
+    gc = got_cache.reshape(-1, 576)
+    gs = got_scale.reshape(-1, 8)
+    rc = ref_cache.reshape(-1, 576)
+    rs = ref_scale.reshape(-1, 8)
+    stats = dict(rows=len(slots), code_diff=0, band_blocks=0, rope_frac=0.0)
+    if len(slots) == 0:
+        return stats
+    slots = np.asarray(slots, np.int64)
+    g_rows, r_rows = gc[slots], rc[slots]
+    g_sc, r_sc = gs[slots], rs[slots]
+    assert np.all(g_sc[:, 7] == canary_scale), f"{what}: reserved scale byte written"
+    # rotary dims as bf16
+    stats["rope_frac"] = check_bf16(
+        g_rows[:, 448:].copy().view(np.uint16), r_rows[:, 448:].copy().view(np.uint16),
+        what + " rope bf16")
+    # exponents
+    e_g = g_sc[:, :7].astype(np.int32) - 127
+    e_r = r_sc[:, :7].astype(np.int32) - 127
+    y = np.asarray(y_ref)[:, :448].reshape(len(slots), 7, 64)
+    amax = np.abs(y).max(axis=2)
+    rho = amax / (448.0 * np.exp2(e_r.astype(np.float64)))
+    in_band = (rho > 1 - BAND) | (rho < 0.5 * (1 + BAND))
+    diff_e = e_g != e_r
+    bad_e = diff_e & ~(in_band & (np.abs(e_g - e_r) == 1))
+    assert not bad_e.any(), (
+        f"{what}: {bad_e.sum()} exponent bytes differ outside the boundary band; "
+        f"first at {np.argwhere(bad_e)[:3].tolist()}")
+    stats["band_blocks"] = int(diff_e.sum())
+    # codes
+    codes_g = g_rows[:, :448].reshape(len(slots), 7, 64)
+    codes_r = r_rows[:, :448].reshape(len(slots), 7, 64)
+    same_e = ~diff_e
+    d = np.abs(_signed_code(codes_g) - _signed_code(codes_r))
+    bad_c = (d > 1) & same_e[:, :, None]
+    assert not bad_c.any(), (
+        f"{what}: {bad_c.sum()} codes more than one E4M3 step apart; first at "
+        f"{np.argwhere(bad_c)[:3].tolist()}")
+    n_same = int(same_e.sum()) * 64
+    n_diff = int(((d != 0) & same_e[:, :, None]).sum())
+    stats["code_diff"] = n_diff
+    if n_same:
+        assert n_diff / n_same <= MAX_MISMATCH, (
+            f"{what}: {n_diff}/{n_same} codes differ")
+    # blocks in the band: dequantised values against the unrounded oracle
+    for (i, b) in np.argwhere(diff_e):
+        deq = _E4M3[codes_g[i, b]] * 2.0 ** e_g[i, b]
+        yy = y[i, b]
+        tol = np.maximum(np.abs(yy) * 2.0 ** -4, 2.0 ** (e_g[i, b] - 10)) * 1.05 + 1e-30
+        assert np.all(np.abs(deq - yy) <= tol), f"{what}: band block {i},{b}"
+    return stats
+
+
+def check_untouched(got_cache, got_scale, written_slots, canary_cache,
+                    canary_scale, what=""):
+    gc = got_cache.reshape(-1, 576)
+    gs = got_scale.reshape(-1, 8)
+    mask = np.ones(gc.shape[0], bool)
+    mask[np.asarray(list(written_slots), np.int64)] = False
+    assert np.all(gc[mask] == canary_cache), f"{what}: untouched cache row written"
+    assert np.all(gs[mask] == canary_scale), f"{what}: untouched scale row written"
+    assert np.all(gs[:, 7] == canary_scale), f"{what}: reserved scale byte written"
+
+
+def valid_slots(slot_mapping, num_slots):
+    sm = np.asarray(slot_mapping, np.int64)
+    return (sm >= 0) & (sm < num_slots)

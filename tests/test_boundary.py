@@ -1,0 +1,163 @@
+"""The C ABI on the CPU: the library loads, exports exactly what
+include/fp8kv.h declares, and rejects bad arguments before touching any
+device (so these calls never launch).  Also the byte accounting and the
+input generators."""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+import torch
+
+import fp8_kv_cache_slot_amd as K
+from fp8_kv_cache_slot_amd import accounting as A
+from fp8_kv_cache_slot_amd import inputs as I
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fp8kv.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b([a-z_][a-z0-9_]*)\s*\(", text)) -
+                  {"defined"})
+
+
+def test_header_declarations_are_exported():
+    names = _declared()
+    assert "qnorm_rope_kv_quant_insert" in names and "qk_norm_rope_packed" in names
+    lib = ctypes.CDLL(K.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert sorted(names) == sorted(K.EXPORTED)
+    assert K.abi_version() == 1
+
+
+def test_exports_nothing_else():
+    import subprocess
+    out = subprocess.run(["nm", "-D", "--defined-only", K.LIB_PATH],
+                         capture_output=True, text=True, check=True).stdout
+    syms = {l.split()[-1] for l in out.splitlines() if " T " in l}
+    assert syms == set(K.EXPORTED)
+
+
+def test_status_strings():
+    for s in range(7):
+        assert K.lib().fp8kv_status_string(s).decode()
+    assert K.lib().fp8kv_status_string(99) == b"unknown status"
+
+
+FAKE = 0x10000  # aligned non-NULL address; never dereferenced (validation fails first)
+
+
+def _prologue(**over):
+    a = dict(q=FAKE, kv=FAKE, qw=FAKE, kw=FAKE, cs=FAKE, pos=FAKE, sm=FAKE,
+             cache=FAKE, scale=FAKE, T=4, H=8, D=512, R=64, maxp=16, pages=1,
+             page=64, eps=1e-6, stream=None)
+    a.update(over)
+    return K.lib().qnorm_rope_kv_quant_insert(*a.values())
+
+
+def _packed(**over):
+    a = dict(qkv=FAKE, T=4, hq=16, hk=8, hv=8, D=128, eps=1e-6, qw=FAKE, kw=FAKE,
+             cs=FAKE, neox=1, pos=FAKE, forced=-1, maxp=16, stream=None)
+    a.update(over)
+    return K.lib().qk_norm_rope_packed(*a.values())
+
+
+@pytest.mark.parametrize("over,want", [
+    (dict(T=-1), 2), (dict(H=0), 2), (dict(maxp=0), 2), (dict(pages=-1), 2),
+    (dict(T=1 << 30, H=64), 2),
+    (dict(D=256), 3), (dict(R=32), 3), (dict(page=16), 3),
+    (dict(q=None), 1), (dict(kv=None), 1), (dict(qw=None), 1), (dict(kw=None), 1),
+    (dict(cs=None), 1), (dict(pos=None), 1), (dict(sm=None), 1),
+    (dict(cache=None), 1), (dict(scale=None), 1),
+    (dict(q=FAKE + 8), 4), (dict(kv=FAKE + 2), 4), (dict(qw=FAKE + 4), 4),
+    (dict(cs=FAKE + 4), 4), (dict(pos=FAKE + 4), 4), (dict(cache=FAKE + 8), 4),
+    (dict(T=0, q=None, kv=None), 0),
+    (dict(pages=0, cache=None, scale=None, T=0), 0),
+])
+def test_prologue_argument_errors(over, want):
+    assert _prologue(**over) == want
+
+
+@pytest.mark.parametrize("over,want", [
+    (dict(T=-1), 2), (dict(hq=0, hk=0), 2), (dict(hv=-1), 2), (dict(maxp=0), 2),
+    (dict(D=64), 3), (dict(neox=0), 3), (dict(forced=0), 3), (dict(forced=4), 3),
+    (dict(qkv=None), 1), (dict(cs=None), 1), (dict(pos=None), 1),
+    (dict(qw=None), 1), (dict(kw=None), 1),
+    (dict(qkv=FAKE + 2), 4), (dict(cs=FAKE + 8), 4), (dict(kw=FAKE + 2), 4),
+    (dict(T=0), 0),
+])
+def test_packed_argument_errors(over, want):
+    assert _packed(**over) == want
+
+
+@pytest.mark.skipif(torch.cuda.device_count() > 0, reason="a GPU is present")
+def test_no_device_is_reported_not_launched():
+    # valid-looking arguments reach the device check, which fails without a
+    # GPU; nothing is dereferenced
+    assert _prologue() == 5
+    assert _packed() == 5
+
+
+def test_knobs():
+    K.set_dispatch_threshold(123)
+    assert K.get_dispatch_threshold() == 123
+    K.set_dispatch_threshold(-1)
+    default = K.get_dispatch_threshold()
+    assert default >= 0
+    K.set_tiling(4, 2)
+    assert K.get_tiling() == (4, 2)
+    with pytest.raises(K.Fp8kvError):
+        K.set_tiling(3, 5)
+    assert K.get_tiling() == (4, 2)
+    K.set_tiling(0, 0)
+
+
+def test_binding_rejects_host_tensors():
+    x = I.make_dsv4(I.DSV4_WORKLOADS["tiny"], "cpu")
+    with pytest.raises(ValueError, match="device tensor"):
+        K.qnorm_rope_kv_quant_insert(x["q"], x["kv"], x["q_weight"],
+                                     x["kv_weight"], x["cos_sin_cache"],
+                                     x["positions"], x["slot_mapping"],
+                                     x["kv_cache"], x["kv_scale"], x["eps"])
+
+
+def test_byte_accounting_totals():
+    # per-token formula applied to each workload's actual slot mapping
+    expect = {"tiny": 553_186, "prefill": 4_356_540_416,
+              "wide128": 8_651_507_712, "long64": 17_426_155_520}
+    for name, total in expect.items():
+        w = I.DSV4_WORKLOADS[name]
+        written = w.num_tokens - w.num_skipped
+        assert A.dsv4_bytes(w.num_tokens, w.num_heads, written) == total, name
+    assert A.dsv4_bytes(1024, 64, 973) == 136_061_915
+    for T, total in [(1, 13_320), (17, 218_248), (8192, 104_923_648)]:
+        assert A.packed_bytes(T, 16, 8, 128) == total
+
+
+def test_generators_shapes_and_slot_maps():
+    for name in ("tiny", "decode"):
+        w = I.DSV4_WORKLOADS[name]
+        x = I.make_dsv4(w, "cpu")
+        sm = x["slot_mapping"].numpy()
+        assert (sm == -1).sum() == w.num_skipped
+        v = sm[sm >= 0]
+        assert len(set(v.tolist())) == len(v) and v.max() < w.num_pages * 64
+        assert x["q"].shape == (w.num_tokens, w.num_heads, 512)
+        assert int(x["positions"].max()) < w.max_position
+    # sequence layout: page-contiguous within each sequence, distinct pages
+    w = I.Dsv4Workload("seq", 512, 2, 1024, 16, False, "arange", "sequences", 0,
+                       7, num_sequences=4)
+    sm = I.make_dsv4(w, "cpu")["slot_mapping"].numpy().reshape(4, 128)
+    assert np.all(sm[:, 1:64] - sm[:, :63] == 1)
+    pages = sm[:, ::64] // 64
+    assert len(set(pages.ravel().tolist())) == 8
+    # packed
+    p = I.make_packed(I.PACKED_WORKLOADS["packed_t17"], "cpu")
+    assert p["qkv"].shape == (17, 32 * 128)
+    assert p["cos_sin_cache"].shape == (8192, 128)

@@ -1,0 +1,357 @@
+"""Parity of the HIP kernels (called through the C ABI via the thin binding)
+with the CPU oracle, on seeded synthetic inputs.  Needs an MI355X."""
+
+import numpy as np
+import pytest
+import torch
+
+import fp8_kv_cache_slot_amd as K
+import oracle as O
+from fp8_kv_cache_slot_amd import inputs as I
+from tests import golden_case
+from tests import parity as P
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+SMALL = 2 ** 63 - 1   # threshold sending every call to the small-batch kernel
+TILED = 0             # threshold sending every call to the tiled kernel
+
+
+@pytest.fixture(autouse=True)
+def _restore_knobs():
+    yield
+    K.set_dispatch_threshold(-1)
+    K.set_tiling(0, 0)
+
+
+def _say(msg):
+    print(msg, flush=True)
+
+
+def _run(x, threshold=None):
+    q = x["q"].clone()
+    cache = x["kv_cache"].clone()
+    scale = x["kv_scale"].clone()
+    if threshold is not None:
+        K.set_dispatch_threshold(threshold)
+    K.qnorm_rope_kv_quant_insert(q, x["kv"], x["q_weight"], x["kv_weight"],
+                                 x["cos_sin_cache"], x["positions"],
+                                 x["slot_mapping"], cache, scale, x["eps"])
+    torch.cuda.synchronize()
+    return q, cache, scale
+
+
+def _host(x):
+    return {k: (I.bits(v) if isinstance(v, torch.Tensor) else v)
+            for k, v in x.items()}
+
+
+def _oracle(h):
+    ref = {k: (v.copy() if isinstance(v, np.ndarray) else v) for k, v in h.items()}
+    O.qnorm_rope_kv_quant_insert(
+        ref["q"], ref["kv"], ref["q_weight"], ref["kv_weight"],
+        ref["cos_sin_cache"], ref["positions"], ref["slot_mapping"],
+        ref["kv_cache"], ref["kv_scale"], ref["eps"])
+    return ref
+
+
+def _compare_full(h, ref, got, what):
+    q, cache, scale = (I.bits(t) for t in got)
+    P.check_bf16(q, ref["q"], what + " q")
+    num_slots = h["kv_cache"].shape[0] * 64
+    v = P.valid_slots(h["slot_mapping"], num_slots)
+    slots = h["slot_mapping"][v]
+    y = O.kv_normalised(h["kv"][v].copy(), h["kv_weight"], h["cos_sin_cache"],
+                        h["positions"][v].copy(), h["eps"])
+    stats = P.check_cache(cache, scale, ref["kv_cache"], ref["kv_scale"], slots, y,
+                          I.CACHE_CANARY, I.SCALE_CANARY, what)
+    P.check_untouched(cache, scale, slots, I.CACHE_CANARY, I.SCALE_CANARY, what)
+    return stats
+
+
+# ---------------------------------------------------------------------------
+# fused prologue
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("threshold", [SMALL, TILED], ids=["small", "tiled"])
+def test_golden_worked_example(threshold):
+    g = golden_case.load()
+    h = golden_case.inputs(g)
+    exp = golden_case.expected(g)
+    x = {k: (I.from_bits(v, DEV) if isinstance(v, np.ndarray) else v)
+         for k, v in h.items()}
+    q, cache, scale = _run(x, threshold)
+    np.testing.assert_array_equal(I.bits(q), exp["q"])
+    np.testing.assert_array_equal(I.bits(scale), exp["kv_scale"])
+    np.testing.assert_array_equal(I.bits(cache), exp["kv_cache"])
+
+
+@pytest.mark.parametrize("name", ["tiny", "decode"])
+def test_small_workloads_all_paths(name):
+    w = I.DSV4_WORKLOADS[name]
+    _say(f"workload {name} T={w.num_tokens} H={w.num_heads}")
+    x = I.make_dsv4(w, DEV)
+    h = _host(x)
+    ref = _oracle(h)
+    outs = {}
+    for label, thr in [("small", SMALL), ("tiled", TILED), ("default", None)]:
+        K.set_dispatch_threshold(-1)
+        got = _run(x, thr)
+        _compare_full(h, ref, got, f"{name}/{label}")
+        outs[label] = [I.bits(t) for t in got]
+    # repeated launches are deterministic
+    again = [I.bits(t) for t in _run(x, TILED)]
+    for a, b in zip(again, outs["tiled"]):
+        np.testing.assert_array_equal(a, b)
+
+
+@pytest.mark.parametrize("heads", [64, 128])
+def test_page_token_counts_both_paths(heads):
+    # Token counts that are not multiples of a plausible tiling, plus 1, 4 and
+    # 17 tokens pushed through the tiled kernel.
+    for T in [1, 4, 17, 511, 512, 777, 1000]:
+        _say(f"T={T} H={heads}")
+        w = I.custom_dsv4(T, heads, seed=2000 + T + heads, max_position=8192)
+        x = I.make_dsv4(w, DEV)
+        h = _host(x)
+        ref = _oracle(h)
+        for label, thr in [("small", SMALL), ("tiled", TILED)]:
+            _compare_full(h, ref, _run(x, thr), f"T={T} H={heads} {label}")
+
+
+def test_every_built_tiling():
+    w = I.custom_dsv4(300, 20, seed=3000, max_position=8192)   # ragged: 20 heads
+    x = I.make_dsv4(w, DEV)
+    h = _host(x)
+    ref = _oracle(h)
+    shapes = [(1, 1), (1, 2), (1, 4), (2, 2), (2, 4), (4, 1), (4, 2), (4, 4),
+              (4, 8), (8, 2), (8, 4)]
+    for wv, qs in shapes:
+        _say(f"tiling {wv}x{qs}")
+        K.set_tiling(wv, qs)
+        _compare_full(h, ref, _run(x, TILED), f"tiling {wv}x{qs}")
+    with pytest.raises(K.Fp8kvError):
+        K.set_tiling(3, 3)
+
+
+def _sampled_tokens(T, rng, n_random=192):
+    picks = set(range(min(64, T))) | set(range(max(0, T - 64), T))
+    picks |= set(rng.choice(T, size=min(n_random, T), replace=False).tolist())
+    return np.array(sorted(picks), np.int64)
+
+
+@pytest.mark.parametrize("name", ["prefill", "wide128", "long64"])
+def test_full_size_workloads(name):
+    # Full size, default dispatch (the configuration the benchmark times):
+    # sampled tokens against the oracle, and at full size the properties the
+    # oracle need not recompute: every valid slot written, every other byte
+    # untouched.
+    w = I.DSV4_WORKLOADS[name]
+    _say(f"workload {name} T={w.num_tokens} H={w.num_heads}")
+    x = I.make_dsv4(w, DEV)
+    q, cache, scale = _run(x)
+    num_slots = w.num_pages * 64
+    sm = x["slot_mapping"]
+    valid = (sm >= 0) & (sm < num_slots)
+    written = sm[valid]
+    mask = torch.ones(num_slots, dtype=torch.bool, device=DEV)
+    mask[written] = False
+    c2, s2 = cache.view(-1, 576), scale.view(-1, 8)
+    assert bool((c2[mask] == I.CACHE_CANARY).all())
+    assert bool((s2[mask] == I.SCALE_CANARY).all())
+    assert bool((s2[:, 7] == I.SCALE_CANARY).all())
+    assert bool((s2[written, :7] != I.SCALE_CANARY).all())
+
+    rng = np.random.default_rng(w.seed)
+    toks = _sampled_tokens(w.num_tokens, rng)
+    ti = torch.from_numpy(toks).to(DEV)
+    h = dict(q=I.bits(x["q"][ti]), kv=I.bits(x["kv"][ti]),
+             q_weight=I.bits(x["q_weight"]), kv_weight=I.bits(x["kv_weight"]),
+             cos_sin_cache=I.bits(x["cos_sin_cache"]),
+             positions=I.bits(x["positions"][ti]),
+             slot_mapping=I.bits(x["slot_mapping"][ti]),
+             kv_cache=np.full((w.num_pages, 64, 576), I.CACHE_CANARY, np.uint8),
+             kv_scale=np.full((w.num_pages, 64, 8), I.SCALE_CANARY, np.uint8),
+             eps=x["eps"])
+    ref = _oracle(h)
+    P.check_bf16(I.bits(q[ti]), ref["q"], name + " q")
+    v = P.valid_slots(h["slot_mapping"], num_slots)
+    slots = h["slot_mapping"][v]
+    y = O.kv_normalised(h["kv"][v].copy(), h["kv_weight"], h["cos_sin_cache"],
+                        h["positions"][v].copy(), h["eps"])
+    P.check_cache(I.bits(cache), I.bits(scale), ref["kv_cache"], ref["kv_scale"],
+                  slots, y, I.CACHE_CANARY, I.SCALE_CANARY, name)
+
+
+def test_rows_of_distinct_magnitude():
+    # Regression for the cross-row reduction: the four 16-lane rows of a head
+    # (dims 0-127, 128-255, 256-383, 384-511) hold very different magnitudes,
+    # so a reduction that drops, doubles or swaps a row cannot match.
+    w = I.custom_dsv4(8, 4, seed=4010)
+    x = I.make_dsv4(w, DEV)
+    scale = torch.tensor([1.0, 8.0, 0.125, 64.0], device=DEV).repeat_interleave(128)
+    x["q"] = (x["q"].float() * scale).to(torch.bfloat16).contiguous()
+    x["kv"] = (x["kv"].float() * scale.flip(0)).to(torch.bfloat16).contiguous()
+    h = _host(x)
+    ref = _oracle(h)
+    for thr in (SMALL, TILED):
+        _compare_full(h, ref, _run(x, thr), "row magnitudes")
+
+
+def test_edge_cases():
+    # one token, one head
+    w = I.custom_dsv4(1, 1, seed=4000)
+    x = I.make_dsv4(w, DEV)
+    h = _host(x)
+    ref = _oracle(h)
+    for thr in (SMALL, TILED):
+        _compare_full(h, ref, _run(x, thr), "T=1 H=1")
+    # all-zero activations
+    w = I.custom_dsv4(9, 3, seed=4001)
+    x = I.make_dsv4(w, DEV)
+    x["q"].zero_()
+    x["kv"].zero_()
+    h = _host(x)
+    ref = _oracle(h)
+    for thr in (SMALL, TILED):
+        _compare_full(h, ref, _run(x, thr), "zeros")
+    # no token writes the cache; zero pages
+    w = I.custom_dsv4(7, 5, seed=4002, num_pages=1)
+    x = I.make_dsv4(w, DEV)
+    x["slot_mapping"][:] = -1
+    x["slot_mapping"][2] = 64          # == num_pages * 64: out of range
+    h = _host(x)
+    ref = _oracle(h)
+    for thr in (SMALL, TILED):
+        _compare_full(h, ref, _run(x, thr), "all skipped")
+    x["kv_cache"] = torch.empty((0, 64, 576), dtype=torch.uint8, device=DEV)
+    x["kv_scale"] = torch.empty((0, 64, 8), dtype=torch.uint8, device=DEV)
+    q, _, _ = _run(x)
+    P.check_bf16(I.bits(q), ref["q"], "zero pages")
+    # zero tokens: nothing happens
+    K.qnorm_rope_kv_quant_insert(
+        x["q"][:0], x["kv"][:0], x["q_weight"], x["kv_weight"],
+        x["cos_sin_cache"], x["positions"][:0], x["slot_mapping"][:0],
+        x["kv_cache"], x["kv_scale"], 1e-6)
+    torch.cuda.synchronize()
+
+
+def test_out_of_range_position_leaves_token_untouched():
+    w = I.custom_dsv4(12, 6, seed=4003, max_position=64)
+    x = I.make_dsv4(w, DEV)
+    x["slot_mapping"] = torch.arange(12, device=DEV, dtype=torch.int64)
+    bad = [3, 7]
+    pos = x["positions"].clone()
+    x["positions"][3] = -1
+    x["positions"][7] = 64
+    for thr in (SMALL, TILED):
+        q, cache, scale = _run(x, thr)
+        for t in bad:
+            assert torch.equal(q[t], x["q"][t])
+            assert bool((cache.view(-1, 576)[t] == I.CACHE_CANARY).all())
+            assert bool((scale.view(-1, 8)[t] == I.SCALE_CANARY).all())
+        # every other token is as the oracle says
+        keep = torch.tensor([t for t in range(12) if t not in bad], device=DEV)
+        y = dict(x)
+        y["positions"] = pos
+        h = _host({k: (v[keep] if k in ("q", "kv", "positions", "slot_mapping")
+                       else v) for k, v in y.items()})
+        ref = _oracle(h)
+        P.check_bf16(I.bits(q[keep]), ref["q"], "in-range tokens")
+
+
+def test_argument_errors_touch_nothing():
+    w = I.custom_dsv4(8, 4, seed=4004)
+    x = I.make_dsv4(w, DEV)
+    q0 = x["q"].clone()
+    L = K.lib()
+    args = [x["q"].data_ptr(), x["kv"].data_ptr(), x["q_weight"].data_ptr(),
+            x["kv_weight"].data_ptr(), x["cos_sin_cache"].data_ptr(),
+            x["positions"].data_ptr(), x["slot_mapping"].data_ptr(),
+            x["kv_cache"].data_ptr(), x["kv_scale"].data_ptr(), 8, 4, 512, 64,
+            x["cos_sin_cache"].shape[0], w.num_pages, 64, 1e-6, None]
+    cases = {2: dict(i=9, v=-1), 3: dict(i=11, v=256), 4: dict(i=0, v=args[0] + 2),
+             1: dict(i=1, v=None)}
+    for want, c in cases.items():
+        a = list(args)
+        a[c["i"]] = c["v"]
+        assert L.qnorm_rope_kv_quant_insert(*a) == want
+    torch.cuda.synchronize()
+    assert torch.equal(x["q"], q0)
+    assert L.qnorm_rope_kv_quant_insert(*args) == 0
+    torch.cuda.synchronize()
+    assert not torch.equal(x["q"], q0)
+
+
+# ---------------------------------------------------------------------------
+# packed Q/K norm + RoPE
+# ---------------------------------------------------------------------------
+
+def _run_packed(x, forced=-1, explicit=True):
+    qkv = x["qkv"].clone()
+    kw = dict(forced_token_heads_per_warp=forced) if explicit else {}
+    K.qk_norm_rope_packed(qkv, x["num_heads_q"], x["num_heads_k"],
+                          x["num_heads_v"], x["head_dim"], x["eps"],
+                          x["q_weight"], x["k_weight"], x["cos_sin_cache"], True,
+                          x["position_ids"], **kw)
+    torch.cuda.synchronize()
+    return qkv
+
+
+def _oracle_packed(x):
+    qkv = I.bits(x["qkv"]).copy()
+    O.qk_norm_rope_packed(qkv, x["num_heads_q"], x["num_heads_k"],
+                          x["num_heads_v"], x["head_dim"], x["eps"],
+                          I.bits(x["q_weight"]), I.bits(x["k_weight"]),
+                          I.bits(x["cos_sin_cache"]), I.bits(x["position_ids"]))
+    return qkv
+
+
+def _compare_packed(x, got, what):
+    ref = _oracle_packed(x)
+    g = I.bits(got)
+    nqk = (x["num_heads_q"] + x["num_heads_k"]) * x["head_dim"]
+    np.testing.assert_array_equal(g[:, nqk:], I.bits(x["qkv"])[:, nqk:],
+                                  err_msg=what + ": V section changed")
+    P.check_bf16(g[:, :nqk], ref[:, :nqk], what)
+
+
+@pytest.mark.parametrize("name", ["packed_t1", "packed_t17", "packed_t8192"])
+def test_packed_workloads(name):
+    _say(f"workload {name}")
+    x = I.make_packed(I.PACKED_WORKLOADS[name], DEV)
+    got = _run_packed(x)
+    _compare_packed(x, got, name)
+    # forced_token_heads_per_warp = -1 passed explicitly or left to the default
+    assert torch.equal(got, _run_packed(x, explicit=False))
+
+
+@pytest.mark.parametrize("heads", [(16, 0, 8), (0, 8, 8), (5, 3, 1), (1, 1, 0),
+                                   (32, 8, 8), (40, 4, 4)])
+def test_packed_head_mixes(heads):
+    hq, hk, hv = heads
+    w = I.PackedWorkload("mix", 33, hq, hk, hv, seed=5000 + hq * 7 + hk)
+    x = I.make_packed(w, DEV)
+    _compare_packed(x, _run_packed(x), f"heads {heads}")
+
+
+def test_packed_rejects_and_skips():
+    x = I.make_packed(I.PackedWorkload("p", 5, seed=5100), DEV)
+    for bad in (dict(forced=4), ):
+        with pytest.raises(K.Fp8kvError):
+            _run_packed(x, forced=bad["forced"])
+    qkv = x["qkv"].clone()
+    with pytest.raises(K.Fp8kvError):
+        K.qk_norm_rope_packed(qkv, 16, 8, 8, 128, 1e-6, x["q_weight"],
+                              x["k_weight"], x["cos_sin_cache"], False,
+                              x["position_ids"])
+    assert torch.equal(qkv, x["qkv"])
+    # out-of-range position: that token is untouched
+    x["position_ids"][2] = x["cos_sin_cache"].shape[0]
+    got = _run_packed(x)
+    assert torch.equal(got[2], x["qkv"][2])
+    keep = torch.tensor([0, 1, 3, 4], device=DEV)
+    y = dict(x)
+    y["qkv"] = x["qkv"][keep].contiguous()
+    y["position_ids"] = x["position_ids"][keep].contiguous()
+    _compare_packed(y, got[keep].contiguous(), "in-range tokens")
