@@ -17,11 +17,17 @@ namespace fp8kv {
 namespace {
 
 // Programs = num_tokens * (num_heads + 1) below which the small-batch kernel
-// runs (the quantity FlagGems PR #5449 "Dispatch threshold" dispatches on);
-// the value is the crossover measured on MI355X.
-constexpr int64_t kDefaultThreshold = 4096;
+// runs (the quantity FlagGems PR #5449 "Dispatch threshold" dispatches on).
+// Measured on MI355X with the caches flushed between launches: below ~8k
+// programs both kernels sit on the same ~6 us launch floor; the tiled kernel
+// is ahead from 8320 programs at 64 heads (128 tokens) and from 8256 at 128
+// heads (64 tokens), so one program count serves both head counts.
+constexpr int64_t kDefaultThreshold = 8192;
+// Tiled shape: 4 waves per block, 2 Q heads per wave.  2x2, 4x2 and 8x2 all
+// reach ~6.1-6.2 TB/s on the large workloads; 4x2 is the most even across
+// 32768x64, 131072x64, 32768x128 and the mid-size (128..2048 token) range.
 constexpr int kDefaultWaves = 4;
-constexpr int kDefaultSlots = 4;
+constexpr int kDefaultSlots = 2;
 
 std::atomic<int64_t> g_threshold{kDefaultThreshold};
 std::atomic<int32_t> g_tiling{(kDefaultWaves << 16) | kDefaultSlots};

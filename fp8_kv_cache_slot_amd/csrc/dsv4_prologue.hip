@@ -11,12 +11,15 @@
 // design (no divergence between the two paths):
 //   blocks [0, kv_blocks)       one KV row per wave
 //   blocks [kv_blocks, ...)     one wave = QS consecutive heads of one token
-// Each Q wave issues its QS head loads before any arithmetic so QS KiB are in
-// flight per wave, reads the token's position and its cos/sin row once, and
-// reduces the sum of squares across the wave with DPP row steps and four
-// v_readlane of the row totals.  The rotary dims 448..511 sit in lanes 56..63, eight values (four
-// interleaved pairs) per lane, so rotation never leaves the register file.
-// The KV quantisation block of dims 64b..64b+63 is the lane group 8b..8b+7:
+// Each Q wave issues its QS head loads before any arithmetic, so QS KiB are
+// in flight per wave.  The q and kv streams are read and written with
+// non-temporal loads and stores: none of it is reused, and keeping it out of
+// the caches measured 9% faster on MI355X.  The wave reads the token's
+// position and cos/sin row once and reduces the sum of squares with DPP row
+// steps plus four v_readlane of the row totals.  The rotary dims 448..511 sit
+// in lanes 56..63, eight values (four interleaved pairs) per lane, so rotation
+// never leaves the register file.  The KV quantisation block of dims
+// 64b..64b+63 is the lane group 8b..8b+7:
 // its absolute maximum is three DPP steps.
 #include <hip/hip_runtime.h>
 
@@ -62,7 +65,6 @@ __device__ __forceinline__ int ue8m0_exponent(float amax) {
   return e > 127 ? 127 : e;
 }
 
-template <bool NT>
 __device__ __forceinline__ void kv_row(
     int32_t t, const uint16_t* __restrict__ kv,
     const uint16_t* __restrict__ kv_weight, const float* __restrict__ cos_sin,
@@ -76,7 +78,7 @@ __device__ __forceinline__ void kv_row(
   const int64_t pos = positions[t];
   if (pos < 0 || pos >= max_position) return;
 
-  const u32x4_t x = load16<NT>(kv + static_cast<int64_t>(t) * 512 + lane * 8);
+  const u32x4_t x = load16<true>(kv + static_cast<int64_t>(t) * 512 + lane * 8);
   float w[8];
   unpack8(load16<false>(kv_weight + lane * 8), w);
   f32x4_t c = {1.f, 1.f, 1.f, 1.f}, s = {0.f, 0.f, 0.f, 0.f};
@@ -104,17 +106,18 @@ __device__ __forceinline__ void kv_row(
     lo = __builtin_amdgcn_cvt_pk_fp8_f32(v[2], v[3], lo, true);
     uint32_t hi = __builtin_amdgcn_cvt_pk_fp8_f32(v[4], v[5], 0, false);
     hi = __builtin_amdgcn_cvt_pk_fp8_f32(v[6], v[7], hi, true);
-    *reinterpret_cast<u32x2_t*>(row + lane * 8) = u32x2_t{lo, hi};
+    __builtin_nontemporal_store(u32x2_t{lo, hi},
+                                reinterpret_cast<u32x2_t*>(row + lane * 8));
     if ((lane & 7) == 0)
       kv_scale[slot * 8 + (lane >> 3)] = static_cast<uint8_t>(e + 127);
   } else {
     u32x4_t o = {pack_bf16(y[0], y[1]), pack_bf16(y[2], y[3]),
                  pack_bf16(y[4], y[5]), pack_bf16(y[6], y[7])};
-    store16<false>(row + 448 + (lane - kRopeLane0) * 16, o);
+    store16<true>(row + 448 + (lane - kRopeLane0) * 16, o);
   }
 }
 
-template <int WAVES, int QS, bool NT>
+template <int WAVES, int QS>
 __global__ void __launch_bounds__(WAVES * 64) dsv4_prologue_kernel(
     uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
     const uint16_t* __restrict__ q_weight,
@@ -130,7 +133,7 @@ __global__ void __launch_bounds__(WAVES * 64) dsv4_prologue_kernel(
   if (b < kv_blocks) {
     const int32_t t = b * WAVES + wave;
     if (t < num_tokens)
-      kv_row<NT>(t, kv, kv_weight, cos_sin, positions, slot_mapping, kv_cache,
+      kv_row(t, kv, kv_weight, cos_sin, positions, slot_mapping, kv_cache,
                  kv_scale, num_cache_slots, max_position, eps);
     return;
   }
@@ -149,7 +152,7 @@ __global__ void __launch_bounds__(WAVES * 64) dsv4_prologue_kernel(
   for (int s = 0; s < QS; ++s) {
     // heads past the last one re-read head h0 (in bounds) and are not stored
     const int off = (h0 + s < num_heads) ? s * 512 : 0;
-    x[s] = load16<NT>(base + off);
+    x[s] = load16<true>(base + off);
   }
   float w[8];
   unpack8(load16<false>(q_weight + lane * 8), w);
@@ -168,11 +171,11 @@ __global__ void __launch_bounds__(WAVES * 64) dsv4_prologue_kernel(
     if (lane >= kRopeLane0) rotate4(y, c, sn);
     u32x4_t o = {pack_bf16(y[0], y[1]), pack_bf16(y[2], y[3]),
                  pack_bf16(y[4], y[5]), pack_bf16(y[6], y[7])};
-    store16<NT>(base + s * 512, o);
+    store16<true>(base + s * 512, o);
   }
 }
 
-template <int WAVES, int QS, bool NT>
+template <int WAVES, int QS>
 int launch(const PrologueArgs& a, hipStream_t stream) {
   const int32_t waves_per_token = (a.num_heads + QS - 1) / QS;
   const int64_t kv_blocks = (static_cast<int64_t>(a.num_tokens) + WAVES - 1) / WAVES;
@@ -194,7 +197,7 @@ int launch(const PrologueArgs& a, hipStream_t stream) {
       const_cast<int64_t*>(&a.num_cache_slots),
       const_cast<int64_t*>(&a.max_position), const_cast<float*>(&a.eps)};
   hipError_t err = hipLaunchKernel(
-      reinterpret_cast<const void*>(&dsv4_prologue_kernel<WAVES, QS, NT>),
+      reinterpret_cast<const void*>(&dsv4_prologue_kernel<WAVES, QS>),
       dim3(static_cast<uint32_t>(blocks)), dim3(WAVES * 64), args, 0, stream);
   return err == hipSuccess ? FP8KV_OK : FP8KV_ERR_LAUNCH;
 }
@@ -205,25 +208,26 @@ int launch(const PrologueArgs& a, hipStream_t stream) {
 // small-batch kernel: one head per 64-lane block.
 int launch_prologue(const PrologueArgs& a, int waves, int qs, hipStream_t stream) {
 #define FP8KV_SHAPE(W, S)                                            \
-  if (waves == W && qs == S) return launch<W, S, false>(a, stream);
+  if (waves == W && qs == S) return launch<W, S>(a, stream);
   FP8KV_SHAPE(1, 1)
   FP8KV_SHAPE(1, 2)
-  FP8KV_SHAPE(1, 4)
+  FP8KV_SHAPE(2, 1)
   FP8KV_SHAPE(2, 2)
-  FP8KV_SHAPE(2, 4)
   FP8KV_SHAPE(4, 1)
   FP8KV_SHAPE(4, 2)
   FP8KV_SHAPE(4, 4)
-  FP8KV_SHAPE(4, 8)
+  FP8KV_SHAPE(8, 1)
   FP8KV_SHAPE(8, 2)
   FP8KV_SHAPE(8, 4)
+  FP8KV_SHAPE(16, 1)
+  FP8KV_SHAPE(16, 2)
 #undef FP8KV_SHAPE
   return FP8KV_ERR_UNSUPPORTED;
 }
 
 bool prologue_shape_built(int waves, int qs) {
-  static const int shapes[][2] = {{1, 1}, {1, 2}, {1, 4}, {2, 2}, {2, 4}, {4, 1},
-                                  {4, 2}, {4, 4}, {4, 8}, {8, 2}, {8, 4}};
+  static const int shapes[][2] = {{1, 1}, {1, 2}, {2, 1}, {2, 2}, {4, 1}, {4, 2},
+                                  {4, 4}, {8, 1}, {8, 2}, {8, 4}, {16, 1}, {16, 2}};
   for (const auto& s : shapes)
     if (s[0] == waves && s[1] == qs) return true;
   return false;

@@ -63,7 +63,7 @@ __global__ void __launch_bounds__(WAVES * 64) qk_norm_rope_packed_kernel(
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int32_t h = h0 + 4 * u + g;
-      x[u] = load16<false>(base + (h < nh ? h : 0) * 128);  // in bounds
+      x[u] = load16<true>(base + (h < nh ? h : 0) * 128);  // in bounds
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -84,7 +84,7 @@ __global__ void __launch_bounds__(WAVES * 64) qk_norm_rope_packed_kernel(
       if (h < nh) {
         u32x4_t v = {pack_bf16(o[0], o[1]), pack_bf16(o[2], o[3]),
                      pack_bf16(o[4], o[5]), pack_bf16(o[6], o[7])};
-        store16<false>(base + h * 128, v);
+        store16<true>(base + h * 128, v);
       }
     }
   }

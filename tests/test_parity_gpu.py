@@ -124,8 +124,8 @@ def test_every_built_tiling():
     x = I.make_dsv4(w, DEV)
     h = _host(x)
     ref = _oracle(h)
-    shapes = [(1, 1), (1, 2), (1, 4), (2, 2), (2, 4), (4, 1), (4, 2), (4, 4),
-              (4, 8), (8, 2), (8, 4)]
+    shapes = [(1, 1), (1, 2), (2, 1), (2, 2), (4, 1), (4, 2), (4, 4), (8, 1),
+              (8, 2), (8, 4), (16, 1), (16, 2)]
     for wv, qs in shapes:
         _say(f"tiling {wv}x{qs}")
         K.set_tiling(wv, qs)
