@@ -44,10 +44,14 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
+KERNEL_SOURCES = ("dsv4_prologue.hip", "wave_ops.hpp")
+
+
 def kernel_source_hash() -> str:
+    """Hash of the sources the fused prologue kernel is compiled from."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "fp8_kv_cache_slot_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
+    for name in KERNEL_SOURCES:
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(name.encode() + b"\0" + f.read())
     return h.hexdigest()[:16]

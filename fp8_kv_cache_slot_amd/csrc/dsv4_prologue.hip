@@ -125,8 +125,8 @@ __global__ void __launch_bounds__(WAVES * 64) dsv4_prologue_kernel(
     const int64_t* __restrict__ positions,
     const int64_t* __restrict__ slot_mapping, uint8_t* __restrict__ kv_cache,
     uint8_t* __restrict__ kv_scale, int32_t num_tokens, int32_t num_heads,
-    int32_t waves_per_token, int32_t kv_blocks, int64_t num_cache_slots,
-    int64_t max_position, float eps) {
+    int32_t waves_per_token, int32_t q_waves, int32_t kv_blocks,
+    int64_t num_cache_slots, int64_t max_position, float eps) {
   const int lane = lane_id();
   const int wave = wave_id();
   int32_t b = blockIdx.x;
@@ -139,23 +139,39 @@ __global__ void __launch_bounds__(WAVES * 64) dsv4_prologue_kernel(
   }
   b -= kv_blocks;
   const int32_t qwave = b * WAVES + wave;
-  const int32_t t = qwave / waves_per_token;
-  if (t >= num_tokens) return;
-  const int32_t h0 = (qwave - t * waves_per_token) * QS;
-  const int64_t pos = positions[t];
-  if (pos < 0 || pos >= max_position) return;
+  if (qwave >= q_waves) return;
 
-  // Issue every load of this wave before any arithmetic.
-  uint16_t* base = q + (static_cast<int64_t>(t) * num_heads + h0) * 512 + lane * 8;
+  // The streaming loads go out first; index arithmetic, the position load and
+  // its range check overlap them.  When H is a multiple of QS the wave's heads
+  // are the flat rows qwave*QS .. qwave*QS+QS-1 of q viewed as [T*H, 512], so
+  // the address needs no token index at all.
+  const bool dense = (num_heads % QS) == 0;
+  int32_t t = 0, h0 = 0;
+  int64_t row0;
+  if (dense) {
+    row0 = static_cast<int64_t>(qwave) * QS;
+  } else {
+    t = qwave / waves_per_token;
+    h0 = (qwave - t * waves_per_token) * QS;
+    row0 = static_cast<int64_t>(t) * num_heads + h0;
+  }
+  uint16_t* base = q + row0 * 512 + lane * 8;
   u32x4_t x[QS];
 #pragma unroll
   for (int s = 0; s < QS; ++s) {
-    // heads past the last one re-read head h0 (in bounds) and are not stored
-    const int off = (h0 + s < num_heads) ? s * 512 : 0;
-    x[s] = load16<true>(base + off);
+    // heads past the last one re-read the wave's first head (in bounds) and
+    // are not stored
+    const bool ok = dense || h0 + s < num_heads;
+    x[s] = load16<true>(base + (ok ? s * 512 : 0));
   }
   float w[8];
   unpack8(load16<false>(q_weight + lane * 8), w);
+  if (dense) {
+    t = qwave / waves_per_token;
+    h0 = (qwave - t * waves_per_token) * QS;
+  }
+  const int64_t pos = positions[t];
+  if (pos < 0 || pos >= max_position) return;
   f32x4_t c = {1.f, 1.f, 1.f, 1.f}, sn = {0.f, 0.f, 0.f, 0.f};
   if (lane >= kRopeLane0) {
     const float* row = cos_sin + pos * 64 + (lane - kRopeLane0) * 4;
@@ -179,8 +195,9 @@ template <int WAVES, int QS>
 int launch(const PrologueArgs& a, hipStream_t stream) {
   const int32_t waves_per_token = (a.num_heads + QS - 1) / QS;
   const int64_t kv_blocks = (static_cast<int64_t>(a.num_tokens) + WAVES - 1) / WAVES;
-  const int64_t q_waves = static_cast<int64_t>(a.num_tokens) * waves_per_token;
-  const int64_t q_blocks = (q_waves + WAVES - 1) / WAVES;
+  const int64_t q_waves64 = static_cast<int64_t>(a.num_tokens) * waves_per_token;
+  int32_t q_waves = static_cast<int32_t>(q_waves64);
+  const int64_t q_blocks = (q_waves64 + WAVES - 1) / WAVES;
   const int64_t blocks = kv_blocks + q_blocks;
   if (blocks > 0x7FFFFFFF) return FP8KV_ERR_SHAPE;
   int32_t kvb = static_cast<int32_t>(kv_blocks);
@@ -193,7 +210,7 @@ int launch(const PrologueArgs& a, hipStream_t stream) {
       const_cast<const int64_t**>(&a.slot_mapping),
       const_cast<uint8_t**>(&a.kv_cache),    const_cast<uint8_t**>(&a.kv_scale),
       const_cast<int32_t*>(&a.num_tokens),   const_cast<int32_t*>(&a.num_heads),
-      const_cast<int32_t*>(&waves_per_token), &kvb,
+      const_cast<int32_t*>(&waves_per_token), &q_waves, &kvb,
       const_cast<int64_t*>(&a.num_cache_slots),
       const_cast<int64_t*>(&a.max_position), const_cast<float*>(&a.eps)};
   hipError_t err = hipLaunchKernel(
