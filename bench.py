@@ -15,7 +15,8 @@ Prints ONE JSON line:
   cpu_baseline the CPU oracle timed on a bounded token slice of the same
                workload, single-threaded
   extra        the other workloads (131072 x 64, 32768 x 128, decode and tiny
-               latencies, the packed Q/K norm+RoPE at 8192 tokens)
+               latencies, the packed Q/K norm+RoPE at 8192 tokens, the cache
+               read side over all 131072 slots of the 131072 x 64 cache)
 
 Usage: python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--quick]
 """
@@ -258,6 +259,23 @@ def main():
                            "gbps": round(nb / m / 1e9, 1),
                            "pct_of_d2d": round(nb / m / 1e9 / d2d_gbps, 4)}
             log(f"{name}: {extra[name]}")
+            if name == "long64":
+                # read side: every slot of the cache just written, in a
+                # seeded random order
+                g = torch.Generator(device=dev)
+                g.manual_seed(7)
+                slots = torch.randperm(wl.num_pages * 64, generator=g, device=dev)
+                out = torch.empty((slots.shape[0], 512), dtype=torch.bfloat16,
+                                  device=dev)
+                tot, per = time_launches(
+                    lambda: K.kv_cache_gather_dequant(cc, ss, slots, out), 20, 3)
+                m = statistics.median(per)
+                nb = A.dequant_bytes(slots.shape[0], slots.shape[0])
+                extra["dequant_long64"] = {
+                    "rows": int(slots.shape[0]), "bytes": nb,
+                    "median_us": round(m * 1e6, 1), "gbps": round(nb / m / 1e9, 1)}
+                log(f"dequant_long64: {extra['dequant_long64']}")
+                del slots, out
             del xx, qq, cc, ss
             torch.cuda.empty_cache()
         for name in ("tiny", "decode"):

@@ -32,6 +32,7 @@ STATUS = {0: "FP8KV_OK", 1: "FP8KV_ERR_NULL", 2: "FP8KV_ERR_SHAPE",
           5: "FP8KV_ERR_DEVICE", 6: "FP8KV_ERR_LAUNCH"}
 
 EXPORTED = ["qnorm_rope_kv_quant_insert", "qk_norm_rope_packed",
+            "kv_cache_gather_dequant",
             "fp8kv_status_string", "fp8kv_abi_version",
             "fp8kv_set_dispatch_threshold", "fp8kv_get_dispatch_threshold",
             "fp8kv_set_tiling", "fp8kv_get_tiling"]
@@ -64,6 +65,8 @@ def lib() -> ctypes.CDLL:
     L.qk_norm_rope_packed.argtypes = [
         P, I64, I32, I32, I32, I32, F, P, P, P, I32, P, I32, I64, P]
     L.qk_norm_rope_packed.restype = ctypes.c_int
+    L.kv_cache_gather_dequant.argtypes = [P, P, I64, I32, P, I64, P, P]
+    L.kv_cache_gather_dequant.restype = ctypes.c_int
     L.fp8kv_status_string.argtypes = [ctypes.c_int]
     L.fp8kv_status_string.restype = ctypes.c_char_p
     L.fp8kv_abi_version.argtypes = []
@@ -163,6 +166,30 @@ def qk_norm_rope_packed(qkv, num_heads_q: int, num_heads_k: int,
         _stream(stream))
     if st:
         raise Fp8kvError(st, "qk_norm_rope_packed")
+
+
+def kv_cache_gather_dequant(kv_cache, kv_scale, slots, out=None,
+                            stream=None):
+    """Gather rows of the paged FP8/UE8M0 cache by slot and dequantise them
+    to bf16 [N, 512]; invalid slots give zero rows.  Returns ``out``."""
+    _check(kv_cache, "kv_cache", torch.uint8)
+    if kv_cache.dim() != 3 or kv_cache.shape[2] != ROW_BYTES:
+        raise ValueError("kv_cache must be [num_pages, page_size, 576]")
+    pages, page_size, _ = kv_cache.shape
+    _check(kv_scale, "kv_scale", torch.uint8, (pages, page_size, SCALE_BYTES))
+    if slots.dim() != 1:
+        raise ValueError("slots must be one-dimensional")
+    _check(slots, "slots", torch.int64)
+    n = slots.shape[0]
+    if out is None:
+        out = torch.empty((n, HEAD_DIM), dtype=torch.bfloat16, device=slots.device)
+    _check(out, "out", torch.bfloat16, (n, HEAD_DIM))
+    st = lib().kv_cache_gather_dequant(
+        kv_cache.data_ptr(), kv_scale.data_ptr(), pages, page_size,
+        slots.data_ptr(), n, out.data_ptr(), _stream(stream))
+    if st:
+        raise Fp8kvError(st, "kv_cache_gather_dequant")
+    return out
 
 
 def set_dispatch_threshold(programs: int) -> None:

@@ -7,6 +7,10 @@ and the slot index (8 + 8 B), one cos/sin row shared by all heads (64 fp32 =
 the 64 bf16 rotary dims (128 B) and 7 exponent bytes; plus both weight vectors
 once (2 * 1024 B).
 
+Cache read side (gather + dequantise), per output row: the slot index (8 B)
+and the bf16 row written (1024 B); per row whose slot is valid also the 576
+cache bytes and the 7 exponent bytes read.
+
 Packed Q/K norm+RoPE, per token: the Q and K heads read + written
 (2 * 2 * (Hq + Hk) * D B), the position (8 B) and one cos/sin row (4 * D B);
 the V heads are never touched; plus both weight vectors once (2 * 2 * D B).
@@ -36,3 +40,7 @@ def packed_bytes(num_tokens: int, num_heads_q: int, num_heads_k: int,
                  head_dim: int) -> int:
     per_token = 4 * (num_heads_q + num_heads_k) * head_dim + 8 + 4 * head_dim
     return num_tokens * per_token + 2 * 2 * head_dim
+
+
+def dequant_bytes(num_rows: int, num_valid: int) -> int:
+    return num_rows * (8 + 2 * HEAD_DIM) + num_valid * (448 + 2 * ROPE_DIM + 7)

@@ -19,7 +19,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libfp8kv.so")
-SOURCES = ["capi.hip", "dsv4_prologue.hip", "qk_norm_rope_packed.hip"]
+SOURCES = ["capi.hip", "dsv4_prologue.hip", "qk_norm_rope_packed.hip",
+           "kv_cache_dequant.hip"]
 ARCH = "gfx950"
 
 

@@ -121,6 +121,26 @@ FP8KV_API int qk_norm_rope_packed(
   return launch_packed(a, static_cast<hipStream_t>(stream));
 }
 
+FP8KV_API int kv_cache_gather_dequant(const uint8_t* kv_cache,
+                                     const uint8_t* kv_scale, int64_t num_pages,
+                                     int32_t page_size, const int64_t* slots,
+                                     int64_t num_rows, void* out, void* stream) {
+  using namespace fp8kv;
+  int st = validate_gather_dequant(kv_cache, kv_scale, num_pages, page_size,
+                                   slots, num_rows, out);
+  if (st != FP8KV_OK || num_rows == 0) return st;
+  st = check_device();
+  if (st != FP8KV_OK) return st;
+  DequantArgs a;
+  a.kv_cache = kv_cache;
+  a.kv_scale = kv_scale;
+  a.slots = slots;
+  a.out = static_cast<uint16_t*>(out);
+  a.num_rows = static_cast<int32_t>(num_rows);
+  a.num_cache_slots = num_pages * kPageSize;
+  return launch_gather_dequant(a, static_cast<hipStream_t>(stream));
+}
+
 FP8KV_API const char* fp8kv_status_string(int status) {
   switch (status) {
     case FP8KV_OK: return "ok";

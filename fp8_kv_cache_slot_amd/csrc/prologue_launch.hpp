@@ -40,11 +40,21 @@ struct PackedArgs {
   float eps;
 };
 
+struct DequantArgs {
+  const uint8_t* kv_cache;
+  const uint8_t* kv_scale;
+  const int64_t* slots;
+  uint16_t* out;
+  int32_t num_rows;
+  int64_t num_cache_slots;  // num_pages * 64
+};
+
 // Launch the fused prologue with `waves` 64-lane waves per block and `qs`
 // Q heads per wave.  Returns FP8KV_ERR_UNSUPPORTED for a shape not built.
 int launch_prologue(const PrologueArgs& a, int waves, int qs, hipStream_t stream);
 bool prologue_shape_built(int waves, int qs);
 
 int launch_packed(const PackedArgs& a, hipStream_t stream);
+int launch_gather_dequant(const DequantArgs& a, hipStream_t stream);
 
 }  // namespace fp8kv

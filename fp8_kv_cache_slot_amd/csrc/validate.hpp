@@ -82,4 +82,21 @@ inline int validate_packed(const void* qkv, int64_t num_tokens,
   return FP8KV_OK;
 }
 
+inline int validate_gather_dequant(const uint8_t* kv_cache,
+                                   const uint8_t* kv_scale, int64_t num_pages,
+                                   int32_t page_size, const int64_t* slots,
+                                   int64_t num_rows, const void* out) {
+  if (num_pages < 0 || num_rows < 0 || num_rows > 0x7FFFFFFF ||
+      num_pages > (int64_t{1} << 40))
+    return FP8KV_ERR_SHAPE;
+  if (page_size != kPageSize) return FP8KV_ERR_UNSUPPORTED;
+  if (num_rows == 0) return FP8KV_OK;
+  if (!slots || !out) return FP8KV_ERR_NULL;
+  if (num_pages > 0 && (!kv_cache || !kv_scale)) return FP8KV_ERR_NULL;
+  if (!aligned(slots, 8) || !aligned(out, 16) ||
+      (kv_cache && !aligned(kv_cache, 16)) || (kv_scale && !aligned(kv_scale, 8)))
+    return FP8KV_ERR_ALIGN;
+  return FP8KV_OK;
+}
+
 }  // namespace fp8kv

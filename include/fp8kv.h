@@ -149,6 +149,31 @@ int qk_norm_rope_packed(
     const int64_t* position_ids, int32_t forced_token_heads_per_warp,
     int64_t max_position, void* stream);
 
+/*
+ * Read side of the paged cache written by qnorm_rope_kv_quant_insert: gather
+ * rows by slot and dequantise them to bf16 (the inverse the cache layout of
+ * FlagGems PR #5449 "Performance" implies: FP8 codes with seven per-block
+ * power-of-two exponents per token).
+ *
+ *   kv_cache   uint8 [num_pages, page_size, 576], layout as above.  16-B aligned.
+ *   kv_scale   uint8 [num_pages, page_size, 8].  8-byte aligned.
+ *   page_size  must be 64 (else FP8KV_ERR_UNSUPPORTED).
+ *   slots      int64 [num_rows]: the flat slot of each output row.  A negative
+ *              slot or one >= num_pages * page_size yields a row of +0.
+ *   out        bf16 [num_rows, 512], written (16-byte aligned):
+ *                out[i, d]       = E4M3(code[s, d]) * 2^(scale[s, d/64] - 127)
+ *                                  for d < 448, rounded to bf16 (exact unless
+ *                                  the exponent leaves bf16's range)
+ *                out[i, 448 + j] = the stored bf16 rotary value j.
+ * Errors: num_rows < 0 or >= 2^31, num_pages < 0 -> FP8KV_ERR_SHAPE; NULL
+ * slots/out, or NULL cache/scale with num_pages > 0 -> FP8KV_ERR_NULL;
+ * misalignment -> FP8KV_ERR_ALIGN.  num_rows == 0 returns FP8KV_OK.
+ */
+int kv_cache_gather_dequant(const uint8_t* kv_cache, const uint8_t* kv_scale,
+                            int64_t num_pages, int32_t page_size,
+                            const int64_t* slots, int64_t num_rows, void* out,
+                            void* stream);
+
 /* Static text for a status code (never NULL). */
 const char* fp8kv_status_string(int status);
 

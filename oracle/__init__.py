@@ -49,6 +49,8 @@ def _load():
     lib.oracle_qnorm_rope_kv_quant_insert.restype = None
     lib.oracle_kv_normalised.argtypes = [P, P, P, P, I64, D, P]
     lib.oracle_kv_normalised.restype = None
+    lib.oracle_kv_cache_gather_dequant.argtypes = [P, P, P, I64, I64, P]
+    lib.oracle_kv_cache_gather_dequant.restype = None
     lib.oracle_qk_norm_rope_packed.argtypes = [
         P, I64, I32, I32, I32, I32, D, P, P, P, P]
     lib.oracle_qk_norm_rope_packed.restype = None
@@ -128,6 +130,19 @@ def kv_normalised(kv, kv_weight, cos_sin_cache, positions, eps):
         _ptr(cos_sin_cache, np.float32), _ptr(positions, np.int64), T,
         float(eps), _ptr(y, np.float64, True))
     return y
+
+
+def kv_cache_gather_dequant(kv_cache, kv_scale, slots):
+    """bf16 bit patterns [N, 512] of the dequantised rows of ``slots``."""
+    pages = kv_cache.shape[0]
+    if kv_cache.shape != (pages, 64, 576) or kv_scale.shape != (pages, 64, 8):
+        raise ValueError("cache must be [pages,64,576], scale [pages,64,8]")
+    slots = np.ascontiguousarray(slots, np.int64)
+    out = np.empty((slots.shape[0], 512), np.uint16)
+    _load().oracle_kv_cache_gather_dequant(
+        _ptr(kv_cache, np.uint8), _ptr(kv_scale, np.uint8), _ptr(slots, np.int64),
+        slots.shape[0], pages, _ptr(out, np.uint16, True))
+    return out
 
 
 def qk_norm_rope_packed(qkv, num_heads_q, num_heads_k, num_heads_v, head_dim,

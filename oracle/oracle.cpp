@@ -240,6 +240,30 @@ void oracle_kv_normalised(const uint16_t* kv, const uint16_t* kv_weight,
   }
 }
 
+void oracle_kv_cache_gather_dequant(const uint8_t* kv_cache,
+                                    const uint8_t* kv_scale,
+                                    const int64_t* slots, int64_t num_rows,
+                                    int64_t num_pages, uint16_t* out) {
+  const int64_t num_slots = num_pages * kPageSize;
+  for (int64_t i = 0; i < num_rows; ++i) {
+    uint16_t* dst = out + i * kHeadDim;
+    const int64_t slot = slots[i];
+    if (slot < 0 || slot >= num_slots) {
+      for (int d = 0; d < kHeadDim; ++d) dst[d] = 0;
+      continue;
+    }
+    const uint8_t* row = kv_cache + slot * kRowBytes;
+    const uint8_t* scale = kv_scale + slot * kScaleBytes;
+    for (int d = 0; d < kRopeStart; ++d) {
+      const int e = static_cast<int>(scale[d / kQuantBlock]) - 127;
+      dst[d] = oracle_bf16_rne(std::ldexp(oracle_e4m3_decode(row[d]), e));
+    }
+    for (int j = 0; j < kRopeDim; ++j)
+      dst[kRopeStart + j] = static_cast<uint16_t>(
+          row[kRopeStart + 2 * j] | (row[kRopeStart + 2 * j + 1] << 8));
+  }
+}
+
 void oracle_qk_norm_rope_packed(
     uint16_t* qkv, int64_t num_tokens, int32_t num_heads_q,
     int32_t num_heads_k, int32_t num_heads_v, int32_t head_dim, double eps,

@@ -90,6 +90,22 @@ void oracle_kv_normalised(const uint16_t* kv, const uint16_t* kv_weight,
                           const float* cos_sin_cache, const int64_t* positions,
                           int64_t num_tokens, double eps, double* y_out);
 
+/* ---- read side of the cache ------------------------------------------------ */
+/*
+ * Gather rows of the paged FP8/UE8M0 cache by slot and dequantise them:
+ *   out[i, d]       = E4M3(kv_cache[s, d]) * 2^(kv_scale[s, d / 64] - 127), d < 448
+ *   out[i, 448 + j] = the stored bf16 rotary value j
+ * with s = slots[i]; a negative slot or one >= num_pages * 64 gives a row of
+ * +0.  out is bf16 [N, 512] (uint16 patterns), rounded to nearest even from
+ * the exact double product (exact in practice: an E4M3 value has 4 significant
+ * bits).  This is the inverse the fused prologue's cache layout implies
+ * ([P1] "Performance": seven per-block power-of-two exponents per token).
+ */
+void oracle_kv_cache_gather_dequant(const uint8_t* kv_cache,
+                                    const uint8_t* kv_scale,
+                                    const int64_t* slots, int64_t num_rows,
+                                    int64_t num_pages, uint16_t* out);
+
 /* ---- entry 2: packed-QKV FusedQkNormRope ([P3] "Summary") ---------------- */
 /*
  *   qkv           bf16 [T, (Hq + Hk + Hv) * D], Q and K heads rewritten in

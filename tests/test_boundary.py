@@ -96,12 +96,34 @@ def test_packed_argument_errors(over, want):
     assert _packed(**over) == want
 
 
+def _dequant(**over):
+    a = dict(cache=FAKE, scale=FAKE, pages=2, page=64, slots=FAKE, rows=10,
+             out=FAKE, stream=None)
+    a.update(over)
+    return K.lib().kv_cache_gather_dequant(*a.values())
+
+
+@pytest.mark.parametrize("over,want", [
+    (dict(rows=-1), 2), (dict(pages=-1), 2), (dict(rows=1 << 31), 2),
+    (dict(page=32), 3),
+    (dict(slots=None), 1), (dict(out=None), 1), (dict(cache=None), 1),
+    (dict(scale=None), 1),
+    (dict(slots=FAKE + 4), 4), (dict(out=FAKE + 8), 4), (dict(cache=FAKE + 8), 4),
+    (dict(scale=FAKE + 4), 4),
+    (dict(rows=0, slots=None, out=None), 0),
+])
+def test_dequant_argument_errors(over, want):
+    assert _dequant(**over) == want
+
+
 @pytest.mark.skipif(torch.cuda.device_count() > 0, reason="a GPU is present")
 def test_no_device_is_reported_not_launched():
     # valid-looking arguments reach the device check, which fails without a
     # GPU; nothing is dereferenced
     assert _prologue() == 5
     assert _packed() == 5
+    assert _dequant() == 5
+    assert _dequant(pages=0, cache=None, scale=None) == 5
 
 
 def test_knobs():
