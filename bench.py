@@ -16,7 +16,9 @@ Prints ONE JSON line:
                workload, single-threaded
   extra        the other workloads (131072 x 64, 32768 x 128, decode and tiny
                latencies, the packed Q/K norm+RoPE at 8192 tokens, the cache
-               read side over all 131072 slots of the 131072 x 64 cache)
+               read side over all 131072 slots of the 131072 x 64 cache, and
+               the same prologue as five separate launches, the unfused
+               baseline, with the fusion speedup)
 
 Usage: python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--quick]
 """
@@ -201,7 +203,20 @@ def main():
             "median_launch_us": round(statistics.median(per) * 1e6, 2),
         },
     }
-    del q, cache, scale
+    # ---- the same call as five separate launches (the unfused baseline) ----
+    kv_work = torch.empty((w.num_tokens, 512), dtype=torch.bfloat16, device=dev)
+
+    def unfused():
+        K.unfused_prologue(q, x["kv"], x["q_weight"], x["kv_weight"],
+                           x["cos_sin_cache"], x["positions"], x["slot_mapping"],
+                           cache, scale, x["eps"], kv_work=kv_work)
+    _, uper = time_launches(unfused, 20, 3)
+    unfused_prefill = {"median_us": round(statistics.median(uper) * 1e6, 1),
+                       "fused_median_us": round(statistics.median(per) * 1e6, 1),
+                       "fusion_speedup": round(statistics.median(uper) /
+                                               statistics.median(per), 3)}
+    log(f"unfused prefill: {unfused_prefill}")
+    del q, cache, scale, kv_work
 
     # ---- CPU baseline: the oracle on a bounded slice of the same workload --
     if not (args.quick or args.no_cpu_baseline):
@@ -278,6 +293,7 @@ def main():
                 del slots, out
             del xx, qq, cc, ss
             torch.cuda.empty_cache()
+        extra["unfused_prefill"] = unfused_prefill
         for name in ("tiny", "decode"):
             wl = I.DSV4_WORKLOADS[name]
             xx = I.make_dsv4(wl, dev)
@@ -285,9 +301,17 @@ def main():
             nb = workload_bytes(wl, xx)
             tot, per = time_launches(lambda: call(xx, qq, cc, ss), 50, 10)
             m = statistics.median(per)
+            kw = torch.empty((wl.num_tokens, 512), dtype=torch.bfloat16, device=dev)
+            _, uper = time_launches(lambda: K.unfused_prologue(
+                qq, xx["kv"], xx["q_weight"], xx["kv_weight"], xx["cos_sin_cache"],
+                xx["positions"], xx["slot_mapping"], cc, ss, xx["eps"], kv_work=kw),
+                50, 10)
+            um = statistics.median(uper)
             extra[name] = {"tokens": wl.num_tokens, "heads": wl.num_heads,
                            "bytes": nb, "median_us": round(m * 1e6, 2),
-                           "gbps": round(nb / m / 1e9, 1)}
+                           "gbps": round(nb / m / 1e9, 1),
+                           "unfused_median_us": round(um * 1e6, 2),
+                           "fusion_speedup": round(um / m, 3)}
             log(f"{name}: {extra[name]}")
         pw = I.PACKED_WORKLOADS["packed_t8192"]
         px = I.make_packed(pw, dev)

@@ -32,7 +32,8 @@ STATUS = {0: "FP8KV_OK", 1: "FP8KV_ERR_NULL", 2: "FP8KV_ERR_SHAPE",
           5: "FP8KV_ERR_DEVICE", 6: "FP8KV_ERR_LAUNCH"}
 
 EXPORTED = ["qnorm_rope_kv_quant_insert", "qk_norm_rope_packed",
-            "kv_cache_gather_dequant",
+            "kv_cache_gather_dequant", "rms_norm_rows", "rope_rows",
+            "kv_quant_insert",
             "fp8kv_status_string", "fp8kv_abi_version",
             "fp8kv_set_dispatch_threshold", "fp8kv_get_dispatch_threshold",
             "fp8kv_set_tiling", "fp8kv_get_tiling"]
@@ -67,6 +68,12 @@ def lib() -> ctypes.CDLL:
     L.qk_norm_rope_packed.restype = ctypes.c_int
     L.kv_cache_gather_dequant.argtypes = [P, P, I64, I32, P, I64, P, P]
     L.kv_cache_gather_dequant.restype = ctypes.c_int
+    L.rms_norm_rows.argtypes = [P, P, P, I64, I32, F, P]
+    L.rms_norm_rows.restype = ctypes.c_int
+    L.rope_rows.argtypes = [P, P, P, I64, I32, I32, I32, I64, P]
+    L.rope_rows.restype = ctypes.c_int
+    L.kv_quant_insert.argtypes = [P, P, P, P, I64, I64, I32, P]
+    L.kv_quant_insert.restype = ctypes.c_int
     L.fp8kv_status_string.argtypes = [ctypes.c_int]
     L.fp8kv_status_string.restype = ctypes.c_char_p
     L.fp8kv_abi_version.argtypes = []
@@ -190,6 +197,78 @@ def kv_cache_gather_dequant(kv_cache, kv_scale, slots, out=None,
     if st:
         raise Fp8kvError(st, "kv_cache_gather_dequant")
     return out
+
+
+def rms_norm_rows(x, weight, eps: float = 1e-6, out=None, stream=None):
+    """bf16 rows [..., 512] -> normalised, weighted bf16 rows (``out`` may be
+    ``x`` for an in-place update).  Returns ``out``."""
+    _check(x, "x", torch.bfloat16)
+    if x.shape[-1] != HEAD_DIM:
+        raise ValueError("rows must be 512 wide")
+    _check(weight, "weight", torch.bfloat16, (HEAD_DIM,))
+    if out is None:
+        out = torch.empty_like(x)
+    _check(out, "out", torch.bfloat16, tuple(x.shape))
+    st = lib().rms_norm_rows(x.data_ptr(), out.data_ptr(), weight.data_ptr(),
+                             x.numel() // HEAD_DIM, HEAD_DIM, float(eps),
+                             _stream(stream))
+    if st:
+        raise Fp8kvError(st, "rms_norm_rows")
+    return out
+
+
+def rope_rows(x, cos_sin_cache, positions, stream=None) -> None:
+    """In place: interleaved RoPE on dims 448..511 of bf16 x [T, R, 512]."""
+    if x.dim() != 3:
+        raise ValueError("x must be [T, rows_per_token, 512]")
+    T, R, D = x.shape
+    _check(x, "x", torch.bfloat16)
+    _check(cos_sin_cache, "cos_sin_cache", torch.float32)
+    if cos_sin_cache.dim() != 2:
+        raise ValueError("cos_sin_cache must be [max_position, 64]")
+    _check(positions, "positions", torch.int64, (T,))
+    st = lib().rope_rows(x.data_ptr(), cos_sin_cache.data_ptr(),
+                         positions.data_ptr(), T, R, D, cos_sin_cache.shape[1],
+                         cos_sin_cache.shape[0], _stream(stream))
+    if st:
+        raise Fp8kvError(st, "rope_rows")
+
+
+def kv_quant_insert(kv, slot_mapping, kv_cache, kv_scale, stream=None) -> None:
+    """Quantise already normalised + rotated bf16 KV rows [T, 512] into the
+    paged cache (the fused call's quantiser, as its own launch)."""
+    if kv.dim() != 2:
+        raise ValueError("kv must be [T, 512]")
+    T = kv.shape[0]
+    _check(kv, "kv", torch.bfloat16, (T, HEAD_DIM))
+    _check(slot_mapping, "slot_mapping", torch.int64, (T,))
+    _check(kv_cache, "kv_cache", torch.uint8)
+    if kv_cache.dim() != 3 or kv_cache.shape[2] != ROW_BYTES:
+        raise ValueError("kv_cache must be [num_pages, page_size, 576]")
+    pages, page_size, _ = kv_cache.shape
+    _check(kv_scale, "kv_scale", torch.uint8, (pages, page_size, SCALE_BYTES))
+    st = lib().kv_quant_insert(kv.data_ptr(), slot_mapping.data_ptr(),
+                               kv_cache.data_ptr(), kv_scale.data_ptr(), T,
+                               pages, page_size, _stream(stream))
+    if st:
+        raise Fp8kvError(st, "kv_quant_insert")
+
+
+def unfused_prologue(q, kv, q_weight, kv_weight, cos_sin_cache, positions,
+                     slot_mapping, kv_cache, kv_scale, eps: float = 1e-6,
+                     kv_work=None, stream=None) -> None:
+    """The prologue as five separate launches (norm q, norm kv into a work
+    buffer, rope q, rope kv, quantise+insert): the unfused baseline.  Same
+    arguments as :func:`qnorm_rope_kv_quant_insert`; ``kv_work`` is an
+    optional bf16 [T, 512] scratch tensor."""
+    T, H, D = q.shape
+    if kv_work is None:
+        kv_work = torch.empty((T, D), dtype=torch.bfloat16, device=q.device)
+    rms_norm_rows(q, q_weight, eps, out=q, stream=stream)
+    rms_norm_rows(kv, kv_weight, eps, out=kv_work, stream=stream)
+    rope_rows(q, cos_sin_cache, positions, stream=stream)
+    rope_rows(kv_work.view(T, 1, D), cos_sin_cache, positions, stream=stream)
+    kv_quant_insert(kv_work, slot_mapping, kv_cache, kv_scale, stream=stream)
 
 
 def set_dispatch_threshold(programs: int) -> None:

@@ -141,6 +141,52 @@ FP8KV_API int kv_cache_gather_dequant(const uint8_t* kv_cache,
   return launch_gather_dequant(a, static_cast<hipStream_t>(stream));
 }
 
+FP8KV_API int rms_norm_rows(const void* x, void* out, const void* weight,
+                            int64_t num_rows, int32_t row_dim, float eps,
+                            void* stream) {
+  using namespace fp8kv;
+  int st = validate_rms_norm_rows(x, out, weight, num_rows, row_dim);
+  if (st != FP8KV_OK || num_rows == 0) return st;
+  st = check_device();
+  if (st != FP8KV_OK) return st;
+  return launch_rms_norm_rows(static_cast<const uint16_t*>(x),
+                              static_cast<uint16_t*>(out),
+                              static_cast<const uint16_t*>(weight), num_rows, eps,
+                              static_cast<hipStream_t>(stream));
+}
+
+FP8KV_API int rope_rows(void* x, const float* cos_sin_cache,
+                        const int64_t* positions, int64_t num_tokens,
+                        int32_t rows_per_token, int32_t row_dim, int32_t rope_dim,
+                        int64_t max_position, void* stream) {
+  using namespace fp8kv;
+  int st = validate_rope_rows(x, cos_sin_cache, positions, num_tokens,
+                              rows_per_token, row_dim, rope_dim, max_position);
+  if (st != FP8KV_OK || num_tokens == 0) return st;
+  st = check_device();
+  if (st != FP8KV_OK) return st;
+  return launch_rope_rows(static_cast<uint16_t*>(x), cos_sin_cache, positions,
+                          num_tokens, rows_per_token, max_position,
+                          static_cast<hipStream_t>(stream));
+}
+
+FP8KV_API int kv_quant_insert(const void* kv, const int64_t* slot_mapping,
+                              uint8_t* kv_cache, uint8_t* kv_scale,
+                              int64_t num_tokens, int64_t num_pages,
+                              int32_t page_size, void* stream) {
+  using namespace fp8kv;
+  int st = validate_kv_quant_insert(kv, slot_mapping, kv_cache, kv_scale,
+                                    num_tokens, num_pages, page_size);
+  if (st != FP8KV_OK || num_tokens == 0) return st;
+  st = check_device();
+  if (st != FP8KV_OK) return st;
+  return launch_kv_quant_insert(static_cast<const uint16_t*>(kv), slot_mapping,
+                                kv_cache, kv_scale,
+                                static_cast<int32_t>(num_tokens),
+                                num_pages * kPageSize,
+                                static_cast<hipStream_t>(stream));
+}
+
 FP8KV_API const char* fp8kv_status_string(int status) {
   switch (status) {
     case FP8KV_OK: return "ok";

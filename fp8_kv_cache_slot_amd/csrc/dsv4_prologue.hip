@@ -25,6 +25,7 @@
 
 #include <cstdint>
 
+#include "kv_quant.hpp"
 #include "prologue_launch.hpp"
 #include "wave_ops.hpp"
 
@@ -54,17 +55,6 @@ __device__ __forceinline__ void rotate4(float* y, f32x4_t c, f32x4_t s) {
   }
 }
 
-// Smallest e with amax <= 448 * 2^e, clamped to [-127, 127]; 0 -> -127.
-// Exact: amax = m 2^k with m in [0.5, 1) and 448 = 0.875 2^9.
-__device__ __forceinline__ int ue8m0_exponent(float amax) {
-  if (!(amax > 0.0f)) return -127;
-  const int k = __builtin_amdgcn_frexp_expf(amax);
-  const float m = __builtin_amdgcn_frexp_mantf(amax);
-  int e = k - 9 + (m > 0.875f ? 1 : 0);
-  e = e < -127 ? -127 : e;
-  return e > 127 ? 127 : e;
-}
-
 __device__ __forceinline__ void kv_row(
     int32_t t, const uint16_t* __restrict__ kv,
     const uint16_t* __restrict__ kv_weight, const float* __restrict__ cos_sin,
@@ -91,30 +81,7 @@ __device__ __forceinline__ void kv_row(
   rms_normalise(x, w, eps, y);
   if (lane >= kRopeLane0) rotate4(y, c, s);
 
-  float amax = 0.0f;
-#pragma unroll
-  for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(y[j]));
-  amax = group8_max(amax);
-  const int e = ue8m0_exponent(amax);
-
-  uint8_t* row = kv_cache + slot * 576;
-  if (lane < kRopeLane0) {
-    float v[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) v[j] = __builtin_ldexpf(y[j], -e);  // exact
-    uint32_t lo = __builtin_amdgcn_cvt_pk_fp8_f32(v[0], v[1], 0, false);
-    lo = __builtin_amdgcn_cvt_pk_fp8_f32(v[2], v[3], lo, true);
-    uint32_t hi = __builtin_amdgcn_cvt_pk_fp8_f32(v[4], v[5], 0, false);
-    hi = __builtin_amdgcn_cvt_pk_fp8_f32(v[6], v[7], hi, true);
-    __builtin_nontemporal_store(u32x2_t{lo, hi},
-                                reinterpret_cast<u32x2_t*>(row + lane * 8));
-    if ((lane & 7) == 0)
-      kv_scale[slot * 8 + (lane >> 3)] = static_cast<uint8_t>(e + 127);
-  } else {
-    u32x4_t o = {pack_bf16(y[0], y[1]), pack_bf16(y[2], y[3]),
-                 pack_bf16(y[4], y[5]), pack_bf16(y[6], y[7])};
-    store16<true>(row + 448 + (lane - kRopeLane0) * 16, o);
-  }
+  quantise_store_row(y, lane, kv_cache + slot * 576, kv_scale + slot * 8);
 }
 
 template <int WAVES, int QS>

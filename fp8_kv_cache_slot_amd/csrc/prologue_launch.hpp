@@ -57,4 +57,14 @@ bool prologue_shape_built(int waves, int qs);
 int launch_packed(const PackedArgs& a, hipStream_t stream);
 int launch_gather_dequant(const DequantArgs& a, hipStream_t stream);
 
+// The prologue's stages as separate launches (the unfused baseline).
+int launch_rms_norm_rows(const uint16_t* x, uint16_t* out, const uint16_t* weight,
+                         int64_t num_rows, float eps, hipStream_t stream);
+int launch_rope_rows(uint16_t* x, const float* cos_sin, const int64_t* positions,
+                     int64_t num_tokens, int32_t rows_per_token,
+                     int64_t max_position, hipStream_t stream);
+int launch_kv_quant_insert(const uint16_t* kv, const int64_t* slot_mapping,
+                           uint8_t* kv_cache, uint8_t* kv_scale, int32_t num_tokens,
+                           int64_t num_cache_slots, hipStream_t stream);
+
 }  // namespace fp8kv

@@ -1,0 +1,150 @@
+// The DeepSeek-V4 prologue taken apart into separate launches, the unfused
+// baseline the fused kernel is measured against (FlagGems PR #5449
+// "Performance": one fused launch against the baseline's two; InfiniOps PR
+// #1019 "Benchmark / Performance Impact": separate RmsNorm and
+// RotaryEmbedding calls).  Each stage reads and writes bf16 in HBM:
+//
+//   rms_norm_rows    out[r, :] = bf16(x[r, :] / rms(x[r, :]) * w), rows of 512
+//   rope_rows        in place, interleaved pairs on dims 448..511 of every
+//                    row of token t, rotated by cos_sin_cache[positions[t]]
+//   kv_quant_insert  already normalised and rotated bf16 KV rows -> FP8 E4M3
+//                    codes + 7 UE8M0 exponents + bf16 rotary dims, scattered
+//                    through slot_mapping (the fused kernel's own quantiser)
+//
+// The layouts follow the fused kernel: a 512-wide row is one 16-byte vector
+// per lane of a wave; the 64 rotary dims of a row are 8 lanes x 16 bytes, so
+// the RoPE stage covers 8 rows per wave and touches only those 128 bytes.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "kv_quant.hpp"
+#include "prologue_launch.hpp"
+#include "wave_ops.hpp"
+
+namespace fp8kv {
+namespace {
+
+constexpr int kWaves = 4;
+constexpr int kRowsPerWave = 2;
+
+template <int RS>
+__global__ void __launch_bounds__(kWaves * 64) rms_norm_rows_kernel(
+    const uint16_t* x, uint16_t* out, const uint16_t* __restrict__ weight,
+    int64_t num_rows, float eps) {
+  // x and out may be the same buffer: each lane reads and then writes only
+  // its own 16 bytes.
+  const int lane = lane_id();
+  const int64_t first =
+      (static_cast<int64_t>(blockIdx.x) * kWaves + wave_id()) * RS;
+  if (first >= num_rows) return;
+  u32x4_t v[RS];
+#pragma unroll
+  for (int r = 0; r < RS; ++r) {
+    const int64_t row = first + r < num_rows ? first + r : first;
+    v[r] = load16<true>(x + row * 512 + lane * 8);
+  }
+  float w[8];
+  unpack8(load16<false>(weight + lane * 8), w);
+#pragma unroll
+  for (int r = 0; r < RS; ++r) {
+    if (first + r >= num_rows) break;
+    float f[8];
+    unpack8(v[r], f);
+    const float ss = wave64_sum(sum_sq8(f));
+    const float rr = __builtin_amdgcn_rsqf(fmaf(ss, 1.0f / 512.0f, eps));
+    float y[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) y[j] = f[j] * rr * w[j];
+    u32x4_t o = {pack_bf16(y[0], y[1]), pack_bf16(y[2], y[3]),
+                 pack_bf16(y[4], y[5]), pack_bf16(y[6], y[7])};
+    store16<true>(out + (first + r) * 512 + lane * 8, o);
+  }
+}
+
+__global__ void __launch_bounds__(kWaves * 64) rope_rows_kernel(
+    uint16_t* __restrict__ x, const float* __restrict__ cos_sin,
+    const int64_t* __restrict__ positions, int64_t num_rows,
+    int32_t rows_per_token, int64_t max_position) {
+  // 8 lanes per row: lane j of the group holds pairs 4j..4j+3 (dims
+  // 448 + 8j .. 455 + 8j).
+  const int lane = lane_id();
+  const int64_t row =
+      (static_cast<int64_t>(blockIdx.x) * kWaves + wave_id()) * 8 + (lane >> 3);
+  if (row >= num_rows) return;
+  const int j = lane & 7;
+  uint16_t* p = x + row * 512 + 448 + j * 8;
+  const u32x4_t v = *reinterpret_cast<const u32x4_t*>(p);
+  const int64_t t = row / rows_per_token;
+  const int64_t pos = positions[t];
+  if (pos < 0 || pos >= max_position) return;
+  const f32x4_t c = load16f(cos_sin + pos * 64 + j * 4);
+  const f32x4_t s = load16f(cos_sin + pos * 64 + 32 + j * 4);
+  float y[8];
+  unpack8(v, y);
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const float a = y[2 * k], b = y[2 * k + 1];
+    y[2 * k] = a * c[k] - b * s[k];
+    y[2 * k + 1] = b * c[k] + a * s[k];
+  }
+  *reinterpret_cast<u32x4_t*>(p) =
+      u32x4_t{pack_bf16(y[0], y[1]), pack_bf16(y[2], y[3]),
+              pack_bf16(y[4], y[5]), pack_bf16(y[6], y[7])};
+}
+
+__global__ void __launch_bounds__(kWaves * 64) kv_quant_insert_kernel(
+    const uint16_t* __restrict__ kv, const int64_t* __restrict__ slot_mapping,
+    uint8_t* __restrict__ kv_cache, uint8_t* __restrict__ kv_scale,
+    int32_t num_tokens, int64_t num_cache_slots) {
+  const int lane = lane_id();
+  const int32_t t = static_cast<int32_t>(blockIdx.x) * kWaves + wave_id();
+  if (t >= num_tokens) return;
+  const int64_t slot = slot_mapping[t];
+  if (slot < 0 || slot >= num_cache_slots) return;
+  float y[8];
+  unpack8(load16<true>(kv + static_cast<int64_t>(t) * 512 + lane * 8), y);
+  quantise_store_row(y, lane, kv_cache + slot * 576, kv_scale + slot * 8);
+}
+
+int to_status(hipError_t e) { return e == hipSuccess ? FP8KV_OK : FP8KV_ERR_LAUNCH; }
+
+}  // namespace
+
+int launch_rms_norm_rows(const uint16_t* x, uint16_t* out, const uint16_t* weight,
+                         int64_t num_rows, float eps, hipStream_t stream) {
+  const int64_t per_block = static_cast<int64_t>(kWaves) * kRowsPerWave;
+  const int64_t blocks = (num_rows + per_block - 1) / per_block;
+  if (blocks > 0x7FFFFFFF) return FP8KV_ERR_SHAPE;
+  void* args[] = {&x, &out, &weight, &num_rows, &eps};
+  return to_status(hipLaunchKernel(
+      reinterpret_cast<const void*>(&rms_norm_rows_kernel<kRowsPerWave>),
+      dim3(static_cast<uint32_t>(blocks)), dim3(kWaves * 64), args, 0, stream));
+}
+
+int launch_rope_rows(uint16_t* x, const float* cos_sin, const int64_t* positions,
+                     int64_t num_tokens, int32_t rows_per_token,
+                     int64_t max_position, hipStream_t stream) {
+  int64_t num_rows = num_tokens * rows_per_token;
+  const int64_t per_block = static_cast<int64_t>(kWaves) * 8;
+  const int64_t blocks = (num_rows + per_block - 1) / per_block;
+  if (blocks > 0x7FFFFFFF) return FP8KV_ERR_SHAPE;
+  void* args[] = {&x, &cos_sin, &positions, &num_rows, &rows_per_token,
+                  &max_position};
+  return to_status(hipLaunchKernel(reinterpret_cast<const void*>(&rope_rows_kernel),
+                                   dim3(static_cast<uint32_t>(blocks)),
+                                   dim3(kWaves * 64), args, 0, stream));
+}
+
+int launch_kv_quant_insert(const uint16_t* kv, const int64_t* slot_mapping,
+                           uint8_t* kv_cache, uint8_t* kv_scale, int32_t num_tokens,
+                           int64_t num_cache_slots, hipStream_t stream) {
+  const int64_t blocks = (static_cast<int64_t>(num_tokens) + kWaves - 1) / kWaves;
+  void* args[] = {&kv, &slot_mapping, &kv_cache, &kv_scale, &num_tokens,
+                  &num_cache_slots};
+  return to_status(hipLaunchKernel(
+      reinterpret_cast<const void*>(&kv_quant_insert_kernel),
+      dim3(static_cast<uint32_t>(blocks)), dim3(kWaves * 64), args, 0, stream));
+}
+
+}  // namespace fp8kv

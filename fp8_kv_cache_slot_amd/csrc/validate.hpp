@@ -99,4 +99,48 @@ inline int validate_gather_dequant(const uint8_t* kv_cache,
   return FP8KV_OK;
 }
 
+inline int validate_rms_norm_rows(const void* x, const void* out,
+                                  const void* weight, int64_t num_rows,
+                                  int32_t row_dim) {
+  if (num_rows < 0 || num_rows > (int64_t{1} << 40)) return FP8KV_ERR_SHAPE;
+  if (row_dim != kHeadDim) return FP8KV_ERR_UNSUPPORTED;
+  if (num_rows == 0) return FP8KV_OK;
+  if (!x || !out || !weight) return FP8KV_ERR_NULL;
+  if (!aligned(x, 16) || !aligned(out, 16) || !aligned(weight, 16))
+    return FP8KV_ERR_ALIGN;
+  return FP8KV_OK;
+}
+
+inline int validate_rope_rows(const void* x, const float* cos_sin_cache,
+                              const int64_t* positions, int64_t num_tokens,
+                              int32_t rows_per_token, int32_t row_dim,
+                              int32_t rope_dim, int64_t max_position) {
+  if (num_tokens < 0 || rows_per_token < 1 || max_position < 1 ||
+      num_tokens > (int64_t{1} << 40) / rows_per_token)
+    return FP8KV_ERR_SHAPE;
+  if (row_dim != kHeadDim || rope_dim != kRopeDim) return FP8KV_ERR_UNSUPPORTED;
+  if (num_tokens == 0) return FP8KV_OK;
+  if (!x || !cos_sin_cache || !positions) return FP8KV_ERR_NULL;
+  if (!aligned(x, 16) || !aligned(cos_sin_cache, 16) || !aligned(positions, 8))
+    return FP8KV_ERR_ALIGN;
+  return FP8KV_OK;
+}
+
+inline int validate_kv_quant_insert(const void* kv, const int64_t* slot_mapping,
+                                    const uint8_t* kv_cache,
+                                    const uint8_t* kv_scale, int64_t num_tokens,
+                                    int64_t num_pages, int32_t page_size) {
+  if (num_tokens < 0 || num_tokens > 0x7FFFFFFF || num_pages < 0 ||
+      num_pages > (int64_t{1} << 40))
+    return FP8KV_ERR_SHAPE;
+  if (page_size != kPageSize) return FP8KV_ERR_UNSUPPORTED;
+  if (num_tokens == 0) return FP8KV_OK;
+  if (!kv || !slot_mapping) return FP8KV_ERR_NULL;
+  if (num_pages > 0 && (!kv_cache || !kv_scale)) return FP8KV_ERR_NULL;
+  if (!aligned(kv, 16) || !aligned(slot_mapping, 8) ||
+      (kv_cache && !aligned(kv_cache, 16)))
+    return FP8KV_ERR_ALIGN;
+  return FP8KV_OK;
+}
+
 }  // namespace fp8kv

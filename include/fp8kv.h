@@ -174,6 +174,38 @@ int kv_cache_gather_dequant(const uint8_t* kv_cache, const uint8_t* kv_scale,
                             const int64_t* slots, int64_t num_rows, void* out,
                             void* stream);
 
+/*
+ * The prologue taken apart into separate launches: the unfused baseline the
+ * fused call is measured against (FlagGems PR #5449 "Performance": one fused
+ * launch against the baseline's two; InfiniOps PR #1019 "Benchmark /
+ * Performance Impact": separate RmsNorm and RotaryEmbedding calls).  Every
+ * stage reads and writes bf16, so the composition rounds to bf16 between
+ * stages where qnorm_rope_kv_quant_insert does not.
+ *
+ * rms_norm_rows: out[r, :] = bf16(x[r, :] / sqrt(mean(x[r, :]^2) + eps) * w)
+ *   for num_rows rows of row_dim = 512 bf16 (x, out, weight 16-B aligned).
+ *   out may equal x (in place); otherwise they must not overlap.
+ * rope_rows: in place on x bf16 [num_tokens, rows_per_token, 512]: the pairs
+ *   (448 + 2i, 449 + 2i), i < rope_dim / 2 = 32, of every row of token t
+ *   rotate by cos_sin_cache[positions[t]] (layout as for the fused call) and
+ *   are rounded to bf16; dims 0..447 are not touched.  A token whose position
+ *   is outside [0, max_position) is left as it was.
+ * kv_quant_insert: kv bf16 [num_tokens, 512] holds KV rows that are already
+ *   normalised and rotated; each row whose slot_mapping entry is valid is
+ *   quantised and written to kv_cache / kv_scale exactly as the fused call
+ *   writes them (the exponent of a block is taken from the bf16 values).
+ * Errors as for the fused call; row_dim != 512, rope_dim != 64 or
+ * page_size != 64 -> FP8KV_ERR_UNSUPPORTED.  Zero rows/tokens return FP8KV_OK.
+ */
+int rms_norm_rows(const void* x, void* out, const void* weight,
+                  int64_t num_rows, int32_t row_dim, float eps, void* stream);
+int rope_rows(void* x, const float* cos_sin_cache, const int64_t* positions,
+              int64_t num_tokens, int32_t rows_per_token, int32_t row_dim,
+              int32_t rope_dim, int64_t max_position, void* stream);
+int kv_quant_insert(const void* kv, const int64_t* slot_mapping,
+                    uint8_t* kv_cache, uint8_t* kv_scale, int64_t num_tokens,
+                    int64_t num_pages, int32_t page_size, void* stream);
+
 /* Static text for a status code (never NULL). */
 const char* fp8kv_status_string(int status);
 

@@ -49,6 +49,12 @@ def _load():
     lib.oracle_qnorm_rope_kv_quant_insert.restype = None
     lib.oracle_kv_normalised.argtypes = [P, P, P, P, I64, D, P]
     lib.oracle_kv_normalised.restype = None
+    lib.oracle_rms_norm_rows.argtypes = [P, P, P, I64, D]
+    lib.oracle_rms_norm_rows.restype = None
+    lib.oracle_rope_rows.argtypes = [P, P, P, I64, I32]
+    lib.oracle_rope_rows.restype = None
+    lib.oracle_kv_quant_insert.argtypes = [P, P, P, P, I64, I64]
+    lib.oracle_kv_quant_insert.restype = None
     lib.oracle_kv_cache_gather_dequant.argtypes = [P, P, P, I64, I64, P]
     lib.oracle_kv_cache_gather_dequant.restype = None
     lib.oracle_qk_norm_rope_packed.argtypes = [
@@ -130,6 +136,42 @@ def kv_normalised(kv, kv_weight, cos_sin_cache, positions, eps):
         _ptr(cos_sin_cache, np.float32), _ptr(positions, np.int64), T,
         float(eps), _ptr(y, np.float64, True))
     return y
+
+
+def rms_norm_rows(x, weight, eps):
+    """bf16 [..., 512] -> new array of normalised, weighted bf16 rows."""
+    if x.shape[-1] != 512 or weight.shape != (512,):
+        raise ValueError("rows must be 512 wide")
+    x = np.ascontiguousarray(x, np.uint16)
+    out = np.empty_like(x)
+    _load().oracle_rms_norm_rows(_ptr(x, np.uint16), _ptr(weight, np.uint16),
+                                 _ptr(out, np.uint16, True), x.size // 512, float(eps))
+    return out
+
+
+def rope_rows(x, cos_sin_cache, positions):
+    """In place on bf16 x [T, rows_per_token, 512] (rotary dims 448..511)."""
+    T, R, D = x.shape
+    if D != 512 or positions.shape != (T,) or cos_sin_cache.shape[1] != 64:
+        raise ValueError("x must be [T, R, 512], cache [max_pos, 64]")
+    if T and (positions.min() < 0 or positions.max() >= cos_sin_cache.shape[0]):
+        raise ValueError("position out of range")
+    _load().oracle_rope_rows(_ptr(x, np.uint16, True), _ptr(cos_sin_cache, np.float32),
+                             _ptr(positions, np.int64), T, R)
+
+
+def kv_quant_insert(kv, slot_mapping, kv_cache, kv_scale):
+    """Quantise already normalised + rotated bf16 rows kv [T, 512] into the
+    cache (in place on kv_cache / kv_scale)."""
+    T = kv.shape[0]
+    pages = kv_cache.shape[0]
+    if kv.shape != (T, 512) or slot_mapping.shape != (T,):
+        raise ValueError("kv must be [T, 512], slot_mapping [T]")
+    if kv_cache.shape != (pages, 64, 576) or kv_scale.shape != (pages, 64, 8):
+        raise ValueError("cache must be [pages,64,576], scale [pages,64,8]")
+    _load().oracle_kv_quant_insert(_ptr(kv, np.uint16), _ptr(slot_mapping, np.int64),
+                                   _ptr(kv_cache, np.uint8, True),
+                                   _ptr(kv_scale, np.uint8, True), T, pages)
 
 
 def kv_cache_gather_dequant(kv_cache, kv_scale, slots):

@@ -81,6 +81,29 @@ void kv_head(const uint16_t* x, const uint16_t* w, const float* cosv,
                 sinv[i]);
 }
 
+// Quantise one normalised, rotated KV head y and write its cache row and
+// exponent bytes.  Seven UE8M0 power-of-two block scales per token ([P1]
+// "Performance": the scalar-scale convention "cannot carry seven per-block
+// exponents per token"), each the smallest power of two that brings the
+// block's largest magnitude within the E4M3 range; the rotary dims are kept
+// as bf16 after the codes (reading).
+void quantise_insert(const double* y, uint8_t* dst, uint8_t* scale) {
+  for (int b = 0; b < kNumBlocks; ++b) {
+    double amax = 0.0;
+    for (int d = b * kQuantBlock; d < (b + 1) * kQuantBlock; ++d)
+      amax = std::fmax(amax, std::fabs(y[d]));
+    int32_t e = oracle_ue8m0_exponent(amax);
+    scale[b] = static_cast<uint8_t>(e + 127);
+    for (int d = b * kQuantBlock; d < (b + 1) * kQuantBlock; ++d)
+      dst[d] = oracle_e4m3_encode(std::ldexp(y[d], -e));  // exact scaling
+  }
+  for (int j = 0; j < kRopeDim; ++j) {
+    uint16_t bits = oracle_bf16_rne(y[kRopeStart + j]);
+    dst[kRopeStart + 2 * j] = static_cast<uint8_t>(bits & 0xFF);
+    dst[kRopeStart + 2 * j + 1] = static_cast<uint8_t>(bits >> 8);
+  }
+}
+
 }  // namespace
 
 extern "C" {
@@ -206,27 +229,7 @@ void oracle_qnorm_rope_kv_quant_insert(
     if (slot < 0 || slot >= num_slots) continue;  // skipped token
     kv_head(kv + t * kHeadDim, kv_weight, cosv, sinv, eps, y);
 
-    uint8_t* dst = kv_cache + slot * kRowBytes;
-    uint8_t* scale = kv_scale + slot * kScaleBytes;
-    // Seven UE8M0 power-of-two block scales per token ([P1] "Performance":
-    // the lightop scalar scale "cannot carry seven per-block exponents per
-    // token"), each the smallest power of two that brings the block's
-    // largest magnitude within the E4M3 range.
-    for (int b = 0; b < kNumBlocks; ++b) {
-      double amax = 0.0;
-      for (int d = b * kQuantBlock; d < (b + 1) * kQuantBlock; ++d)
-        amax = std::fmax(amax, std::fabs(y[d]));
-      int32_t e = oracle_ue8m0_exponent(amax);
-      scale[b] = static_cast<uint8_t>(e + 127);
-      for (int d = b * kQuantBlock; d < (b + 1) * kQuantBlock; ++d)
-        dst[d] = oracle_e4m3_encode(std::ldexp(y[d], -e));  // exact scaling
-    }
-    // The rotary dims are kept as bf16 after the codes (reading).
-    for (int j = 0; j < kRopeDim; ++j) {
-      uint16_t bits = oracle_bf16_rne(y[kRopeStart + j]);
-      dst[kRopeStart + 2 * j] = static_cast<uint8_t>(bits & 0xFF);
-      dst[kRopeStart + 2 * j + 1] = static_cast<uint8_t>(bits >> 8);
-    }
+    quantise_insert(y, kv_cache + slot * kRowBytes, kv_scale + slot * kScaleBytes);
   }
 }
 
@@ -237,6 +240,46 @@ void oracle_kv_normalised(const uint16_t* kv, const uint16_t* kv_weight,
     const float* row = cos_sin_cache + positions[t] * kRopeDim;
     kv_head(kv + t * kHeadDim, kv_weight, row, row + kRopeDim / 2, eps,
             y_out + t * kHeadDim);
+  }
+}
+
+void oracle_rms_norm_rows(const uint16_t* x, const uint16_t* weight,
+                          uint16_t* out, int64_t num_rows, double eps) {
+  double y[kHeadDim];
+  for (int64_t r = 0; r < num_rows; ++r) {
+    rms_norm(x + r * kHeadDim, weight, kHeadDim, eps, y);
+    for (int d = 0; d < kHeadDim; ++d) out[r * kHeadDim + d] = oracle_bf16_rne(y[d]);
+  }
+}
+
+void oracle_rope_rows(uint16_t* x, const float* cos_sin_cache,
+                      const int64_t* positions, int64_t num_tokens,
+                      int32_t rows_per_token) {
+  for (int64_t t = 0; t < num_tokens; ++t) {
+    const float* row = cos_sin_cache + positions[t] * kRopeDim;
+    for (int32_t h = 0; h < rows_per_token; ++h) {
+      uint16_t* xr = x + (t * rows_per_token + h) * kHeadDim;
+      for (int i = 0; i < kRopeDim / 2; ++i) {
+        double a = oracle_bf16_to_double(xr[kRopeStart + 2 * i]);
+        double b = oracle_bf16_to_double(xr[kRopeStart + 2 * i + 1]);
+        rotate_pair(&a, &b, row[i], row[kRopeDim / 2 + i]);
+        xr[kRopeStart + 2 * i] = oracle_bf16_rne(a);
+        xr[kRopeStart + 2 * i + 1] = oracle_bf16_rne(b);
+      }
+    }
+  }
+}
+
+void oracle_kv_quant_insert(const uint16_t* kv, const int64_t* slot_mapping,
+                            uint8_t* kv_cache, uint8_t* kv_scale,
+                            int64_t num_tokens, int64_t num_pages) {
+  const int64_t num_slots = num_pages * kPageSize;
+  double y[kHeadDim];
+  for (int64_t t = 0; t < num_tokens; ++t) {
+    const int64_t slot = slot_mapping[t];
+    if (slot < 0 || slot >= num_slots) continue;
+    for (int d = 0; d < kHeadDim; ++d) y[d] = oracle_bf16_to_double(kv[t * kHeadDim + d]);
+    quantise_insert(y, kv_cache + slot * kRowBytes, kv_scale + slot * kScaleBytes);
   }
 }
 

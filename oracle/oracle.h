@@ -90,6 +90,33 @@ void oracle_kv_normalised(const uint16_t* kv, const uint16_t* kv_weight,
                           const float* cos_sin_cache, const int64_t* positions,
                           int64_t num_tokens, double eps, double* y_out);
 
+/* ---- the prologue as separate stages (an unfused pipeline) ---------------- */
+/*
+ * The same operator taken apart into the launches an unfused implementation
+ * would make ([P1] "Performance": the baseline's two launches against one
+ * fused launch; [P3] "Benchmark / Performance Impact": separate RmsNorm and
+ * RotaryEmbedding calls).  Each stage reads and writes bf16, so the pipeline
+ * rounds to bf16 between stages where the fused operator does not.
+ *
+ * oracle_rms_norm_rows: out[r, :] = bf16(x[r, :] / sqrt(mean(x^2) + eps) * w)
+ *   for rows of 512; out may equal x.
+ * oracle_rope_rows: in place on x [T, rows_per_token, 512]; the pairs
+ *   (448 + 2i, 449 + 2i) of every row of token t rotate by cos_sin_cache row
+ *   positions[t], result rounded to bf16; the other dims are not touched.
+ * oracle_kv_quant_insert: kv [T, 512] holds bf16 values that are already
+ *   normalised and rotated; quantise and insert them exactly as entry 1 does
+ *   with its unrounded values (seven UE8M0 blocks over dims 0..447, dims
+ *   448..511 copied as bf16).
+ */
+void oracle_rms_norm_rows(const uint16_t* x, const uint16_t* weight,
+                          uint16_t* out, int64_t num_rows, double eps);
+void oracle_rope_rows(uint16_t* x, const float* cos_sin_cache,
+                      const int64_t* positions, int64_t num_tokens,
+                      int32_t rows_per_token);
+void oracle_kv_quant_insert(const uint16_t* kv, const int64_t* slot_mapping,
+                            uint8_t* kv_cache, uint8_t* kv_scale,
+                            int64_t num_tokens, int64_t num_pages);
+
 /* ---- read side of the cache ------------------------------------------------ */
 /*
  * Gather rows of the paged FP8/UE8M0 cache by slot and dequantise them:

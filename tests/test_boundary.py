@@ -116,6 +116,42 @@ def test_dequant_argument_errors(over, want):
     assert _dequant(**over) == want
 
 
+def _norm(**over):
+    a = dict(x=FAKE, out=FAKE, w=FAKE, rows=10, dim=512, eps=1e-6, stream=None)
+    a.update(over)
+    return K.lib().rms_norm_rows(*a.values())
+
+
+def _rope(**over):
+    a = dict(x=FAKE, cs=FAKE, pos=FAKE, T=3, R=4, dim=512, rope=64, maxp=8,
+             stream=None)
+    a.update(over)
+    return K.lib().rope_rows(*a.values())
+
+
+def _quant(**over):
+    a = dict(kv=FAKE, sm=FAKE, cache=FAKE, scale=FAKE, T=3, pages=1, page=64,
+             stream=None)
+    a.update(over)
+    return K.lib().kv_quant_insert(*a.values())
+
+
+@pytest.mark.parametrize("fn,over,want", [
+    (_norm, dict(rows=-1), 2), (_norm, dict(dim=256), 3), (_norm, dict(x=None), 1),
+    (_norm, dict(out=None), 1), (_norm, dict(w=None), 1), (_norm, dict(out=FAKE + 8), 4),
+    (_norm, dict(rows=0, x=None), 0),
+    (_rope, dict(T=-1), 2), (_rope, dict(R=0), 2), (_rope, dict(maxp=0), 2),
+    (_rope, dict(dim=128), 3), (_rope, dict(rope=32), 3), (_rope, dict(x=None), 1),
+    (_rope, dict(cs=None), 1), (_rope, dict(pos=None), 1), (_rope, dict(x=FAKE + 2), 4),
+    (_rope, dict(T=0, x=None), 0),
+    (_quant, dict(T=-1), 2), (_quant, dict(pages=-1), 2), (_quant, dict(page=32), 3),
+    (_quant, dict(kv=None), 1), (_quant, dict(sm=None), 1), (_quant, dict(cache=None), 1),
+    (_quant, dict(kv=FAKE + 8), 4), (_quant, dict(T=0, kv=None), 0),
+])
+def test_stage_argument_errors(fn, over, want):
+    assert fn(**over) == want
+
+
 @pytest.mark.skipif(torch.cuda.device_count() > 0, reason="a GPU is present")
 def test_no_device_is_reported_not_launched():
     # valid-looking arguments reach the device check, which fails without a
@@ -124,6 +160,7 @@ def test_no_device_is_reported_not_launched():
     assert _packed() == 5
     assert _dequant() == 5
     assert _dequant(pages=0, cache=None, scale=None) == 5
+    assert _norm() == 5 and _rope() == 5 and _quant() == 5
 
 
 def test_knobs():
