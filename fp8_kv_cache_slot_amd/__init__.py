@@ -33,6 +33,7 @@ STATUS = {0: "FP8KV_OK", 1: "FP8KV_ERR_NULL", 2: "FP8KV_ERR_SHAPE",
 
 EXPORTED = ["qnorm_rope_kv_quant_insert", "qk_norm_rope_packed",
             "kv_cache_gather_dequant", "rms_norm_rows", "rope_rows",
+            "qk_norm_rope_packed_ex",
             "kv_quant_insert",
             "fp8kv_status_string", "fp8kv_abi_version",
             "fp8kv_set_dispatch_threshold", "fp8kv_get_dispatch_threshold",
@@ -66,6 +67,9 @@ def lib() -> ctypes.CDLL:
     L.qk_norm_rope_packed.argtypes = [
         P, I64, I32, I32, I32, I32, F, P, P, P, I32, P, I32, I64, P]
     L.qk_norm_rope_packed.restype = ctypes.c_int
+    L.qk_norm_rope_packed_ex.argtypes = [
+        P, I64, I32, I32, I32, I32, F, P, P, P, I32, P, I32, I32, I64, P]
+    L.qk_norm_rope_packed_ex.restype = ctypes.c_int
     L.kv_cache_gather_dequant.argtypes = [P, P, I64, I32, P, I64, P, P]
     L.kv_cache_gather_dequant.restype = ctypes.c_int
     L.rms_norm_rows.argtypes = [P, P, P, I64, I32, F, P]
@@ -173,6 +177,39 @@ def qk_norm_rope_packed(qkv, num_heads_q: int, num_heads_k: int,
         _stream(stream))
     if st:
         raise Fp8kvError(st, "qk_norm_rope_packed")
+
+
+def qk_norm_rope_packed_ex(qkv, num_heads_q: int, num_heads_k: int,
+                           num_heads_v: int, head_dim: int, eps: float,
+                           q_weight, k_weight, cos_sin_cache, is_neox: bool,
+                           position_ids, rotary_dim: int | None = None,
+                           stream=None) -> None:
+    """Packed Q/K RMSNorm + RoPE for head_dim 64/128/256, partial rotary
+    (``rotary_dim``, default the whole head), NeoX or interleaved pairs, bf16
+    or fp16 (the dtype of ``qkv``), in place; V heads untouched."""
+    if qkv.dim() != 2:
+        raise ValueError("qkv must be [T, (Hq+Hk+Hv)*D]")
+    dtypes = {torch.bfloat16: 0, torch.float16: 1}
+    if qkv.dtype not in dtypes:
+        raise TypeError("qkv must be bfloat16 or float16")
+    T = qkv.shape[0]
+    R = head_dim if rotary_dim is None else int(rotary_dim)
+    _check(qkv, "qkv", qkv.dtype,
+           (T, (num_heads_q + num_heads_k + num_heads_v) * head_dim))
+    _check(q_weight, "q_weight", qkv.dtype, (head_dim,))
+    _check(k_weight, "k_weight", qkv.dtype, (head_dim,))
+    _check(cos_sin_cache, "cos_sin_cache", torch.float32)
+    if cos_sin_cache.dim() != 2 or cos_sin_cache.shape[1] != R:
+        raise ValueError("cos_sin_cache must be [max_position, rotary_dim]")
+    _check(position_ids, "position_ids", torch.int64, (T,))
+    st = lib().qk_norm_rope_packed_ex(
+        qkv.data_ptr(), T, num_heads_q, num_heads_k, num_heads_v, head_dim,
+        float(eps), q_weight.data_ptr(), k_weight.data_ptr(),
+        cos_sin_cache.data_ptr() if R else None, int(bool(is_neox)),
+        position_ids.data_ptr(), R, dtypes[qkv.dtype],
+        max(1, cos_sin_cache.shape[0]), _stream(stream))
+    if st:
+        raise Fp8kvError(st, "qk_norm_rope_packed_ex")
 
 
 def kv_cache_gather_dequant(kv_cache, kv_scale, slots, out=None,

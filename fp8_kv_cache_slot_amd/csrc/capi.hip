@@ -121,6 +121,56 @@ FP8KV_API int qk_norm_rope_packed(
   return launch_packed(a, static_cast<hipStream_t>(stream));
 }
 
+FP8KV_API int qk_norm_rope_packed_ex(
+    void* qkv, int64_t num_tokens, int32_t num_heads_q, int32_t num_heads_k,
+    int32_t num_heads_v, int32_t head_dim, float eps, const void* q_weight,
+    const void* k_weight, const float* cos_sin_cache, int32_t is_neox,
+    const int64_t* position_ids, int32_t rotary_dim, int32_t dtype,
+    int64_t max_position, void* stream) {
+  using namespace fp8kv;
+  int st = validate_packed_ex(qkv, num_tokens, num_heads_q, num_heads_k,
+                              num_heads_v, head_dim, q_weight, k_weight,
+                              cos_sin_cache, is_neox, position_ids, rotary_dim,
+                              dtype, max_position);
+  if (st != FP8KV_OK || num_tokens == 0) return st;
+  st = check_device();
+  if (st != FP8KV_OK) return st;
+  // The guarded case (bf16, 128 wide, full NeoX) has its own tuned kernel.
+  if (dtype == FP8KV_DTYPE_BF16 && head_dim == kPackedHeadDim &&
+      rotary_dim == kPackedHeadDim && is_neox == 1) {
+    PackedArgs a;
+    a.qkv = static_cast<uint16_t*>(qkv);
+    a.q_weight = static_cast<const uint16_t*>(q_weight);
+    a.k_weight = static_cast<const uint16_t*>(k_weight);
+    a.cos_sin = cos_sin_cache;
+    a.position_ids = position_ids;
+    a.num_tokens = static_cast<int32_t>(num_tokens);
+    a.num_heads_q = num_heads_q;
+    a.num_heads_k = num_heads_k;
+    a.row_elems = (num_heads_q + num_heads_k + num_heads_v) * kPackedHeadDim;
+    a.max_position = max_position;
+    a.eps = eps;
+    return launch_packed(a, static_cast<hipStream_t>(stream));
+  }
+  PackedExArgs a;
+  a.qkv = static_cast<uint16_t*>(qkv);
+  a.q_weight = static_cast<const uint16_t*>(q_weight);
+  a.k_weight = static_cast<const uint16_t*>(k_weight);
+  a.cos_sin = cos_sin_cache;
+  a.position_ids = position_ids;
+  a.num_tokens = static_cast<int32_t>(num_tokens);
+  a.num_heads_q = num_heads_q;
+  a.num_heads_k = num_heads_k;
+  a.row_elems = (num_heads_q + num_heads_k + num_heads_v) * head_dim;
+  a.head_dim = head_dim;
+  a.rotary_dim = rotary_dim;
+  a.is_neox = is_neox;
+  a.is_fp16 = dtype == FP8KV_DTYPE_FP16;
+  a.max_position = max_position;
+  a.eps = eps;
+  return launch_packed_ex(a, static_cast<hipStream_t>(stream));
+}
+
 FP8KV_API int kv_cache_gather_dequant(const uint8_t* kv_cache,
                                      const uint8_t* kv_scale, int64_t num_pages,
                                      int32_t page_size, const int64_t* slots,

@@ -40,6 +40,24 @@ struct PackedArgs {
   float eps;
 };
 
+struct PackedExArgs {
+  uint16_t* qkv;
+  const uint16_t* q_weight;
+  const uint16_t* k_weight;
+  const float* cos_sin;
+  const int64_t* position_ids;
+  int32_t num_tokens;
+  int32_t num_heads_q;
+  int32_t num_heads_k;
+  int32_t row_elems;  // (Hq + Hk + Hv) * head_dim
+  int32_t head_dim;   // 64, 128 or 256
+  int32_t rotary_dim; // multiple of 16, <= head_dim
+  int32_t is_neox;
+  int32_t is_fp16;
+  int64_t max_position;
+  float eps;
+};
+
 struct DequantArgs {
   const uint8_t* kv_cache;
   const uint8_t* kv_scale;
@@ -56,6 +74,7 @@ bool prologue_shape_built(int waves, int qs);
 
 int launch_packed(const PackedArgs& a, hipStream_t stream);
 int launch_gather_dequant(const DequantArgs& a, hipStream_t stream);
+int launch_packed_ex(const PackedExArgs& a, hipStream_t stream);
 
 // The prologue's stages as separate launches (the unfused baseline).
 int launch_rms_norm_rows(const uint16_t* x, uint16_t* out, const uint16_t* weight,

@@ -1,0 +1,222 @@
+// Packed-QKV Q/K RMSNorm + RoPE beyond the guarded fast path (InfiniOps PR
+// #1019 "FusedQkNormRope", "Summary" and "Notes for Reviewers": the first
+// implementation accepts only bf16, head_dim 128 and full-dimension NeoX
+// rotation).  This kernel covers
+//   head_dim D in {64, 128, 256}    (8, 16 or 32 lanes per head)
+//   rotary_dim R, a multiple of 16, 0 <= R <= D (partial rotary: dims [R, D)
+//                are normalised and weighted only)
+//   NeoX pairs (i, i + R/2) or interleaved pairs (2i, 2i + 1)
+//   bf16 or fp16 qkv and weights
+// V heads are never read or written.
+//
+// Layout of the work.  One wave per token; a head is D/8 lanes of one 16-byte
+// vector each, so a wave covers 512/D heads per access and loops over the
+// token's Q and K heads with four accesses' loads issued ahead.  The sum of
+// squares is reduced over the head's lanes (DPP row steps, plus one lane
+// shuffle across rows for D = 256).  Interleaved pairs sit inside a lane;
+// a NeoX partner sits R/16 lanes away within the head and arrives through
+// one ds_bpermute per value.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "prologue_launch.hpp"
+#include "wave_ops.hpp"
+
+namespace fp8kv {
+namespace {
+
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+
+template <bool FP16>
+__device__ __forceinline__ void unpack8_any(u32x4_t x, float* f) {
+  if constexpr (FP16) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      // copy the element out first: hipcc (ROCm 7.2) evaluates a
+      // __builtin_bit_cast of an ext_vector element as element 0
+      const uint32_t word = x[i];
+      const float2_t v =
+          __builtin_convertvector(__builtin_bit_cast(f16x2_t, word), float2_t);
+      f[2 * i] = v[0];
+      f[2 * i + 1] = v[1];
+    }
+  } else {
+    unpack8(x, f);
+  }
+}
+
+template <bool FP16>
+__device__ __forceinline__ uint32_t pack2_any(float a, float b) {
+  if constexpr (FP16) {
+    float2_t f = {a, b};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, f16x2_t));
+  } else {
+    return pack_bf16(a, b);
+  }
+}
+
+// Sum over each group of LPH consecutive lanes (LPH = 8, 16 or 32).
+template <int LPH>
+__device__ __forceinline__ float head_sum(float v) {
+  v += dpp<kDppQuadXor1>(v);
+  v += dpp<kDppQuadXor2>(v);
+  v += dpp<kDppRowHalfMirror>(v);
+  if constexpr (LPH >= 16) v += dpp<kDppRowMirror>(v);
+  if constexpr (LPH >= 32) v += __shfl_xor(v, 16, 64);
+  return v;
+}
+
+template <int D, bool FP16, bool NEOX>
+__global__ void __launch_bounds__(256) qk_norm_rope_packed_ex_kernel(
+    uint16_t* __restrict__ qkv, const uint16_t* __restrict__ q_weight,
+    const uint16_t* __restrict__ k_weight, const float* __restrict__ cos_sin,
+    const int64_t* __restrict__ position_ids, int32_t num_tokens,
+    int32_t num_heads_q, int32_t num_heads_k, int32_t row_elems,
+    int32_t rotary_dim, int64_t max_position, float eps) {
+  constexpr int LPH = D / 8;   // lanes per head
+  constexpr int HPW = 64 / LPH;  // heads per wave access
+  constexpr int U = 4;         // accesses per batch of loads
+  const int lane = lane_id();
+  const int32_t t = static_cast<int32_t>(blockIdx.x) * 4 + wave_id();
+  if (t >= num_tokens) return;
+  const int64_t pos = position_ids[t];
+  if (pos < 0 || pos >= max_position) return;
+  const int g = lane / LPH;    // head slot within an access
+  const int lh = lane % LPH;   // lane within the head: dims 8lh .. 8lh+7
+  const int32_t nh = num_heads_q + num_heads_k;
+
+  float wq[8], wk[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) wq[j] = wk[j] = 0.0f;
+  if (num_heads_q > 0) unpack8_any<FP16>(load16<false>(q_weight + lh * 8), wq);
+  if (num_heads_k > 0) unpack8_any<FP16>(load16<false>(k_weight + lh * 8), wk);
+
+  // Rotation coefficients of this lane: identity outside the rotary dims.
+  const int rot_lanes = rotary_dim / 8;
+  const bool rotary = lh < rot_lanes;
+  float c[8], s[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    c[j] = 1.0f;
+    s[j] = 0.0f;
+  }
+  int partner = lane;
+  if (rotary) {
+    const float* row = cos_sin + pos * rotary_dim;
+    const int half = rotary_dim / 2;
+    if constexpr (NEOX) {
+      // dims 8lh.. pair with dims 8lh +- R/2, R/16 lanes away; the first half
+      // takes n c - n' s, the second half n c + n' s
+      const bool first = lh < rot_lanes / 2;
+      const int i0 = first ? 8 * lh : 8 * lh - half;
+      const f32x4_t c0 = load16f(row + i0), c1 = load16f(row + i0 + 4);
+      const f32x4_t s0 = load16f(row + half + i0), s1 = load16f(row + half + i0 + 4);
+      const float sg = first ? -1.0f : 1.0f;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        c[j] = c0[j];
+        c[4 + j] = c1[j];
+        s[j] = sg * s0[j];
+        s[4 + j] = sg * s1[j];
+      }
+      partner = first ? lane + rot_lanes / 2 : lane - rot_lanes / 2;
+    } else {
+      // pairs 4lh .. 4lh+3 inside the lane
+      const f32x4_t cc = load16f(row + 4 * lh), ss = load16f(row + half + 4 * lh);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        c[2 * k] = c[2 * k + 1] = cc[k];
+        s[2 * k] = -ss[k];      // a' = a c - b s
+        s[2 * k + 1] = ss[k];   // b' = b c + a s
+      }
+    }
+  }
+  const int partner_addr = partner * 4;  // ds_bpermute byte address
+
+  uint16_t* base = qkv + static_cast<int64_t>(t) * row_elems + lh * 8;
+  for (int32_t h0 = 0; h0 < nh; h0 += U * HPW) {
+    u32x4_t x[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int32_t h = h0 + u * HPW + g;
+      x[u] = load16<true>(base + static_cast<int64_t>(h < nh ? h : 0) * D);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int32_t h = h0 + u * HPW + g;
+      if (h0 + u * HPW >= nh) break;  // no head of this access exists
+      float f[8], n[8], o[8];
+      unpack8_any<FP16>(x[u], f);
+      const float ss = head_sum<LPH>(sum_sq8(f));
+      const float r = __builtin_amdgcn_rsqf(fmaf(ss, 1.0f / D, eps));
+      const bool is_q = h < num_heads_q;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) n[j] = f[j] * r * (is_q ? wq[j] : wk[j]);
+      if constexpr (NEOX) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const float p = __builtin_bit_cast(
+              float, __builtin_amdgcn_ds_bpermute(partner_addr,
+                                                  __builtin_bit_cast(int, n[j])));
+          o[j] = n[j] * c[j] + p * s[j];
+        }
+      } else {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          o[2 * k] = n[2 * k] * c[2 * k] + n[2 * k + 1] * s[2 * k];
+          o[2 * k + 1] = n[2 * k + 1] * c[2 * k + 1] + n[2 * k] * s[2 * k + 1];
+        }
+      }
+      if (h < nh) {
+        u32x4_t v = {pack2_any<FP16>(o[0], o[1]), pack2_any<FP16>(o[2], o[3]),
+                     pack2_any<FP16>(o[4], o[5]), pack2_any<FP16>(o[6], o[7])};
+        store16<true>(base + static_cast<int64_t>(h) * D, v);
+      }
+    }
+  }
+}
+
+template <int D, bool FP16, bool NEOX>
+int launch_ex(const PackedExArgs& a, hipStream_t stream) {
+  const int64_t blocks = (static_cast<int64_t>(a.num_tokens) + 3) / 4;
+  if (blocks > 0x7FFFFFFF) return FP8KV_ERR_SHAPE;
+  void* args[] = {const_cast<uint16_t**>(&a.qkv),
+                  const_cast<const uint16_t**>(&a.q_weight),
+                  const_cast<const uint16_t**>(&a.k_weight),
+                  const_cast<const float**>(&a.cos_sin),
+                  const_cast<const int64_t**>(&a.position_ids),
+                  const_cast<int32_t*>(&a.num_tokens),
+                  const_cast<int32_t*>(&a.num_heads_q),
+                  const_cast<int32_t*>(&a.num_heads_k),
+                  const_cast<int32_t*>(&a.row_elems),
+                  const_cast<int32_t*>(&a.rotary_dim),
+                  const_cast<int64_t*>(&a.max_position),
+                  const_cast<float*>(&a.eps)};
+  hipError_t err = hipLaunchKernel(
+      reinterpret_cast<const void*>(&qk_norm_rope_packed_ex_kernel<D, FP16, NEOX>),
+      dim3(static_cast<uint32_t>(blocks)), dim3(256), args, 0, stream);
+  return err == hipSuccess ? FP8KV_OK : FP8KV_ERR_LAUNCH;
+}
+
+template <int D>
+int launch_d(const PackedExArgs& a, hipStream_t stream) {
+  if (a.is_fp16)
+    return a.is_neox ? launch_ex<D, true, true>(a, stream)
+                     : launch_ex<D, true, false>(a, stream);
+  return a.is_neox ? launch_ex<D, false, true>(a, stream)
+                   : launch_ex<D, false, false>(a, stream);
+}
+
+}  // namespace
+
+int launch_packed_ex(const PackedExArgs& a, hipStream_t stream) {
+  switch (a.head_dim) {
+    case 64: return launch_d<64>(a, stream);
+    case 128: return launch_d<128>(a, stream);
+    case 256: return launch_d<256>(a, stream);
+    default: return FP8KV_ERR_UNSUPPORTED;
+  }
+}
+
+}  // namespace fp8kv

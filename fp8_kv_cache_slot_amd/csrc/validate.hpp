@@ -82,6 +82,38 @@ inline int validate_packed(const void* qkv, int64_t num_tokens,
   return FP8KV_OK;
 }
 
+inline int validate_packed_ex(const void* qkv, int64_t num_tokens,
+                              int32_t num_heads_q, int32_t num_heads_k,
+                              int32_t num_heads_v, int32_t head_dim,
+                              const void* q_weight, const void* k_weight,
+                              const float* cos_sin_cache, int32_t is_neox,
+                              const int64_t* position_ids, int32_t rotary_dim,
+                              int32_t dtype, int64_t max_position) {
+  if (num_tokens < 0 || num_heads_q < 0 || num_heads_k < 0 ||
+      num_heads_v < 0 || num_heads_q + num_heads_k < 1 || max_position < 1)
+    return FP8KV_ERR_SHAPE;
+  if ((head_dim != 64 && head_dim != 128 && head_dim != 256) ||
+      rotary_dim < 0 || rotary_dim > head_dim || rotary_dim % 16 != 0 ||
+      (is_neox != 0 && is_neox != 1) ||
+      (dtype != FP8KV_DTYPE_BF16 && dtype != FP8KV_DTYPE_FP16))
+    return FP8KV_ERR_UNSUPPORTED;
+  const int64_t heads = static_cast<int64_t>(num_heads_q) + num_heads_k;
+  if (num_tokens > 0 &&
+      (num_tokens > ((int64_t{1} << 31) - 1) / heads ||
+       (heads + num_heads_v) * head_dim > (int64_t{1} << 30)))
+    return FP8KV_ERR_SHAPE;
+  if (num_tokens == 0) return FP8KV_OK;
+  if (!qkv || !position_ids || (rotary_dim > 0 && !cos_sin_cache))
+    return FP8KV_ERR_NULL;
+  if ((num_heads_q > 0 && !q_weight) || (num_heads_k > 0 && !k_weight))
+    return FP8KV_ERR_NULL;
+  if (!aligned(qkv, 16) || !aligned(position_ids, 8) ||
+      (cos_sin_cache && !aligned(cos_sin_cache, 16)) ||
+      (q_weight && !aligned(q_weight, 16)) || (k_weight && !aligned(k_weight, 16)))
+    return FP8KV_ERR_ALIGN;
+  return FP8KV_OK;
+}
+
 inline int validate_gather_dequant(const uint8_t* kv_cache,
                                    const uint8_t* kv_scale, int64_t num_pages,
                                    int32_t page_size, const int64_t* slots,

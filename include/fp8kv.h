@@ -149,6 +149,32 @@ int qk_norm_rope_packed(
     const int64_t* position_ids, int32_t forced_token_heads_per_warp,
     int64_t max_position, void* stream);
 
+/* Element types of qk_norm_rope_packed_ex. */
+enum fp8kv_dtype { FP8KV_DTYPE_BF16 = 0, FP8KV_DTYPE_FP16 = 1 };
+
+/*
+ * Packed-QKV Q/K RMSNorm + RoPE beyond the guarded fast path that InfiniOps
+ * PR #1019 ships ("Notes for Reviewers": bf16, head_dim 128, full-dimension
+ * NeoX only).  Same arguments and semantics as qk_norm_rope_packed, plus:
+ *   head_dim     64, 128 or 256
+ *   rotary_dim   R, a multiple of 16 with 0 <= R <= head_dim: only dims
+ *                [0, R) of a head rotate; dims [R, head_dim) are normalised
+ *                and weighted only (partial rotary); R = 0 is RMSNorm alone
+ *   is_neox      1: pairs (i, i + R/2); 0: interleaved pairs (2i, 2i + 1);
+ *                i < R/2, rotated by cos_sin_cache row positions[t] =
+ *                [R/2 cosines | R/2 sines] (fp32 [max_position, R]; may be
+ *                NULL when R = 0)
+ *   dtype        FP8KV_DTYPE_BF16 or FP8KV_DTYPE_FP16: the type of qkv and of
+ *                both weights; outputs round to nearest even in that type
+ * Anything else -> FP8KV_ERR_UNSUPPORTED.  There is no scheduling knob.
+ */
+int qk_norm_rope_packed_ex(
+    void* qkv, int64_t num_tokens, int32_t num_heads_q, int32_t num_heads_k,
+    int32_t num_heads_v, int32_t head_dim, float eps, const void* q_weight,
+    const void* k_weight, const float* cos_sin_cache, int32_t is_neox,
+    const int64_t* position_ids, int32_t rotary_dim, int32_t dtype,
+    int64_t max_position, void* stream);
+
 /*
  * Read side of the paged cache written by qnorm_rope_kv_quant_insert: gather
  * rows by slot and dequantise them to bf16 (the inverse the cache layout of

@@ -38,6 +38,10 @@ def _load():
     lib.oracle_bf16_to_double.restype = D
     lib.oracle_bf16_rne.argtypes = [D]
     lib.oracle_bf16_rne.restype = ctypes.c_uint16
+    lib.oracle_fp16_to_double.argtypes = [ctypes.c_uint16]
+    lib.oracle_fp16_to_double.restype = D
+    lib.oracle_fp16_rne.argtypes = [D]
+    lib.oracle_fp16_rne.restype = ctypes.c_uint16
     lib.oracle_e4m3_decode.argtypes = [ctypes.c_uint8]
     lib.oracle_e4m3_decode.restype = D
     lib.oracle_e4m3_encode.argtypes = [D]
@@ -60,6 +64,9 @@ def _load():
     lib.oracle_qk_norm_rope_packed.argtypes = [
         P, I64, I32, I32, I32, I32, D, P, P, P, P]
     lib.oracle_qk_norm_rope_packed.restype = None
+    lib.oracle_qk_norm_rope_packed_ex.argtypes = [
+        P, I64, I32, I32, I32, I32, I32, I32, I32, D, P, P, P, P]
+    lib.oracle_qk_norm_rope_packed_ex.restype = None
     _lib = lib
     return lib
 
@@ -82,6 +89,14 @@ def bf16_to_double(bits: int) -> float:
 
 def bf16_rne(v: float) -> int:
     return _load().oracle_bf16_rne(float(v))
+
+
+def fp16_to_double(bits: int) -> float:
+    return _load().oracle_fp16_to_double(int(bits))
+
+
+def fp16_rne(v: float) -> int:
+    return _load().oracle_fp16_rne(float(v))
 
 
 def e4m3_decode(code: int) -> float:
@@ -205,3 +220,25 @@ def qk_norm_rope_packed(qkv, num_heads_q, num_heads_k, num_heads_v, head_dim,
         head_dim, float(eps), _ptr(q_weight, np.uint16),
         _ptr(k_weight, np.uint16), _ptr(cos_sin_cache, np.float32),
         _ptr(position_ids, np.int64))
+
+
+def qk_norm_rope_packed_ex(qkv, num_heads_q, num_heads_k, num_heads_v,
+                           head_dim, rotary_dim, is_neox, is_fp16, eps,
+                           q_weight, k_weight, cos_sin_cache, position_ids):
+    """In place on ``qkv`` (uint16 bit patterns of bf16 or fp16
+    [T,(Hq+Hk+Hv)*D]); V heads untouched."""
+    T = qkv.shape[0]
+    if qkv.shape[1] != (num_heads_q + num_heads_k + num_heads_v) * head_dim:
+        raise ValueError("qkv width does not match the head counts")
+    if rotary_dim % 2 or rotary_dim > head_dim or cos_sin_cache.shape[1] != rotary_dim:
+        raise ValueError("cos_sin_cache must be [max_position, rotary_dim]")
+    if position_ids.shape != (T,):
+        raise ValueError("position_ids must be [T]")
+    if T and (position_ids.min() < 0
+              or position_ids.max() >= cos_sin_cache.shape[0]):
+        raise ValueError("position out of range")
+    _load().oracle_qk_norm_rope_packed_ex(
+        _ptr(qkv, np.uint16, True), T, num_heads_q, num_heads_k, num_heads_v,
+        head_dim, rotary_dim, int(is_neox), int(is_fp16), float(eps),
+        _ptr(q_weight, np.uint16), _ptr(k_weight, np.uint16),
+        _ptr(cos_sin_cache, np.float32), _ptr(position_ids, np.int64))

@@ -139,6 +139,44 @@ uint16_t oracle_bf16_rne(double v) {
   return sign | static_cast<uint16_t>(u >> 16);
 }
 
+double oracle_fp16_to_double(uint16_t bits) {
+  // IEEE binary16: sign, 5 exponent bits (bias 15), 10 mantissa bits.
+  const int sign = bits >> 15;
+  const int exp_field = (bits >> 10) & 0x1F;
+  const int mant = bits & 0x3FF;
+  double mag;
+  if (exp_field == 0x1F)
+    mag = mant ? std::nan("") : HUGE_VAL;
+  else if (exp_field == 0)
+    mag = std::ldexp(static_cast<double>(mant), -24);
+  else
+    mag = std::ldexp(1.0 + mant / 1024.0, exp_field - 15);
+  return sign ? -mag : mag;
+}
+
+uint16_t oracle_fp16_rne(double v) {
+  if (std::isnan(v)) return 0x7E00;
+  NearestEven mode;
+  const uint16_t sign = std::signbit(v) ? 0x8000 : 0;
+  const double a = std::fabs(v);
+  double r = 0.0;
+  if (a != 0.0) {
+    int k;
+    std::frexp(a, &k);
+    const int top = k - 1;
+    const int lsb_exp = (top < -14 ? -14 : top) - 10;  // subnormal spacing 2^-24
+    r = round_to_quantum(a, std::ldexp(1.0, lsb_exp));
+  }
+  if (r > 65504.0) return sign | 0x7C00;  // rounds past the largest finite
+  if (r < std::ldexp(1.0, -14))
+    return sign | static_cast<uint16_t>(std::ldexp(r, 24));
+  int k;
+  const double m = std::frexp(r, &k);
+  const int exp_field = (k - 1) + 15;
+  const int mant = static_cast<int>((2.0 * m - 1.0) * 1024.0);
+  return sign | static_cast<uint16_t>((exp_field << 10) | mant);
+}
+
 double oracle_e4m3_decode(uint8_t code) {
   // OCP 8-bit floating point, E4M3: sign, 4 exponent bits (bias 7), 3
   // mantissa bits; exponent field 0 is subnormal; S.1111.111 is NaN.
@@ -330,6 +368,45 @@ void oracle_qk_norm_rope_packed(
       // own weight into the rotation ([P3] "Summary", paired-weight rule).
       for (int i = 0; i < half; ++i) rotate_pair(&y[i], &y[i + half], cosv[i], sinv[i]);
       for (int d = 0; d < head_dim; ++d) xh[d] = oracle_bf16_rne(y[d]);
+    }
+  }
+  delete[] y;
+}
+
+void oracle_qk_norm_rope_packed_ex(
+    uint16_t* qkv, int64_t num_tokens, int32_t num_heads_q,
+    int32_t num_heads_k, int32_t num_heads_v, int32_t head_dim,
+    int32_t rotary_dim, int32_t is_neox, int32_t is_fp16, double eps,
+    const uint16_t* q_weight, const uint16_t* k_weight,
+    const float* cos_sin_cache, const int64_t* position_ids) {
+  const int64_t row_elems =
+      static_cast<int64_t>(num_heads_q + num_heads_k + num_heads_v) * head_dim;
+  const int half = rotary_dim / 2;
+  auto decode = [is_fp16](uint16_t b) {
+    return is_fp16 ? oracle_fp16_to_double(b) : oracle_bf16_to_double(b);
+  };
+  auto encode = [is_fp16](double v) {
+    return is_fp16 ? oracle_fp16_rne(v) : oracle_bf16_rne(v);
+  };
+  double* y = new double[head_dim];
+  for (int64_t t = 0; t < num_tokens; ++t) {
+    const float* row = cos_sin_cache + position_ids[t] * rotary_dim;
+    for (int32_t h = 0; h < num_heads_q + num_heads_k; ++h) {
+      uint16_t* xh = qkv + t * row_elems + static_cast<int64_t>(h) * head_dim;
+      const uint16_t* w = h < num_heads_q ? q_weight : k_weight;
+      // RMSNorm over the whole head with its own weight per element
+      double sum_sq = 0.0;
+      for (int d = 0; d < head_dim; ++d) sum_sq += decode(xh[d]) * decode(xh[d]);
+      const double inv_rms = 1.0 / std::sqrt(sum_sq / head_dim + eps);
+      for (int d = 0; d < head_dim; ++d) y[d] = decode(xh[d]) * inv_rms * decode(w[d]);
+      // rotation of the first rotary_dim dims only
+      for (int i = 0; i < half; ++i) {
+        if (is_neox)
+          rotate_pair(&y[i], &y[i + half], row[i], row[half + i]);
+        else
+          rotate_pair(&y[2 * i], &y[2 * i + 1], row[i], row[half + i]);
+      }
+      for (int d = 0; d < head_dim; ++d) xh[d] = encode(y[d]);
     }
   }
   delete[] y;

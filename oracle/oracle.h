@@ -44,6 +44,12 @@ double oracle_bf16_to_double(uint16_t bits);
 /* bf16 bit pattern nearest to v, ties to even (one rounding from double). */
 uint16_t oracle_bf16_rne(double v);
 
+/* Exact value of an IEEE binary16 (fp16) bit pattern. */
+double oracle_fp16_to_double(uint16_t bits);
+
+/* fp16 bit pattern nearest to v, ties to even; overflow gives +-inf. */
+uint16_t oracle_fp16_rne(double v);
+
 /* Value of an OCP FP8 E4M3 ("fn": no infinities, 0x7F/0xFF are NaN) code.
  * NaN codes decode to NaN. */
 double oracle_e4m3_decode(uint8_t code);
@@ -147,6 +153,26 @@ void oracle_kv_cache_gather_dequant(const uint8_t* kv_cache,
 void oracle_qk_norm_rope_packed(
     uint16_t* qkv, int64_t num_tokens, int32_t num_heads_q,
     int32_t num_heads_k, int32_t num_heads_v, int32_t head_dim, double eps,
+    const uint16_t* q_weight, const uint16_t* k_weight,
+    const float* cos_sin_cache, const int64_t* position_ids);
+
+/*
+ * The packed operator beyond the page's guarded fast path ([P3] "Summary" and
+ * "Notes for Reviewers": the first implementation is restricted to bf16,
+ * head_dim 128, full-dimension NeoX RoPE).  Here:
+ *   head_dim      any even D
+ *   rotary_dim    R, even, R <= D: only dims [0, R) of a head rotate (partial
+ *                 rotary); dims [R, D) are normalised and weighted only
+ *   is_neox       1: pairs (i, i + R/2); 0: interleaved pairs (2i, 2i + 1);
+ *                 i < R/2 in both, rotated by cos_i, sin_i
+ *   is_fp16       0: qkv and both weights are bf16; 1: all three are fp16
+ *   cos_sin_cache fp32 [max_position, R] = R/2 cosines then R/2 sines
+ * With D = R = 128, is_neox = 1, is_fp16 = 0 this is oracle_qk_norm_rope_packed.
+ */
+void oracle_qk_norm_rope_packed_ex(
+    uint16_t* qkv, int64_t num_tokens, int32_t num_heads_q,
+    int32_t num_heads_k, int32_t num_heads_v, int32_t head_dim,
+    int32_t rotary_dim, int32_t is_neox, int32_t is_fp16, double eps,
     const uint16_t* q_weight, const uint16_t* k_weight,
     const float* cos_sin_cache, const int64_t* position_ids);
 

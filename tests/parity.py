@@ -51,6 +51,28 @@ def check_bf16(got, ref, what=""):
     return frac
 
 
+def fp16_val(bits):
+    return np.asarray(bits, np.uint16).view(np.float16).astype(np.float64)
+
+
+def check_fp16(got, ref, what=""):
+    """fp16 outputs: |got - ref| <= 2^-10 |ref| + 1e-4 (one fp16 step) and at
+    most MAX_MISMATCH of the values differing in their bits."""
+    got = np.asarray(got, np.uint16)
+    ref = np.asarray(ref, np.uint16)
+    assert got.shape == ref.shape, (what, got.shape, ref.shape)
+    g, r = fp16_val(got), fp16_val(ref)
+    bad = ~(np.abs(g - r) <= 2.0 ** -10 * np.abs(r) + 1e-4)
+    if bad.any():
+        i = np.flatnonzero(bad.ravel())[:5]
+        raise AssertionError(
+            f"{what}: {bad.sum()} fp16 values out of tolerance, e.g. at {i}: "
+            f"got {g.ravel()[i]} ref {r.ravel()[i]}")
+    frac = float(np.mean(got != ref)) if got.size else 0.0
+    assert frac <= MAX_MISMATCH, f"{what}: {frac:.2e} of fp16 values differ in bits"
+    return frac
+
+
 def _signed_code(c):
     c = np.asarray(c, np.int32)
     mag = c & 0x7F

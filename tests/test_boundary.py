@@ -96,6 +96,25 @@ def test_packed_argument_errors(over, want):
     assert _packed(**over) == want
 
 
+def _packed_ex(**over):
+    a = dict(qkv=FAKE, T=4, hq=16, hk=8, hv=8, D=128, eps=1e-6, qw=FAKE, kw=FAKE,
+             cs=FAKE, neox=1, pos=FAKE, R=64, dtype=0, maxp=16, stream=None)
+    a.update(over)
+    return K.lib().qk_norm_rope_packed_ex(*a.values())
+
+
+@pytest.mark.parametrize("over,want", [
+    (dict(T=-1), 2), (dict(hq=0, hk=0), 2), (dict(maxp=0), 2),
+    (dict(D=96), 3), (dict(D=512), 3), (dict(R=24), 3), (dict(R=144), 3),
+    (dict(R=-16), 3), (dict(neox=2), 3), (dict(dtype=2), 3),
+    (dict(qkv=None), 1), (dict(pos=None), 1), (dict(cs=None), 1),
+    (dict(qw=None), 1), (dict(qkv=FAKE + 8), 4), (dict(cs=FAKE + 4), 4),
+    (dict(T=0), 0),
+])
+def test_packed_ex_argument_errors(over, want):
+    assert _packed_ex(**over) == want
+
+
 def _dequant(**over):
     a = dict(cache=FAKE, scale=FAKE, pages=2, page=64, slots=FAKE, rows=10,
              out=FAKE, stream=None)
@@ -161,6 +180,7 @@ def test_no_device_is_reported_not_launched():
     assert _dequant() == 5
     assert _dequant(pages=0, cache=None, scale=None) == 5
     assert _norm() == 5 and _rope() == 5 and _quant() == 5
+    assert _packed_ex() == 5 and _packed_ex(R=0, cs=None) == 5
 
 
 def test_knobs():

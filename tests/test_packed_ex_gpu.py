@@ -1,0 +1,117 @@
+"""Parity of the general packed Q/K norm + RoPE (head_dim 64/128/256, partial
+rotary, NeoX or interleaved, bf16 or fp16) with the oracle's general form.
+Needs an MI355X."""
+
+import numpy as np
+import pytest
+import torch
+
+import fp8_kv_cache_slot_amd as K
+import oracle as O
+from fp8_kv_cache_slot_amd import inputs as I
+from tests import parity as P
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def _bits(t):
+    t = t.detach().contiguous().cpu()
+    return t.view(torch.int16).numpy().view(np.uint16)
+
+
+def _make(T, hq, hk, hv, D, R, dtype, seed, max_pos=4096):
+    g = torch.Generator(device=DEV)
+    g.manual_seed(seed)
+    qkv = torch.randn((T, (hq + hk + hv) * D), generator=g, device=DEV).to(dtype)
+    qw = (torch.rand(D, generator=g, device=DEV) + 0.5).to(dtype)
+    kw = (torch.rand(D, generator=g, device=DEV) + 0.5).to(dtype)
+    cs = I.cos_sin_cache(max_pos, max(R, 2), device=DEV)
+    if R == 0:
+        cs = torch.zeros((max_pos, 0), dtype=torch.float32, device=DEV)
+    pos = torch.randint(0, max_pos, (T,), generator=g, device=DEV)
+    return qkv, qw, kw, cs, pos
+
+
+def _check(qkv, out, hq, hk, hv, D, R, neox, dtype, qw, kw, cs, pos, what):
+    ref = _bits(qkv).copy()
+    O.qk_norm_rope_packed_ex(ref, hq, hk, hv, D, R, int(neox),
+                             int(dtype == torch.float16), 1e-6, _bits(qw),
+                             _bits(kw), I.bits(cs).copy(), I.bits(pos))
+    got = _bits(out)
+    n = (hq + hk) * D
+    np.testing.assert_array_equal(got[:, n:], _bits(qkv)[:, n:],
+                                  err_msg=what + ": V changed")
+    chk = P.check_fp16 if dtype == torch.float16 else P.check_bf16
+    chk(got[:, :n], ref[:, :n], what)
+
+
+CASES = [(D, R, neox, dt)
+         for D in (64, 128, 256)
+         for R in sorted({D, D // 2, 16 if D == 64 else 32})
+         for neox in (True, False)
+         for dt in (torch.bfloat16, torch.float16)]
+# rotary widths whose NeoX partner distance (R/16 lanes) is not a power of two
+CASES += [(128, 48, True, torch.bfloat16), (128, 48, False, torch.float16),
+          (256, 80, True, torch.float16), (256, 208, True, torch.bfloat16)]
+
+
+@pytest.mark.parametrize("D,R,neox,dtype", CASES,
+                         ids=[f"D{c[0]}-R{c[1]}-{'neox' if c[2] else 'inter'}-"
+                              f"{'f16' if c[3] == torch.float16 else 'bf16'}"
+                              for c in CASES])
+def test_variants(D, R, neox, dtype):
+    for T, (hq, hk, hv) in [(1, (16, 8, 8)), (33, (5, 3, 1)), (7, (0, 4, 2))]:
+        qkv, qw, kw, cs, pos = _make(T, hq, hk, hv, D, R, dtype, seed=D + R + T)
+        out = qkv.clone()
+        K.qk_norm_rope_packed_ex(out, hq, hk, hv, D, 1e-6, qw, kw, cs, neox, pos,
+                                 rotary_dim=R)
+        torch.cuda.synchronize()
+        _check(qkv, out, hq, hk, hv, D, R, neox, dtype, qw, kw, cs, pos,
+               f"D={D} R={R} neox={neox} {dtype} T={T} heads={hq},{hk},{hv}")
+
+
+def test_no_rotation_and_large_token_count():
+    qkv, qw, kw, cs, pos = _make(2048, 16, 8, 8, 128, 0, torch.float16, seed=91)
+    out = qkv.clone()
+    K.qk_norm_rope_packed_ex(out, 16, 8, 8, 128, 1e-6, qw, kw, cs, True, pos,
+                             rotary_dim=0)
+    torch.cuda.synchronize()
+    _check(qkv, out, 16, 8, 8, 128, 0, True, torch.float16, qw, kw, cs, pos, "R=0")
+    qkv, qw, kw, cs, pos = _make(8192, 32, 8, 8, 64, 64, torch.bfloat16, seed=92)
+    out = qkv.clone()
+    K.qk_norm_rope_packed_ex(out, 32, 8, 8, 64, 1e-6, qw, kw, cs, False, pos)
+    torch.cuda.synchronize()
+    _check(qkv, out, 32, 8, 8, 64, 64, False, torch.bfloat16, qw, kw, cs, pos,
+           "T=8192 D=64")
+
+
+def test_guarded_case_goes_to_the_tuned_kernel_with_identical_results():
+    x = I.make_packed(I.PACKED_WORKLOADS["packed_t17"], DEV)
+    a, b = x["qkv"].clone(), x["qkv"].clone()
+    K.qk_norm_rope_packed(a, 16, 8, 8, 128, 1e-6, x["q_weight"], x["k_weight"],
+                          x["cos_sin_cache"], True, x["position_ids"])
+    K.qk_norm_rope_packed_ex(b, 16, 8, 8, 128, 1e-6, x["q_weight"], x["k_weight"],
+                             x["cos_sin_cache"], True, x["position_ids"])
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
+def test_rejects_and_out_of_range_positions():
+    for R in (40, 136):   # not a multiple of 16 / wider than the head
+        qkv, qw, kw, cs, pos = _make(5, 4, 2, 2, 128, R, torch.bfloat16, seed=93)
+        before = qkv.clone()
+        with pytest.raises(K.Fp8kvError):
+            K.qk_norm_rope_packed_ex(qkv, 4, 2, 2, 128, 1e-6, qw, kw, cs, True,
+                                     pos, rotary_dim=R)
+        assert torch.equal(qkv, before)
+    qkv, qw, kw, cs, pos = _make(5, 4, 2, 2, 64, 32, torch.float16, seed=94)
+    pos[3] = cs.shape[0]
+    out = qkv.clone()
+    K.qk_norm_rope_packed_ex(out, 4, 2, 2, 64, 1e-6, qw, kw, cs, False, pos,
+                             rotary_dim=32)
+    torch.cuda.synchronize()
+    assert torch.equal(out[3], qkv[3])
+    keep = torch.tensor([0, 1, 2, 4], device=DEV)
+    _check(qkv[keep].contiguous(), out[keep].contiguous(), 4, 2, 2, 64, 32, False,
+           torch.float16, qw, kw, cs, pos[keep].contiguous(), "in-range tokens")
