@@ -47,7 +47,7 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-KERNEL_SOURCES = ("dsv4_prologue.hip", "wave_ops.hpp")
+KERNEL_SOURCES = ("dsv4_prologue.hip", "kv_quant.hpp", "wave_ops.hpp")
 
 
 def kernel_source_hash() -> str:
@@ -216,6 +216,18 @@ def main():
                        "fusion_speedup": round(statistics.median(uper) /
                                                statistics.median(per), 3)}
     log(f"unfused prefill: {unfused_prefill}")
+
+    # ---- the scalar-scale cache convention on the same workload ----------
+    sscale = torch.tensor([0.0173], dtype=torch.float32, device=dev)
+    _, sper = time_launches(lambda: K.qnorm_rope_kv_quant_insert_scalar_scale(
+        q, x["kv"], x["q_weight"], x["kv_weight"], x["cos_sin_cache"],
+        x["positions"], x["slot_mapping"], cache, sscale, x["eps"]), 20, 3)
+    sm_all = x["slot_mapping"]
+    written = int(((sm_all >= 0) & (sm_all < w.num_pages * 64)).sum().item())
+    sb = A.dsv4_scalar_bytes(w.num_tokens, w.num_heads, written)
+    scalar_prefill = {"median_us": round(statistics.median(sper) * 1e6, 1),
+                      "gbps": round(sb / statistics.median(sper) / 1e9, 1)}
+    log(f"scalar-scale prefill: {scalar_prefill}")
     del q, cache, scale, kv_work
 
     # ---- CPU baseline: the oracle on a bounded slice of the same workload --
@@ -294,6 +306,7 @@ def main():
             del xx, qq, cc, ss
             torch.cuda.empty_cache()
         extra["unfused_prefill"] = unfused_prefill
+        extra["scalar_scale_prefill"] = scalar_prefill
         for name in ("tiny", "decode"):
             wl = I.DSV4_WORKLOADS[name]
             xx = I.make_dsv4(wl, dev)
@@ -329,6 +342,26 @@ def main():
                                  "bytes": nb, "median_us": round(m * 1e6, 2),
                                  "gbps": round(nb / m / 1e9, 1)}
         log(f"packed_t8192: {extra['packed_t8192']}")
+        # packed variants the guarded fast path does not cover
+        for label, D, R, neox, dt in [("packed_ex_d64_inter_f16", 64, 64, False, torch.float16),
+                                      ("packed_ex_d256_neox_r128_bf16", 256, 128, True,
+                                       torch.bfloat16)]:
+            g = torch.Generator(device=dev)
+            g.manual_seed(D + R)
+            hq, hk, hv = 16, 8, 8
+            T = 8192
+            vq = torch.randn((T, (hq + hk + hv) * D), generator=g, device=dev).to(dt)
+            vw = (torch.rand(D, generator=g, device=dev) + 0.5).to(dt)
+            vcs = I.cos_sin_cache(8192, R, device=dev)
+            vpos = torch.randint(0, 8192, (T,), generator=g, device=dev)
+            tot, per = time_launches(lambda: K.qk_norm_rope_packed_ex(
+                vq, hq, hk, hv, D, 1e-6, vw, vw, vcs, neox, vpos, rotary_dim=R), 50, 10)
+            m = statistics.median(per)
+            nb = A.packed_bytes(T, hq, hk, D, R)
+            extra[label] = {"tokens": T, "heads": f"{hq}q/{hk}k/{hv}v x {D}",
+                            "rotary_dim": R, "bytes": nb,
+                            "median_us": round(m * 1e6, 2), "gbps": round(nb / m / 1e9, 1)}
+            log(f"{label}: {extra[label]}")
         result["extra"] = extra
 
     print(json.dumps(result), flush=True)

@@ -34,6 +34,8 @@ STATUS = {0: "FP8KV_OK", 1: "FP8KV_ERR_NULL", 2: "FP8KV_ERR_SHAPE",
 EXPORTED = ["qnorm_rope_kv_quant_insert", "qk_norm_rope_packed",
             "kv_cache_gather_dequant", "rms_norm_rows", "rope_rows",
             "qk_norm_rope_packed_ex",
+            "qnorm_rope_kv_quant_insert_scalar_scale",
+            "kv_cache_gather_dequant_scalar_scale",
             "kv_quant_insert",
             "fp8kv_status_string", "fp8kv_abi_version",
             "fp8kv_set_dispatch_threshold", "fp8kv_get_dispatch_threshold",
@@ -67,6 +69,11 @@ def lib() -> ctypes.CDLL:
     L.qk_norm_rope_packed.argtypes = [
         P, I64, I32, I32, I32, I32, F, P, P, P, I32, P, I32, I64, P]
     L.qk_norm_rope_packed.restype = ctypes.c_int
+    L.qnorm_rope_kv_quant_insert_scalar_scale.argtypes = [
+        P, P, P, P, P, P, P, P, P, I64, I32, I32, I32, I64, I64, I32, F, P]
+    L.qnorm_rope_kv_quant_insert_scalar_scale.restype = ctypes.c_int
+    L.kv_cache_gather_dequant_scalar_scale.argtypes = [P, P, I64, I32, P, I64, P, P]
+    L.kv_cache_gather_dequant_scalar_scale.restype = ctypes.c_int
     L.qk_norm_rope_packed_ex.argtypes = [
         P, I64, I32, I32, I32, I32, F, P, P, P, I32, P, I32, I32, I64, P]
     L.qk_norm_rope_packed_ex.restype = ctypes.c_int
@@ -148,6 +155,63 @@ def qnorm_rope_kv_quant_insert(q, kv, q_weight, kv_weight, cos_sin_cache,
         float(eps), _stream(stream))
     if st:
         raise Fp8kvError(st, "qnorm_rope_kv_quant_insert")
+
+
+def qnorm_rope_kv_quant_insert_scalar_scale(q, kv, q_weight, kv_weight,
+                                            cos_sin_cache, positions,
+                                            slot_mapping, kv_cache,
+                                            kv_cache_scale, eps: float = 1e-6,
+                                            stream=None) -> None:
+    """The fused prologue writing the scalar-scale FP8 cache: codes of
+    y / kv_cache_scale (a one-element fp32 device tensor), no exponents."""
+    if q.dim() != 3:
+        raise ValueError("q must be [T, H, 512]")
+    T, H, D = q.shape
+    _check(q, "q", torch.bfloat16)
+    _check(kv, "kv", torch.bfloat16, (T, D))
+    _check(q_weight, "q_weight", torch.bfloat16, (D,))
+    _check(kv_weight, "kv_weight", torch.bfloat16, (D,))
+    _check(cos_sin_cache, "cos_sin_cache", torch.float32)
+    if cos_sin_cache.dim() != 2:
+        raise ValueError("cos_sin_cache must be [max_position, rope_dim]")
+    _check(positions, "positions", torch.int64, (T,))
+    _check(slot_mapping, "slot_mapping", torch.int64, (T,))
+    _check(kv_cache, "kv_cache", torch.uint8)
+    if kv_cache.dim() != 3 or kv_cache.shape[2] != ROW_BYTES:
+        raise ValueError("kv_cache must be [num_pages, page_size, 576]")
+    pages, page_size, _ = kv_cache.shape
+    _check(kv_cache_scale, "kv_cache_scale", torch.float32, (1,))
+    st = lib().qnorm_rope_kv_quant_insert_scalar_scale(
+        q.data_ptr(), kv.data_ptr(), q_weight.data_ptr(), kv_weight.data_ptr(),
+        cos_sin_cache.data_ptr(), positions.data_ptr(), slot_mapping.data_ptr(),
+        kv_cache.data_ptr(), kv_cache_scale.data_ptr(), T, H, D,
+        cos_sin_cache.shape[1], cos_sin_cache.shape[0], pages, page_size,
+        float(eps), _stream(stream))
+    if st:
+        raise Fp8kvError(st, "qnorm_rope_kv_quant_insert_scalar_scale")
+
+
+def kv_cache_gather_dequant_scalar_scale(kv_cache, kv_cache_scale, slots,
+                                         out=None, stream=None):
+    """Read side of the scalar-scale cache: bf16 [N, 512]."""
+    _check(kv_cache, "kv_cache", torch.uint8)
+    if kv_cache.dim() != 3 or kv_cache.shape[2] != ROW_BYTES:
+        raise ValueError("kv_cache must be [num_pages, page_size, 576]")
+    pages, page_size, _ = kv_cache.shape
+    _check(kv_cache_scale, "kv_cache_scale", torch.float32, (1,))
+    if slots.dim() != 1:
+        raise ValueError("slots must be one-dimensional")
+    _check(slots, "slots", torch.int64)
+    n = slots.shape[0]
+    if out is None:
+        out = torch.empty((n, HEAD_DIM), dtype=torch.bfloat16, device=slots.device)
+    _check(out, "out", torch.bfloat16, (n, HEAD_DIM))
+    st = lib().kv_cache_gather_dequant_scalar_scale(
+        kv_cache.data_ptr(), kv_cache_scale.data_ptr(), pages, page_size,
+        slots.data_ptr(), n, out.data_ptr(), _stream(stream))
+    if st:
+        raise Fp8kvError(st, "kv_cache_gather_dequant_scalar_scale")
+    return out
 
 
 def qk_norm_rope_packed(qkv, num_heads_q: int, num_heads_k: int,

@@ -7,6 +7,9 @@ and the slot index (8 + 8 B), one cos/sin row shared by all heads (64 fp32 =
 the 64 bf16 rotary dims (128 B) and 7 exponent bytes; plus both weight vectors
 once (2 * 1024 B).
 
+The scalar-scale cache convention moves the same bytes minus the 7
+exponent bytes per written token (plus one 4-byte scale).
+
 Cache read side (gather + dequantise), per output row: the slot index (8 B)
 and the bf16 row written (1024 B); per row whose slot is valid also the 576
 cache bytes and the 7 exponent bytes read.
@@ -37,10 +40,17 @@ def dsv4_bytes(num_tokens: int, num_heads: int, num_written: int) -> int:
 
 
 def packed_bytes(num_tokens: int, num_heads_q: int, num_heads_k: int,
-                 head_dim: int) -> int:
-    per_token = 4 * (num_heads_q + num_heads_k) * head_dim + 8 + 4 * head_dim
+                 head_dim: int, rotary_dim: int | None = None) -> int:
+    """Per token: Q and K heads read + written (2-byte elements), the
+    position, one cos/sin row of rotary_dim fp32 (default the whole head)."""
+    r = head_dim if rotary_dim is None else rotary_dim
+    per_token = 4 * (num_heads_q + num_heads_k) * head_dim + 8 + 4 * r
     return num_tokens * per_token + 2 * 2 * head_dim
 
 
 def dequant_bytes(num_rows: int, num_valid: int) -> int:
     return num_rows * (8 + 2 * HEAD_DIM) + num_valid * (448 + 2 * ROPE_DIM + 7)
+
+
+def dsv4_scalar_bytes(num_tokens: int, num_heads: int, num_written: int) -> int:
+    return dsv4_bytes(num_tokens, num_heads, num_written) - 7 * num_written + 4

@@ -52,19 +52,26 @@ int check_device() {
 }  // namespace
 }  // namespace fp8kv
 
-FP8KV_API int qnorm_rope_kv_quant_insert(
-    void* q, const void* kv, const void* q_weight, const void* kv_weight,
-    const float* cos_sin_cache, const int64_t* positions,
-    const int64_t* slot_mapping, uint8_t* kv_cache, uint8_t* kv_scale,
-    int64_t num_tokens, int32_t num_heads, int32_t head_dim, int32_t rope_dim,
-    int64_t max_position, int64_t num_pages, int32_t page_size, float eps,
-    void* stream) {
-  using namespace fp8kv;
+namespace fp8kv {
+namespace {
+
+int prologue(void* q, const void* kv, const void* q_weight, const void* kv_weight,
+             const float* cos_sin_cache, const int64_t* positions,
+             const int64_t* slot_mapping, uint8_t* kv_cache, uint8_t* kv_scale,
+             bool scalar, const float* scalar_scale, int64_t num_tokens,
+             int32_t num_heads,
+             int32_t head_dim, int32_t rope_dim, int64_t max_position,
+             int64_t num_pages, int32_t page_size, float eps, void* stream) {
+  // For the scalar-scale convention the scale pointer takes the exponent
+  // tensor's place in the NULL check (required when the cache has pages).
+  const uint8_t* scale_ptr =
+      scalar ? reinterpret_cast<const uint8_t*>(scalar_scale) : kv_scale;
   int st = validate_prologue(q, kv, q_weight, kv_weight, cos_sin_cache,
-                             positions, slot_mapping, kv_cache, kv_scale,
+                             positions, slot_mapping, kv_cache, scale_ptr,
                              num_tokens, num_heads, head_dim, rope_dim,
                              max_position, num_pages, page_size);
   if (st != FP8KV_OK || num_tokens == 0) return st;
+  if (scalar && scalar_scale && !aligned(scalar_scale, 4)) return FP8KV_ERR_ALIGN;
   st = check_device();
   if (st != FP8KV_OK) return st;
 
@@ -77,7 +84,9 @@ FP8KV_API int qnorm_rope_kv_quant_insert(
   a.positions = positions;
   a.slot_mapping = slot_mapping;
   a.kv_cache = kv_cache;
-  a.kv_scale = kv_scale;
+  a.kv_scale = scalar ? nullptr : kv_scale;
+  a.scalar_scale = scalar ? scalar_scale : nullptr;
+  a.scalar = scalar;
   a.num_tokens = static_cast<int32_t>(num_tokens);
   a.num_heads = num_heads;
   a.num_cache_slots = num_pages * kPageSize;
@@ -90,6 +99,37 @@ FP8KV_API int qnorm_rope_kv_quant_insert(
     return launch_prologue(a, 1, 1, s);
   const int32_t tiling = g_tiling.load(std::memory_order_relaxed);
   return launch_prologue(a, tiling >> 16, tiling & 0xFFFF, s);
+}
+
+}  // namespace
+}  // namespace fp8kv
+
+FP8KV_API int qnorm_rope_kv_quant_insert(
+    void* q, const void* kv, const void* q_weight, const void* kv_weight,
+    const float* cos_sin_cache, const int64_t* positions,
+    const int64_t* slot_mapping, uint8_t* kv_cache, uint8_t* kv_scale,
+    int64_t num_tokens, int32_t num_heads, int32_t head_dim, int32_t rope_dim,
+    int64_t max_position, int64_t num_pages, int32_t page_size, float eps,
+    void* stream) {
+  return fp8kv::prologue(q, kv, q_weight, kv_weight, cos_sin_cache, positions,
+                         slot_mapping, kv_cache, kv_scale, false, nullptr,
+                         num_tokens,
+                         num_heads, head_dim, rope_dim, max_position, num_pages,
+                         page_size, eps, stream);
+}
+
+FP8KV_API int qnorm_rope_kv_quant_insert_scalar_scale(
+    void* q, const void* kv, const void* q_weight, const void* kv_weight,
+    const float* cos_sin_cache, const int64_t* positions,
+    const int64_t* slot_mapping, uint8_t* kv_cache, const float* kv_cache_scale,
+    int64_t num_tokens, int32_t num_heads, int32_t head_dim, int32_t rope_dim,
+    int64_t max_position, int64_t num_pages, int32_t page_size, float eps,
+    void* stream) {
+  return fp8kv::prologue(q, kv, q_weight, kv_weight, cos_sin_cache, positions,
+                         slot_mapping, kv_cache, nullptr, true, kv_cache_scale,
+                         num_tokens,
+                         num_heads, head_dim, rope_dim, max_position, num_pages,
+                         page_size, eps, stream);
 }
 
 FP8KV_API int qk_norm_rope_packed(
@@ -184,6 +224,8 @@ FP8KV_API int kv_cache_gather_dequant(const uint8_t* kv_cache,
   DequantArgs a;
   a.kv_cache = kv_cache;
   a.kv_scale = kv_scale;
+  a.scalar_scale = nullptr;
+  a.scalar = false;
   a.slots = slots;
   a.out = static_cast<uint16_t*>(out);
   a.num_rows = static_cast<int32_t>(num_rows);
@@ -235,6 +277,30 @@ FP8KV_API int kv_quant_insert(const void* kv, const int64_t* slot_mapping,
                                 static_cast<int32_t>(num_tokens),
                                 num_pages * kPageSize,
                                 static_cast<hipStream_t>(stream));
+}
+
+FP8KV_API int kv_cache_gather_dequant_scalar_scale(
+    const uint8_t* kv_cache, const float* kv_cache_scale, int64_t num_pages,
+    int32_t page_size, const int64_t* slots, int64_t num_rows, void* out,
+    void* stream) {
+  using namespace fp8kv;
+  int st = validate_gather_dequant(
+      kv_cache, reinterpret_cast<const uint8_t*>(kv_cache_scale), num_pages,
+      page_size, slots, num_rows, out);
+  if (st != FP8KV_OK || num_rows == 0) return st;
+  if (num_pages > 0 && !aligned(kv_cache_scale, 4)) return FP8KV_ERR_ALIGN;
+  st = check_device();
+  if (st != FP8KV_OK) return st;
+  DequantArgs a;
+  a.kv_cache = kv_cache;
+  a.kv_scale = nullptr;
+  a.scalar_scale = kv_cache_scale;  // read only for valid slots (num_pages > 0)
+  a.scalar = true;
+  a.slots = slots;
+  a.out = static_cast<uint16_t*>(out);
+  a.num_rows = static_cast<int32_t>(num_rows);
+  a.num_cache_slots = num_pages * kPageSize;
+  return launch_gather_dequant(a, static_cast<hipStream_t>(stream));
 }
 
 FP8KV_API const char* fp8kv_status_string(int status) {

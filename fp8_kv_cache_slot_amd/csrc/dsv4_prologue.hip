@@ -55,13 +55,14 @@ __device__ __forceinline__ void rotate4(float* y, f32x4_t c, f32x4_t s) {
   }
 }
 
+template <bool SCALAR>
 __device__ __forceinline__ void kv_row(
     int32_t t, const uint16_t* __restrict__ kv,
     const uint16_t* __restrict__ kv_weight, const float* __restrict__ cos_sin,
     const int64_t* __restrict__ positions,
     const int64_t* __restrict__ slot_mapping, uint8_t* __restrict__ kv_cache,
-    uint8_t* __restrict__ kv_scale, int64_t num_cache_slots,
-    int64_t max_position, float eps) {
+    uint8_t* __restrict__ kv_scale, const float* __restrict__ scalar_scale,
+    int64_t num_cache_slots, int64_t max_position, float eps) {
   const int lane = lane_id();
   const int64_t slot = slot_mapping[t];
   if (slot < 0 || slot >= num_cache_slots) return;  // skipped token
@@ -81,17 +82,21 @@ __device__ __forceinline__ void kv_row(
   rms_normalise(x, w, eps, y);
   if (lane >= kRopeLane0) rotate4(y, c, s);
 
-  quantise_store_row(y, lane, kv_cache + slot * 576, kv_scale + slot * 8);
+  if constexpr (SCALAR)
+    quantise_store_row_scalar(y, lane, kv_cache + slot * 576, *scalar_scale);
+  else
+    quantise_store_row(y, lane, kv_cache + slot * 576, kv_scale + slot * 8);
 }
 
-template <int WAVES, int QS>
+template <int WAVES, int QS, bool SCALAR>
 __global__ void __launch_bounds__(WAVES * 64) dsv4_prologue_kernel(
     uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
     const uint16_t* __restrict__ q_weight,
     const uint16_t* __restrict__ kv_weight, const float* __restrict__ cos_sin,
     const int64_t* __restrict__ positions,
     const int64_t* __restrict__ slot_mapping, uint8_t* __restrict__ kv_cache,
-    uint8_t* __restrict__ kv_scale, int32_t num_tokens, int32_t num_heads,
+    uint8_t* __restrict__ kv_scale, const float* __restrict__ scalar_scale,
+    int32_t num_tokens, int32_t num_heads,
     int32_t waves_per_token, int32_t q_waves, int32_t kv_blocks,
     int64_t num_cache_slots, int64_t max_position, float eps) {
   const int lane = lane_id();
@@ -100,8 +105,9 @@ __global__ void __launch_bounds__(WAVES * 64) dsv4_prologue_kernel(
   if (b < kv_blocks) {
     const int32_t t = b * WAVES + wave;
     if (t < num_tokens)
-      kv_row(t, kv, kv_weight, cos_sin, positions, slot_mapping, kv_cache,
-                 kv_scale, num_cache_slots, max_position, eps);
+      kv_row<SCALAR>(t, kv, kv_weight, cos_sin, positions, slot_mapping,
+                     kv_cache, kv_scale, scalar_scale, num_cache_slots,
+                     max_position, eps);
     return;
   }
   b -= kv_blocks;
@@ -158,7 +164,7 @@ __global__ void __launch_bounds__(WAVES * 64) dsv4_prologue_kernel(
   }
 }
 
-template <int WAVES, int QS>
+template <int WAVES, int QS, bool SCALAR>
 int launch(const PrologueArgs& a, hipStream_t stream) {
   const int32_t waves_per_token = (a.num_heads + QS - 1) / QS;
   const int64_t kv_blocks = (static_cast<int64_t>(a.num_tokens) + WAVES - 1) / WAVES;
@@ -176,12 +182,13 @@ int launch(const PrologueArgs& a, hipStream_t stream) {
       const_cast<const int64_t**>(&a.positions),
       const_cast<const int64_t**>(&a.slot_mapping),
       const_cast<uint8_t**>(&a.kv_cache),    const_cast<uint8_t**>(&a.kv_scale),
+      const_cast<const float**>(&a.scalar_scale),
       const_cast<int32_t*>(&a.num_tokens),   const_cast<int32_t*>(&a.num_heads),
       const_cast<int32_t*>(&waves_per_token), &q_waves, &kvb,
       const_cast<int64_t*>(&a.num_cache_slots),
       const_cast<int64_t*>(&a.max_position), const_cast<float*>(&a.eps)};
   hipError_t err = hipLaunchKernel(
-      reinterpret_cast<const void*>(&dsv4_prologue_kernel<WAVES, QS>),
+      reinterpret_cast<const void*>(&dsv4_prologue_kernel<WAVES, QS, SCALAR>),
       dim3(static_cast<uint32_t>(blocks)), dim3(WAVES * 64), args, 0, stream);
   return err == hipSuccess ? FP8KV_OK : FP8KV_ERR_LAUNCH;
 }
@@ -191,8 +198,14 @@ int launch(const PrologueArgs& a, hipStream_t stream) {
 // Instantiated (waves per block, Q heads per wave) shapes.  (1, 1) is the
 // small-batch kernel: one head per 64-lane block.
 int launch_prologue(const PrologueArgs& a, int waves, int qs, hipStream_t stream) {
+  // The scalar-scale cache convention is built for the small-batch shape and
+  // the default tiled shape only.
+  if (a.scalar) {
+    if (waves == 1 && qs == 1) return launch<1, 1, true>(a, stream);
+    return launch<4, 2, true>(a, stream);
+  }
 #define FP8KV_SHAPE(W, S)                                            \
-  if (waves == W && qs == S) return launch<W, S>(a, stream);
+  if (waves == W && qs == S) return launch<W, S, false>(a, stream);
   FP8KV_SHAPE(1, 1)
   FP8KV_SHAPE(1, 2)
   FP8KV_SHAPE(2, 1)

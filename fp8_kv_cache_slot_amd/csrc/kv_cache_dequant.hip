@@ -25,11 +25,13 @@ namespace {
 
 constexpr int kRopeLane0 = 56;
 
-template <int WAVES, int RS>
+// SCALAR: the scalar-scale convention, out = E4M3(code) * scalar_scale[0]
+// (rounded once to fp32, then to bf16) and no exponent bytes are read.
+template <int WAVES, int RS, bool SCALAR>
 __global__ void __launch_bounds__(WAVES * 64) kv_cache_gather_dequant_kernel(
     const uint8_t* __restrict__ kv_cache, const uint8_t* __restrict__ kv_scale,
-    const int64_t* __restrict__ slots, uint16_t* __restrict__ out,
-    int32_t num_rows, int64_t num_cache_slots) {
+    const float* __restrict__ scalar_scale, const int64_t* __restrict__ slots,
+    uint16_t* __restrict__ out, int32_t num_rows, int64_t num_cache_slots) {
   const int lane = lane_id();
   const int32_t first = (static_cast<int32_t>(blockIdx.x) * WAVES + wave_id()) * RS;
   if (first >= num_rows) return;
@@ -51,7 +53,8 @@ __global__ void __launch_bounds__(WAVES * 64) kv_cache_gather_dequant_kernel(
     rope[r] = u32x4_t{0u, 0u, 0u, 0u};
     if (ok[r]) {
       const uint8_t* row = kv_cache + slot[r] * 576;
-      sc[r] = *reinterpret_cast<const u32x2_t*>(kv_scale + slot[r] * 8);
+      if constexpr (!SCALAR)
+        sc[r] = *reinterpret_cast<const u32x2_t*>(kv_scale + slot[r] * 8);
       if (lane < kRopeLane0)
         codes[r] = *reinterpret_cast<const u32x2_t*>(row + lane * 8);
       else
@@ -67,6 +70,10 @@ __global__ void __launch_bounds__(WAVES * 64) kv_cache_gather_dequant_kernel(
     u32x4_t o = {0u, 0u, 0u, 0u};
     if (ok[r]) {
       if (lane < kRopeLane0) {
+        // a valid slot exists only when the cache has pages, and then the
+        // scalar scale pointer is a checked device pointer
+        float fs = 1.0f;
+        if constexpr (SCALAR) fs = *scalar_scale;
         const uint32_t word = b < 4 ? sc[r][0] : sc[r][1];
         const int e = static_cast<int>((word >> (8 * (b & 3))) & 0xFFu) - 127;
         const int lo = static_cast<int>(codes[r][0]);
@@ -78,8 +85,13 @@ __global__ void __launch_bounds__(WAVES * 64) kv_cache_gather_dequant_kernel(
         float v[8];
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-          v[2 * k] = __builtin_ldexpf(p[k][0], e);
-          v[2 * k + 1] = __builtin_ldexpf(p[k][1], e);
+          if constexpr (SCALAR) {
+            v[2 * k] = p[k][0] * fs;
+            v[2 * k + 1] = p[k][1] * fs;
+          } else {
+            v[2 * k] = __builtin_ldexpf(p[k][0], e);
+            v[2 * k + 1] = __builtin_ldexpf(p[k][1], e);
+          }
         }
         o = u32x4_t{pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3]),
                     pack_bf16(v[4], v[5]), pack_bf16(v[6], v[7])};
@@ -103,13 +115,18 @@ int launch_gather_dequant(const DequantArgs& a, hipStream_t stream) {
   if (blocks > 0x7FFFFFFF) return FP8KV_ERR_SHAPE;
   void* args[] = {const_cast<const uint8_t**>(&a.kv_cache),
                   const_cast<const uint8_t**>(&a.kv_scale),
+                  const_cast<const float**>(&a.scalar_scale),
                   const_cast<const int64_t**>(&a.slots),
                   const_cast<uint16_t**>(&a.out),
                   const_cast<int32_t*>(&a.num_rows),
                   const_cast<int64_t*>(&a.num_cache_slots)};
-  hipError_t err = hipLaunchKernel(
-      reinterpret_cast<const void*>(
-          &kv_cache_gather_dequant_kernel<kDequantWaves, kDequantRows>),
+  const void* fn =
+      a.scalar
+          ? reinterpret_cast<const void*>(
+                &kv_cache_gather_dequant_kernel<kDequantWaves, kDequantRows, true>)
+          : reinterpret_cast<const void*>(
+                &kv_cache_gather_dequant_kernel<kDequantWaves, kDequantRows, false>);
+  hipError_t err = hipLaunchKernel(fn,
       dim3(static_cast<uint32_t>(blocks)), dim3(kDequantWaves * 64), args, 0,
       stream);
   return err == hipSuccess ? FP8KV_OK : FP8KV_ERR_LAUNCH;

@@ -54,4 +54,28 @@ __device__ __forceinline__ void quantise_store_row(const float* y, int lane,
   }
 }
 
+// The scalar-scale convention (one kv_cache_scale float for the whole cache,
+// FlagGems PR #5449 "Performance"): codes of y / scale, saturated to the
+// E4M3 range; dims 448..511 as bf16; no exponent bytes.  No cross-lane work.
+__device__ __forceinline__ void quantise_store_row_scalar(const float* y, int lane,
+                                                          uint8_t* row,
+                                                          float scale) {
+  constexpr int kRopeLane0 = 56;
+  if (lane < kRopeLane0) {
+    float v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = fminf(fmaxf(y[j] / scale, -448.0f), 448.0f);
+    uint32_t lo = __builtin_amdgcn_cvt_pk_fp8_f32(v[0], v[1], 0, false);
+    lo = __builtin_amdgcn_cvt_pk_fp8_f32(v[2], v[3], lo, true);
+    uint32_t hi = __builtin_amdgcn_cvt_pk_fp8_f32(v[4], v[5], 0, false);
+    hi = __builtin_amdgcn_cvt_pk_fp8_f32(v[6], v[7], hi, true);
+    __builtin_nontemporal_store(u32x2_t{lo, hi},
+                                reinterpret_cast<u32x2_t*>(row + lane * 8));
+  } else {
+    u32x4_t o = {pack_bf16(y[0], y[1]), pack_bf16(y[2], y[3]),
+                 pack_bf16(y[4], y[5]), pack_bf16(y[6], y[7])};
+    store16<true>(row + 448 + (lane - kRopeLane0) * 16, o);
+  }
+}
+
 }  // namespace fp8kv

@@ -18,7 +18,9 @@ struct PrologueArgs {
   const int64_t* positions;
   const int64_t* slot_mapping;
   uint8_t* kv_cache;
-  uint8_t* kv_scale;
+  uint8_t* kv_scale;           // blockwise exponents (unused when scalar)
+  const float* scalar_scale;   // one device float: the scalar-scale convention
+  bool scalar;                 // use scalar_scale instead of kv_scale
   int32_t num_tokens;
   int32_t num_heads;
   int64_t num_cache_slots;  // num_pages * 64
@@ -60,7 +62,9 @@ struct PackedExArgs {
 
 struct DequantArgs {
   const uint8_t* kv_cache;
-  const uint8_t* kv_scale;
+  const uint8_t* kv_scale;       // blockwise exponents (unused when scalar)
+  const float* scalar_scale;     // one device float: the scalar-scale convention
+  bool scalar;                   // use scalar_scale instead of kv_scale
   const int64_t* slots;
   uint16_t* out;
   int32_t num_rows;

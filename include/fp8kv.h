@@ -115,6 +115,27 @@ int qnorm_rope_kv_quant_insert(
     void* stream);
 
 /*
+ * The same prologue writing the scalar-scale FP8 cache convention that the
+ * pages set against the blockwise one (FlagGems PR #5449 "Performance": a
+ * single kv_cache_scale float for the whole cache, which cannot carry
+ * per-block exponents).  Arguments as qnorm_rope_kv_quant_insert, except:
+ *   kv_cache_scale  DEVICE pointer to one fp32 scale s > 0 (4-byte aligned),
+ *                   required when num_pages > 0.  The value is a precondition
+ *                   (not checked: a non-positive or non-finite s gives
+ *                   saturated or undefined codes, never a fault).
+ * q is processed exactly as by qnorm_rope_kv_quant_insert.  A written cache
+ * row holds E4M3(y_d / s) for d < 448 (nearest even, saturating at +-448) and
+ * dims 448..511 as bf16; there is no exponent tensor.
+ */
+int qnorm_rope_kv_quant_insert_scalar_scale(
+    void* q, const void* kv, const void* q_weight, const void* kv_weight,
+    const float* cos_sin_cache, const int64_t* positions,
+    const int64_t* slot_mapping, uint8_t* kv_cache, const float* kv_cache_scale,
+    int64_t num_tokens, int32_t num_heads, int32_t head_dim, int32_t rope_dim,
+    int64_t max_position, int64_t num_pages, int32_t page_size, float eps,
+    void* stream);
+
+/*
  * Packed-QKV FusedQkNormRope (InfiniOps PR #1019, "Summary").
  *
  *   qkv           bf16 [T, (Hq + Hk + Hv) * D], heads packed as
@@ -231,6 +252,18 @@ int rope_rows(void* x, const float* cos_sin_cache, const int64_t* positions,
 int kv_quant_insert(const void* kv, const int64_t* slot_mapping,
                     uint8_t* kv_cache, uint8_t* kv_scale, int64_t num_tokens,
                     int64_t num_pages, int32_t page_size, void* stream);
+
+/*
+ * Read side of the scalar-scale convention: as kv_cache_gather_dequant, with
+ * out[i, d] = bf16(E4M3(code[s, d]) * kv_cache_scale[0]) for d < 448 (the
+ * product rounded to fp32, then to bf16) and no exponent tensor.
+ * kv_cache_scale is a device pointer, required when num_pages > 0.
+ */
+int kv_cache_gather_dequant_scalar_scale(const uint8_t* kv_cache,
+                                         const float* kv_cache_scale,
+                                         int64_t num_pages, int32_t page_size,
+                                         const int64_t* slots, int64_t num_rows,
+                                         void* out, void* stream);
 
 /* Static text for a status code (never NULL). */
 const char* fp8kv_status_string(int status);

@@ -51,6 +51,9 @@ def _load():
     lib.oracle_qnorm_rope_kv_quant_insert.argtypes = [
         P, P, P, P, P, P, P, P, P, I64, I32, I64, D]
     lib.oracle_qnorm_rope_kv_quant_insert.restype = None
+    lib.oracle_qnorm_rope_kv_quant_insert_scalar.argtypes = [
+        P, P, P, P, P, P, P, P, ctypes.c_float, I64, I32, I64, D]
+    lib.oracle_qnorm_rope_kv_quant_insert_scalar.restype = None
     lib.oracle_kv_normalised.argtypes = [P, P, P, P, I64, D, P]
     lib.oracle_kv_normalised.restype = None
     lib.oracle_rms_norm_rows.argtypes = [P, P, P, I64, D]
@@ -60,6 +63,9 @@ def _load():
     lib.oracle_kv_quant_insert.argtypes = [P, P, P, P, I64, I64]
     lib.oracle_kv_quant_insert.restype = None
     lib.oracle_kv_cache_gather_dequant.argtypes = [P, P, P, I64, I64, P]
+    lib.oracle_kv_cache_gather_dequant_scalar.argtypes = [
+        P, ctypes.c_float, P, I64, I64, P]
+    lib.oracle_kv_cache_gather_dequant_scalar.restype = None
     lib.oracle_kv_cache_gather_dequant.restype = None
     lib.oracle_qk_norm_rope_packed.argtypes = [
         P, I64, I32, I32, I32, I32, D, P, P, P, P]
@@ -138,6 +144,31 @@ def qnorm_rope_kv_quant_insert(q, kv, q_weight, kv_weight, cos_sin_cache,
         T, H, pages, float(eps))
 
 
+def qnorm_rope_kv_quant_insert_scalar(q, kv, q_weight, kv_weight,
+                                      cos_sin_cache, positions, slot_mapping,
+                                      kv_cache, kv_cache_scale, eps):
+    """Scalar-scale cache convention: in place on ``q`` and ``kv_cache``
+    (uint8 [pages,64,576]); no exponent tensor."""
+    T, H, D = q.shape
+    if D != 512 or kv.shape != (T, 512):
+        raise ValueError("q must be [T,H,512] and kv [T,512]")
+    if positions.shape != (T,) or slot_mapping.shape != (T,):
+        raise ValueError("positions and slot_mapping must be [T]")
+    pages = kv_cache.shape[0]
+    if kv_cache.shape != (pages, 64, 576):
+        raise ValueError("cache must be [pages,64,576]")
+    if not (kv_cache_scale > 0 and np.isfinite(kv_cache_scale)):
+        raise ValueError("kv_cache_scale must be positive and finite")
+    if T and (positions.min() < 0 or positions.max() >= cos_sin_cache.shape[0]):
+        raise ValueError("position out of range")
+    _load().oracle_qnorm_rope_kv_quant_insert_scalar(
+        _ptr(q, np.uint16, True), _ptr(kv, np.uint16), _ptr(q_weight, np.uint16),
+        _ptr(kv_weight, np.uint16), _ptr(cos_sin_cache, np.float32),
+        _ptr(positions, np.int64), _ptr(slot_mapping, np.int64),
+        _ptr(kv_cache, np.uint8, True), float(kv_cache_scale), T, H, pages,
+        float(eps))
+
+
 def kv_normalised(kv, kv_weight, cos_sin_cache, positions, eps):
     """Unrounded normalised + rotated KV rows, float64 [T, 512]."""
     T = kv.shape[0]
@@ -198,6 +229,19 @@ def kv_cache_gather_dequant(kv_cache, kv_scale, slots):
     out = np.empty((slots.shape[0], 512), np.uint16)
     _load().oracle_kv_cache_gather_dequant(
         _ptr(kv_cache, np.uint8), _ptr(kv_scale, np.uint8), _ptr(slots, np.int64),
+        slots.shape[0], pages, _ptr(out, np.uint16, True))
+    return out
+
+
+def kv_cache_gather_dequant_scalar(kv_cache, kv_cache_scale, slots):
+    """Scalar-scale read side: bf16 bit patterns [N, 512]."""
+    pages = kv_cache.shape[0]
+    if kv_cache.shape != (pages, 64, 576):
+        raise ValueError("cache must be [pages,64,576]")
+    slots = np.ascontiguousarray(slots, np.int64)
+    out = np.empty((slots.shape[0], 512), np.uint16)
+    _load().oracle_kv_cache_gather_dequant_scalar(
+        _ptr(kv_cache, np.uint8), float(kv_cache_scale), _ptr(slots, np.int64),
         slots.shape[0], pages, _ptr(out, np.uint16, True))
     return out
 

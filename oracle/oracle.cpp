@@ -271,6 +271,41 @@ void oracle_qnorm_rope_kv_quant_insert(
   }
 }
 
+void oracle_qnorm_rope_kv_quant_insert_scalar(
+    uint16_t* q, const uint16_t* kv, const uint16_t* q_weight,
+    const uint16_t* kv_weight, const float* cos_sin_cache,
+    const int64_t* positions, const int64_t* slot_mapping, uint8_t* kv_cache,
+    float kv_cache_scale, int64_t num_tokens, int32_t num_heads,
+    int64_t num_pages, double eps) {
+  const int64_t num_slots = num_pages * kPageSize;
+  double y[kHeadDim];
+  for (int64_t t = 0; t < num_tokens; ++t) {
+    const float* row = cos_sin_cache + positions[t] * kRopeDim;
+    const float* cosv = row;
+    const float* sinv = row + kRopeDim / 2;
+    for (int32_t h = 0; h < num_heads; ++h) {
+      uint16_t* qh = q + (t * num_heads + h) * kHeadDim;
+      rms_norm(qh, q_weight, kHeadDim, eps, y);
+      for (int i = 0; i < kRopeDim / 2; ++i)
+        rotate_pair(&y[kRopeStart + 2 * i], &y[kRopeStart + 2 * i + 1],
+                    cosv[i], sinv[i]);
+      for (int d = 0; d < kHeadDim; ++d) qh[d] = oracle_bf16_rne(y[d]);
+    }
+    const int64_t slot = slot_mapping[t];
+    if (slot < 0 || slot >= num_slots) continue;
+    kv_head(kv + t * kHeadDim, kv_weight, cosv, sinv, eps, y);
+    uint8_t* dst = kv_cache + slot * kRowBytes;
+    // one scale for everything: codes of y / s, saturating at the E4M3 range
+    for (int d = 0; d < kRopeStart; ++d)
+      dst[d] = oracle_e4m3_encode(y[d] / static_cast<double>(kv_cache_scale));
+    for (int j = 0; j < kRopeDim; ++j) {
+      uint16_t bits = oracle_bf16_rne(y[kRopeStart + j]);
+      dst[kRopeStart + 2 * j] = static_cast<uint8_t>(bits & 0xFF);
+      dst[kRopeStart + 2 * j + 1] = static_cast<uint8_t>(bits >> 8);
+    }
+  }
+}
+
 void oracle_kv_normalised(const uint16_t* kv, const uint16_t* kv_weight,
                           const float* cos_sin_cache, const int64_t* positions,
                           int64_t num_tokens, double eps, double* y_out) {
@@ -278,6 +313,29 @@ void oracle_kv_normalised(const uint16_t* kv, const uint16_t* kv_weight,
     const float* row = cos_sin_cache + positions[t] * kRopeDim;
     kv_head(kv + t * kHeadDim, kv_weight, row, row + kRopeDim / 2, eps,
             y_out + t * kHeadDim);
+  }
+}
+
+void oracle_kv_cache_gather_dequant_scalar(const uint8_t* kv_cache,
+                                           float kv_cache_scale,
+                                           const int64_t* slots,
+                                           int64_t num_rows, int64_t num_pages,
+                                           uint16_t* out) {
+  const int64_t num_slots = num_pages * kPageSize;
+  for (int64_t i = 0; i < num_rows; ++i) {
+    uint16_t* dst = out + i * kHeadDim;
+    const int64_t slot = slots[i];
+    if (slot < 0 || slot >= num_slots) {
+      for (int d = 0; d < kHeadDim; ++d) dst[d] = 0;
+      continue;
+    }
+    const uint8_t* row = kv_cache + slot * kRowBytes;
+    for (int d = 0; d < kRopeStart; ++d)
+      dst[d] = oracle_bf16_rne(oracle_e4m3_decode(row[d]) *
+                               static_cast<double>(kv_cache_scale));
+    for (int j = 0; j < kRopeDim; ++j)
+      dst[kRopeStart + j] = static_cast<uint16_t>(
+          row[kRopeStart + 2 * j] | (row[kRopeStart + 2 * j + 1] << 8));
   }
 }
 

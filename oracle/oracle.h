@@ -89,6 +89,22 @@ void oracle_qnorm_rope_kv_quant_insert(
     uint8_t* kv_scale, int64_t num_tokens, int32_t num_heads,
     int64_t num_pages, double eps);
 
+/*
+ * The same prologue with the scalar-scale FP8 cache convention the pages set
+ * against the blockwise one ([P1] "Performance": a single kv_cache_scale
+ * float for the whole cache, which cannot carry per-block exponents).  q is
+ * processed exactly as above; the KV row's dims 0..447 become
+ * E4M3(y_d / kv_cache_scale) (nearest even, saturating at +-448) and dims
+ * 448..511 are stored as bf16 as before; no exponent bytes exist.
+ * kv_cache_scale must be positive and finite.
+ */
+void oracle_qnorm_rope_kv_quant_insert_scalar(
+    uint16_t* q, const uint16_t* kv, const uint16_t* q_weight,
+    const uint16_t* kv_weight, const float* cos_sin_cache,
+    const int64_t* positions, const int64_t* slot_mapping, uint8_t* kv_cache,
+    float kv_cache_scale, int64_t num_tokens, int32_t num_heads,
+    int64_t num_pages, double eps);
+
 /* The KV head of each token after RMSNorm and rotation, before any rounding
  * (double [T, 512]): the values entry 1 quantises.  Exposed so that tests can
  * tell how close a block maximum sits to a power-of-two exponent boundary. */
@@ -138,6 +154,15 @@ void oracle_kv_cache_gather_dequant(const uint8_t* kv_cache,
                                     const uint8_t* kv_scale,
                                     const int64_t* slots, int64_t num_rows,
                                     int64_t num_pages, uint16_t* out);
+
+/* Read side of the scalar-scale convention: out[i, d] =
+ * bf16(E4M3(code[s, d]) * kv_cache_scale) for d < 448, rotary part copied,
+ * invalid slots give +0 rows.  The product is rounded once from double. */
+void oracle_kv_cache_gather_dequant_scalar(const uint8_t* kv_cache,
+                                           float kv_cache_scale,
+                                           const int64_t* slots,
+                                           int64_t num_rows, int64_t num_pages,
+                                           uint16_t* out);
 
 /* ---- entry 2: packed-QKV FusedQkNormRope ([P3] "Summary") ---------------- */
 /*

@@ -136,6 +136,16 @@ def check_cache(got_cache, got_scale, ref_cache, ref_scale, slots, y_ref,
     return stats
 
 
+def check_codes(got, ref, what=""):
+    """E4M3 codes without exponents (the scalar-scale convention): at most one
+    step apart on the signed line and at most MAX_MISMATCH differing."""
+    d = np.abs(_signed_code(got) - _signed_code(ref))
+    assert d.max(initial=0) <= 1, f"{what}: codes more than one step apart"
+    frac = float(np.mean(d != 0)) if d.size else 0.0
+    assert frac <= MAX_MISMATCH, f"{what}: {frac:.2e} of codes differ"
+    return frac
+
+
 def check_untouched(got_cache, got_scale, written_slots, canary_cache,
                     canary_scale, what=""):
     gc = got_cache.reshape(-1, 576)

@@ -96,6 +96,34 @@ def test_packed_argument_errors(over, want):
     assert _packed(**over) == want
 
 
+def _prologue_scalar(**over):
+    a = dict(q=FAKE, kv=FAKE, qw=FAKE, kw=FAKE, cs=FAKE, pos=FAKE, sm=FAKE,
+             cache=FAKE, scale=FAKE, T=4, H=8, D=512, R=64, maxp=16, pages=1,
+             page=64, eps=1e-6, stream=None)
+    a.update(over)
+    return K.lib().qnorm_rope_kv_quant_insert_scalar_scale(*a.values())
+
+
+def _dequant_scalar(**over):
+    a = dict(cache=FAKE, scale=FAKE, pages=2, page=64, slots=FAKE, rows=10,
+             out=FAKE, stream=None)
+    a.update(over)
+    return K.lib().kv_cache_gather_dequant_scalar_scale(*a.values())
+
+
+@pytest.mark.parametrize("fn,over,want", [
+    (_prologue_scalar, dict(T=-1), 2), (_prologue_scalar, dict(D=256), 3),
+    (_prologue_scalar, dict(scale=None), 1), (_prologue_scalar, dict(cache=None), 1),
+    (_prologue_scalar, dict(scale=FAKE + 2), 4), (_prologue_scalar, dict(q=FAKE + 8), 4),
+    (_prologue_scalar, dict(T=0, q=None), 0),
+    (_dequant_scalar, dict(rows=-1), 2), (_dequant_scalar, dict(page=16), 3),
+    (_dequant_scalar, dict(scale=None), 1), (_dequant_scalar, dict(scale=FAKE + 2), 4),
+    (_dequant_scalar, dict(rows=0, slots=None), 0),
+])
+def test_scalar_scale_argument_errors(fn, over, want):
+    assert fn(**over) == want
+
+
 def _packed_ex(**over):
     a = dict(qkv=FAKE, T=4, hq=16, hk=8, hv=8, D=128, eps=1e-6, qw=FAKE, kw=FAKE,
              cs=FAKE, neox=1, pos=FAKE, R=64, dtype=0, maxp=16, stream=None)
@@ -181,6 +209,8 @@ def test_no_device_is_reported_not_launched():
     assert _dequant(pages=0, cache=None, scale=None) == 5
     assert _norm() == 5 and _rope() == 5 and _quant() == 5
     assert _packed_ex() == 5 and _packed_ex(R=0, cs=None) == 5
+    assert _prologue_scalar() == 5 and _dequant_scalar() == 5
+    assert _prologue_scalar(pages=0, cache=None, scale=None) == 5
 
 
 def test_knobs():
