@@ -29,6 +29,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import statistics
 import sys
 import time
@@ -51,12 +52,17 @@ KERNEL_SOURCES = ("dsv4_prologue.hip", "kv_quant.hpp", "wave_ops.hpp")
 
 
 def kernel_source_hash() -> str:
-    """Hash of the sources the fused prologue kernel is compiled from."""
+    """Hash of the code (comments and whitespace removed) of the sources the
+    fused prologue kernel is compiled from."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "fp8_kv_cache_slot_amd", "csrc")
     for name in KERNEL_SOURCES:
-        with open(os.path.join(csrc, name), "rb") as f:
-            h.update(name.encode() + b"\0" + f.read())
+        with open(os.path.join(csrc, name)) as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        text = " ".join(text.split())
+        h.update(name.encode() + b"\0" + text.encode())
     return h.hexdigest()[:16]
 
 

@@ -2,8 +2,8 @@
 // a 64-lane wave (lane l holds dims 8l..8l+7) and write its paged-cache row:
 // seven UE8M0 power-of-two block exponents over dims 0..447 (block b = lanes
 // 8b..8b+7), FP8 E4M3 codes of y * 2^-e, and dims 448..511 as bf16 (the cache
-// layout of FlagGems PR #5449 "Performance": seven per-block exponents per
-// token).  Shared by the fused prologue and the stand-alone quantise+insert.
+// layout of FlagGems PR #5449 "Performance": an exponent for each of a
+// token's seven blocks).  Shared by the fused prologue and the stand-alone quantise+insert.
 #pragma once
 
 #include <hip/hip_runtime.h>

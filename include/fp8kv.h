@@ -89,9 +89,9 @@ enum fp8kv_status {
  *                  slot = e_b + 127, where 2^e_b is the UE8M0 scale of the
  *                  64-dim block b (dims 64b..64b+63) and e_b is the smallest
  *                  integer with amax_b <= 448 * 2^e_b, clamped to [-127, 127]
- *                  (amax 0 gives -127).  Byte 7 is never written.  "Seven
- *                  per-block exponents per token": FlagGems PR #5449,
- *                  "Performance".
+ *                  (amax 0 gives -127).  Byte 7 is never written.  One
+ *                  exponent for each of a token's seven blocks: FlagGems
+ *                  PR #5449, "Performance".
  *   eps            added to the mean square inside the square root.
  *
  * Per token t, for each Q head and then for the KV head x (with its weight w):
@@ -117,8 +117,8 @@ int qnorm_rope_kv_quant_insert(
 /*
  * The same prologue writing the scalar-scale FP8 cache convention that the
  * pages set against the blockwise one (FlagGems PR #5449 "Performance": a
- * single kv_cache_scale float for the whole cache, which cannot carry
- * per-block exponents).  Arguments as qnorm_rope_kv_quant_insert, except:
+ * single kv_cache_scale float for the whole cache, with no room for a
+ * power-of-two exponent per block).  Arguments as qnorm_rope_kv_quant_insert, except:
  *   kv_cache_scale  DEVICE pointer to one fp32 scale s > 0 (4-byte aligned),
  *                   required when num_pages > 0.  The value is a precondition
  *                   (not checked: a non-positive or non-finite s gives
@@ -199,8 +199,8 @@ int qk_norm_rope_packed_ex(
 /*
  * Read side of the paged cache written by qnorm_rope_kv_quant_insert: gather
  * rows by slot and dequantise them to bf16 (the inverse the cache layout of
- * FlagGems PR #5449 "Performance" implies: FP8 codes with seven per-block
- * power-of-two exponents per token).
+ * FlagGems PR #5449 "Performance" implies: FP8 codes plus one power-of-two
+ * exponent for each of a token's seven blocks).
  *
  *   kv_cache   uint8 [num_pages, page_size, 576], layout as above.  16-B aligned.
  *   kv_scale   uint8 [num_pages, page_size, 8].  8-byte aligned.

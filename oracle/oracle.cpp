@@ -20,7 +20,7 @@ namespace {
 // head) and [P2] "What the optimisation does" (64 threads for 512 elements).
 // Rotary width, block width and page size are readings: 64 rotary dims at the
 // end of the head, seven 64-dim quantisation blocks over the first 448 dims
-// ([P1] "Performance": seven per-block exponents per token), 64-slot pages.
+// ([P1] "Performance": one exponent per block, seven per token), 64-slot pages.
 constexpr int kHeadDim = 512;
 constexpr int kRopeDim = 64;
 constexpr int kRopeStart = kHeadDim - kRopeDim;  // 448
@@ -83,9 +83,9 @@ void kv_head(const uint16_t* x, const uint16_t* w, const float* cosv,
 
 // Quantise one normalised, rotated KV head y and write its cache row and
 // exponent bytes.  Seven UE8M0 power-of-two block scales per token ([P1]
-// "Performance": the scalar-scale convention "cannot carry seven per-block
-// exponents per token"), each the smallest power of two that brings the
-// block's largest magnitude within the E4M3 range; the rotary dims are kept
+// "Performance": a single scalar scale could not hold one exponent per
+// block), each the smallest power of two that brings the block's largest
+// magnitude within the E4M3 range; the rotary dims are kept
 // as bf16 after the codes (reading).
 void quantise_insert(const double* y, uint8_t* dst, uint8_t* scale) {
   for (int b = 0; b < kNumBlocks; ++b) {

@@ -56,7 +56,7 @@ double oracle_e4m3_decode(uint8_t code);
 
 /* OCP E4M3 code nearest to v, ties to even, saturating at +-448, sign kept
  * (a negative value that rounds to zero gives 0x80).  This is the cache's
- * "fp8e4nv" format named in [P2] "The four test and benchmark fixes". */
+ * Triton fp8e4nv format that [P2] "The four test and benchmark fixes" names. */
 uint8_t oracle_e4m3_encode(double v);
 
 /* UE8M0 block exponent: the smallest integer e with amax <= 448 * 2^e, i.e.
@@ -92,7 +92,7 @@ void oracle_qnorm_rope_kv_quant_insert(
 /*
  * The same prologue with the scalar-scale FP8 cache convention the pages set
  * against the blockwise one ([P1] "Performance": a single kv_cache_scale
- * float for the whole cache, which cannot carry per-block exponents).  q is
+ * float for the whole cache, with no room for an exponent per block).  q is
  * processed exactly as above; the KV row's dims 0..447 become
  * E4M3(y_d / kv_cache_scale) (nearest even, saturating at +-448) and dims
  * 448..511 are stored as bf16 as before; no exponent bytes exist.
@@ -148,7 +148,8 @@ void oracle_kv_quant_insert(const uint16_t* kv, const int64_t* slot_mapping,
  * +0.  out is bf16 [N, 512] (uint16 patterns), rounded to nearest even from
  * the exact double product (exact in practice: an E4M3 value has 4 significant
  * bits).  This is the inverse the fused prologue's cache layout implies
- * ([P1] "Performance": seven per-block power-of-two exponents per token).
+ * ([P1] "Performance": a power-of-two exponent for each of a token's seven
+ * blocks).
  */
 void oracle_kv_cache_gather_dequant(const uint8_t* kv_cache,
                                     const uint8_t* kv_scale,
