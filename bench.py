@@ -9,16 +9,22 @@ generated on the GPU and resident in HBM before timing starts.
 Prints ONE JSON line:
   value        whole-job HBM throughput in GB/s (algorithmic bytes / time)
   pct_of_d2d   value as a fraction of a measured 512 MiB device-to-device copy
-               (hipMemcpyAsync, read + write bytes counted)
+               (hipMemcpyAsync, read + write bytes counted); beside it the
+               library's hand-written 16 B/lane copy of the same 512 MiB and
+               its in-place 16 B/lane read-modify-write over 2 GiB
   roofline     dominant kernel: algorithmic bytes per launch / mean launch
                duration (HIP events on the launch stream) against 8 TB/s
   cpu_baseline the CPU oracle timed on a bounded token slice of the same
-               workload, single-threaded
+               workload, single-threaded (cpu_baseline_all_cores: the same
+               oracle over disjoint token slices on every core of the share)
   extra        the other workloads (131072 x 64, 32768 x 128, decode and tiny
                latencies, the packed Q/K norm+RoPE at 8192 tokens, the cache
                read side over all 131072 slots of the 131072 x 64 cache, and
                the same prologue as five separate launches, the unfused
-               baseline, with the fusion speedup)
+               baseline, with the fusion speedup).  Each of these launches is
+               timed alone after a 1 GiB cache-flushing write (median and
+               minimum), so no working set starts in the 256 MB Infinity
+               Cache; prefill_flushed is the headline kernel timed that way.
 
 Usage: python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--quick]
 """
@@ -26,6 +32,7 @@ Usage: python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--quick]
 from __future__ import annotations
 
 import argparse
+import concurrent.futures as cf
 import hashlib
 import json
 import os
@@ -42,6 +49,17 @@ METRIC = ("achieved HBM GB/s & % of measured D2D-copy peak at tokens×heads "
 HBM_PEAK_GBPS = 8000.0
 PROFILE_COUNTERS = os.path.join(ROOT, "profiles",
                                 "dsv4_prologue_prefill_32768x64_counters.json")
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def log(msg):
@@ -126,8 +144,48 @@ def main():
         e1.synchronize()
         times.append(e0.elapsed_time(e1) / 1e3)
     d2d_gbps = 2 * n / statistics.median(times) / 1e9
-    del src, dst
     log(f"D2D copy ceiling {d2d_gbps:.1f} GB/s")
+
+    def median_launch(fn, iters=20, warmup=3):
+        for _ in range(warmup):
+            fn()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(iters)]
+        for a, b in ev:
+            a.record(stream)
+            fn()
+            b.record(stream)
+        torch.cuda.synchronize()
+        return statistics.median(a.elapsed_time(b) / 1e3 for a, b in ev)
+
+    # the same 512 MiB through the library's hand-written 16 B/lane copy, and
+    # an in-place 16 B/lane read-modify-write over 2 GiB (the size and access
+    # pattern of the prefill Q heads, without the arithmetic)
+    copy_gbps = 2 * n / median_launch(lambda: K.stream_copy(dst, src)) / 1e9
+    del src, dst
+    rbuf = torch.zeros(2 ** 31, dtype=torch.uint8, device=dev)
+    rmw_gbps = 2 * rbuf.numel() / median_launch(lambda: K.stream_rmw(rbuf, 0)) / 1e9
+    del rbuf
+    log(f"16 B/lane copy kernel {copy_gbps:.1f} GB/s, in-place RMW {rmw_gbps:.1f} GB/s")
+
+    # 1 GiB written between timed launches: more than the 256 MB Infinity
+    # Cache plus the L2s, so every timed launch starts from cold caches
+    flush_buf = torch.empty(2 ** 30, dtype=torch.uint8, device=dev)
+
+    def time_flushed(fn, iters=20, warmup=3):
+        """Per-launch seconds of `iters` launches, each preceded (outside its
+        events) by a 1 GiB cache-flushing write."""
+        for _ in range(warmup):
+            fn()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(iters)]
+        for i, (a, b) in enumerate(ev):
+            flush_buf.fill_(i & 0xFF)
+            a.record(stream)
+            fn()
+            b.record(stream)
+        torch.cuda.synchronize()
+        return [a.elapsed_time(b) / 1e3 for a, b in ev]
 
     def call(x, q, cache, scale):
         K.qnorm_rope_kv_quant_insert(q, x["kv"], x["q_weight"], x["kv_weight"],
@@ -197,6 +255,9 @@ def main():
         },
         "pct_of_d2d": round(value / d2d_gbps, 4),
         "d2d_copy_gbps": round(d2d_gbps, 1),
+        "copy_kernel_gbps": round(copy_gbps, 1),
+        "rmw_kernel_gbps": round(rmw_gbps, 1),
+        "pct_of_rmw_kernel": round(value / rmw_gbps, 4),
         "roofline": {
             "bound": "hbm",
             "achieved": round(achieved, 1),
@@ -216,22 +277,29 @@ def main():
         K.unfused_prologue(q, x["kv"], x["q_weight"], x["kv_weight"],
                            x["cos_sin_cache"], x["positions"], x["slot_mapping"],
                            cache, scale, x["eps"], kv_work=kv_work)
-    _, uper = time_launches(unfused, 20, 3)
+    fper = time_flushed(lambda: call(x, q, cache, scale))
+    prefill_flushed = {"median_us": round(statistics.median(fper) * 1e6, 1),
+                       "min_us": round(min(fper) * 1e6, 1),
+                       "gbps": round(nbytes / statistics.median(fper) / 1e9, 1)}
+    log(f"prefill, caches flushed: {prefill_flushed}")
+    uper = time_flushed(unfused)
     unfused_prefill = {"median_us": round(statistics.median(uper) * 1e6, 1),
-                       "fused_median_us": round(statistics.median(per) * 1e6, 1),
+                       "min_us": round(min(uper) * 1e6, 1),
+                       "fused_median_us": round(statistics.median(fper) * 1e6, 1),
                        "fusion_speedup": round(statistics.median(uper) /
-                                               statistics.median(per), 3)}
+                                               statistics.median(fper), 3)}
     log(f"unfused prefill: {unfused_prefill}")
 
     # ---- the scalar-scale cache convention on the same workload ----------
     sscale = torch.tensor([0.0173], dtype=torch.float32, device=dev)
-    _, sper = time_launches(lambda: K.qnorm_rope_kv_quant_insert_scalar_scale(
+    sper = time_flushed(lambda: K.qnorm_rope_kv_quant_insert_scalar_scale(
         q, x["kv"], x["q_weight"], x["kv_weight"], x["cos_sin_cache"],
-        x["positions"], x["slot_mapping"], cache, sscale, x["eps"]), 20, 3)
+        x["positions"], x["slot_mapping"], cache, sscale, x["eps"]))
     sm_all = x["slot_mapping"]
     written = int(((sm_all >= 0) & (sm_all < w.num_pages * 64)).sum().item())
     sb = A.dsv4_scalar_bytes(w.num_tokens, w.num_heads, written)
     scalar_prefill = {"median_us": round(statistics.median(sper) * 1e6, 1),
+                      "min_us": round(min(sper) * 1e6, 1),
                       "gbps": round(sb / statistics.median(sper) / 1e9, 1)}
     log(f"scalar-scale prefill: {scalar_prefill}")
     del q, cache, scale, kv_work
@@ -242,18 +310,32 @@ def main():
 
         import oracle as O
 
-        def oracle_on(tokens):
-            sl = slice(0, tokens)
-            h = dict(q=I.bits(x["q"][sl]).copy(), kv=I.bits(x["kv"][sl]).copy(),
-                     qw=I.bits(x["q_weight"]), kw=I.bits(x["kv_weight"]),
-                     cs=I.bits(x["cos_sin_cache"]),
-                     pos=I.bits(x["positions"][sl]).copy(),
-                     sm=I.bits(x["slot_mapping"][sl]).copy())
+        def oracle_on(tokens, threads=1):
+            """Seconds for the oracle over the first `tokens` prefill tokens,
+            split into `threads` disjoint token slices run concurrently (the
+            oracle's C entry releases the interpreter lock; the slot map is
+            injective, so the slices write disjoint cache rows)."""
+            qw, kw = I.bits(x["q_weight"]), I.bits(x["kv_weight"])
+            cs = I.bits(x["cos_sin_cache"])
             c = np.full((w.num_pages, 64, 576), I.CACHE_CANARY, np.uint8)
             s = np.full((w.num_pages, 64, 8), I.SCALE_CANARY, np.uint8)
+            cuts = [tokens * i // threads for i in range(threads + 1)]
+            parts = []
+            for a, b in zip(cuts[:-1], cuts[1:]):
+                sl = slice(a, b)
+                parts.append((I.bits(x["q"][sl]).copy(), I.bits(x["kv"][sl]).copy(),
+                              I.bits(x["positions"][sl]).copy(),
+                              I.bits(x["slot_mapping"][sl]).copy()))
+
+            def run(p):
+                O.qnorm_rope_kv_quant_insert(p[0], p[1], qw, kw, cs, p[2], p[3],
+                                             c, s, w.eps)
             t0 = time.perf_counter()
-            O.qnorm_rope_kv_quant_insert(h["q"], h["kv"], h["qw"], h["kw"], h["cs"],
-                                         h["pos"], h["sm"], c, s, w.eps)
+            if threads == 1:
+                run(parts[0])
+            else:
+                with cf.ThreadPoolExecutor(threads) as ex:
+                    list(ex.map(run, parts))
             return time.perf_counter() - t0
 
         probe = 256
@@ -271,8 +353,21 @@ def main():
                       f"+ KV), {dt:.1f} s single-threaded double-precision C++",
             "seconds": round(dt, 2),
             "host_cpus": os.cpu_count(),
+            "cpu_model": cpu_model(),
         }
         log(f"cpu oracle: {tokens} tokens in {dt:.1f} s")
+        # every core of this process's CPU share, over disjoint token slices
+        threads = max(1, min(16, len(os.sched_getaffinity(0))))
+        mt = int(min(w.num_tokens, tokens * threads)) // 64 * 64
+        mdt = oracle_on(mt, threads)
+        mbytes = A.dsv4_bytes(mt, w.num_heads, mt)
+        result["cpu_baseline_all_cores"] = {
+            "value": round(mbytes / mdt / 1e9, 4), "unit": "GB/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"first {mt} of the 32768 prefill tokens in {threads} "
+                      f"disjoint slices, one thread each, {mdt:.1f} s wall",
+            "seconds": round(mdt, 2)}
+        log(f"cpu oracle, {threads} threads: {mt} tokens in {mdt:.1f} s")
 
     del x
     torch.cuda.empty_cache()
@@ -285,10 +380,11 @@ def main():
             xx = I.make_dsv4(wl, dev)
             qq, cc, ss = xx["q"].clone(), xx["kv_cache"].clone(), xx["kv_scale"].clone()
             nb = workload_bytes(wl, xx)
-            tot, per = time_launches(lambda: call(xx, qq, cc, ss), 20, 3)
+            per = time_flushed(lambda: call(xx, qq, cc, ss))
             m = statistics.median(per)
             extra[name] = {"tokens": wl.num_tokens, "heads": wl.num_heads,
                            "bytes": nb, "median_us": round(m * 1e6, 1),
+                           "min_us": round(min(per) * 1e6, 1),
                            "gbps": round(nb / m / 1e9, 1),
                            "pct_of_d2d": round(nb / m / 1e9 / d2d_gbps, 4)}
             log(f"{name}: {extra[name]}")
@@ -300,17 +396,19 @@ def main():
                 slots = torch.randperm(wl.num_pages * 64, generator=g, device=dev)
                 out = torch.empty((slots.shape[0], 512), dtype=torch.bfloat16,
                                   device=dev)
-                tot, per = time_launches(
-                    lambda: K.kv_cache_gather_dequant(cc, ss, slots, out), 20, 3)
+                per = time_flushed(
+                    lambda: K.kv_cache_gather_dequant(cc, ss, slots, out))
                 m = statistics.median(per)
                 nb = A.dequant_bytes(slots.shape[0], slots.shape[0])
                 extra["dequant_long64"] = {
                     "rows": int(slots.shape[0]), "bytes": nb,
-                    "median_us": round(m * 1e6, 1), "gbps": round(nb / m / 1e9, 1)}
+                    "median_us": round(m * 1e6, 1), "min_us": round(min(per) * 1e6, 1),
+                    "gbps": round(nb / m / 1e9, 1)}
                 log(f"dequant_long64: {extra['dequant_long64']}")
                 del slots, out
             del xx, qq, cc, ss
             torch.cuda.empty_cache()
+        extra["prefill_flushed"] = prefill_flushed
         extra["unfused_prefill"] = unfused_prefill
         extra["scalar_scale_prefill"] = scalar_prefill
         for name in ("tiny", "decode"):
@@ -318,16 +416,17 @@ def main():
             xx = I.make_dsv4(wl, dev)
             qq, cc, ss = xx["q"].clone(), xx["kv_cache"].clone(), xx["kv_scale"].clone()
             nb = workload_bytes(wl, xx)
-            tot, per = time_launches(lambda: call(xx, qq, cc, ss), 50, 10)
+            per = time_flushed(lambda: call(xx, qq, cc, ss), 50, 10)
             m = statistics.median(per)
             kw = torch.empty((wl.num_tokens, 512), dtype=torch.bfloat16, device=dev)
-            _, uper = time_launches(lambda: K.unfused_prologue(
+            uper = time_flushed(lambda: K.unfused_prologue(
                 qq, xx["kv"], xx["q_weight"], xx["kv_weight"], xx["cos_sin_cache"],
                 xx["positions"], xx["slot_mapping"], cc, ss, xx["eps"], kv_work=kw),
                 50, 10)
             um = statistics.median(uper)
             extra[name] = {"tokens": wl.num_tokens, "heads": wl.num_heads,
                            "bytes": nb, "median_us": round(m * 1e6, 2),
+                           "min_us": round(min(per) * 1e6, 2),
                            "gbps": round(nb / m / 1e9, 1),
                            "unfused_median_us": round(um * 1e6, 2),
                            "fusion_speedup": round(um / m, 3)}
@@ -341,11 +440,12 @@ def main():
                                   pw.num_heads_v, pw.head_dim, pw.eps,
                                   px["q_weight"], px["k_weight"],
                                   px["cos_sin_cache"], True, px["position_ids"])
-        tot, per = time_launches(pcall, 50, 10)
+        per = time_flushed(pcall, 50, 10)
         m = statistics.median(per)
         nb = A.packed_bytes(pw.num_tokens, pw.num_heads_q, pw.num_heads_k, pw.head_dim)
         extra["packed_t8192"] = {"tokens": pw.num_tokens, "heads": "16q/8k/8v x 128",
                                  "bytes": nb, "median_us": round(m * 1e6, 2),
+                                 "min_us": round(min(per) * 1e6, 2),
                                  "gbps": round(nb / m / 1e9, 1)}
         log(f"packed_t8192: {extra['packed_t8192']}")
         # packed variants the guarded fast path does not cover
@@ -360,13 +460,15 @@ def main():
             vw = (torch.rand(D, generator=g, device=dev) + 0.5).to(dt)
             vcs = I.cos_sin_cache(8192, R, device=dev)
             vpos = torch.randint(0, 8192, (T,), generator=g, device=dev)
-            tot, per = time_launches(lambda: K.qk_norm_rope_packed_ex(
+            per = time_flushed(lambda: K.qk_norm_rope_packed_ex(
                 vq, hq, hk, hv, D, 1e-6, vw, vw, vcs, neox, vpos, rotary_dim=R), 50, 10)
             m = statistics.median(per)
             nb = A.packed_bytes(T, hq, hk, D, R)
             extra[label] = {"tokens": T, "heads": f"{hq}q/{hk}k/{hv}v x {D}",
                             "rotary_dim": R, "bytes": nb,
-                            "median_us": round(m * 1e6, 2), "gbps": round(nb / m / 1e9, 1)}
+                            "median_us": round(m * 1e6, 2),
+                            "min_us": round(min(per) * 1e6, 2),
+                            "gbps": round(nb / m / 1e9, 1)}
             log(f"{label}: {extra[label]}")
         result["extra"] = extra
 

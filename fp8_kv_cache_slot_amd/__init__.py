@@ -39,7 +39,8 @@ EXPORTED = ["qnorm_rope_kv_quant_insert", "qk_norm_rope_packed",
             "kv_quant_insert",
             "fp8kv_status_string", "fp8kv_abi_version",
             "fp8kv_set_dispatch_threshold", "fp8kv_get_dispatch_threshold",
-            "fp8kv_set_tiling", "fp8kv_get_tiling"]
+            "fp8kv_set_tiling", "fp8kv_get_tiling",
+            "fp8kv_stream_copy", "fp8kv_stream_rmw"]
 
 
 class Fp8kvError(RuntimeError):
@@ -97,6 +98,10 @@ def lib() -> ctypes.CDLL:
     L.fp8kv_set_tiling.restype = ctypes.c_int
     L.fp8kv_get_tiling.argtypes = [ctypes.POINTER(I32), ctypes.POINTER(I32)]
     L.fp8kv_get_tiling.restype = None
+    L.fp8kv_stream_copy.argtypes = [P, P, I64, P]
+    L.fp8kv_stream_copy.restype = ctypes.c_int
+    L.fp8kv_stream_rmw.argtypes = [P, I64, ctypes.c_uint32, P]
+    L.fp8kv_stream_rmw.restype = ctypes.c_int
     _lib = L
     return L
 
@@ -394,3 +399,30 @@ def get_tiling():
 
 def abi_version() -> int:
     return lib().fp8kv_abi_version()
+
+
+def stream_copy(dst, src, stream=None) -> None:
+    """Reference streaming copy (16 bytes per lane): dst[:] = src[:], both
+    contiguous device tensors of the same byte size (a multiple of 16)."""
+    for t, name in ((dst, "dst"), (src, "src")):
+        if not (isinstance(t, torch.Tensor) and t.device.type == "cuda"
+                and t.is_contiguous()):
+            raise ValueError(f"{name} must be a contiguous device tensor")
+    nb = dst.numel() * dst.element_size()
+    if src.numel() * src.element_size() != nb:
+        raise ValueError("dst and src must have the same byte size")
+    st = lib().fp8kv_stream_copy(dst.data_ptr(), src.data_ptr(), nb, _stream(stream))
+    if st:
+        raise Fp8kvError(st, "stream_copy")
+
+
+def stream_rmw(buf, mask: int = 0, stream=None) -> None:
+    """Reference in-place streaming read-modify-write (16 bytes per lane):
+    every 32-bit word of ``buf`` is XORed with ``mask`` (0 keeps the bytes)."""
+    if not (isinstance(buf, torch.Tensor) and buf.device.type == "cuda"
+            and buf.is_contiguous()):
+        raise ValueError("buf must be a contiguous device tensor")
+    st = lib().fp8kv_stream_rmw(buf.data_ptr(), buf.numel() * buf.element_size(),
+                                int(mask) & 0xFFFFFFFF, _stream(stream))
+    if st:
+        raise Fp8kvError(st, "stream_rmw")

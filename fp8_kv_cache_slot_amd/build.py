@@ -20,7 +20,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libfp8kv.so")
 SOURCES = ["capi.hip", "dsv4_prologue.hip", "qk_norm_rope_packed.hip",
-           "kv_cache_dequant.hip", "unfused.hip", "qk_norm_rope_packed_ex.hip"]
+           "kv_cache_dequant.hip", "unfused.hip", "qk_norm_rope_packed_ex.hip",
+           "stream_ref.hip"]
 ARCH = "gfx950"
 
 

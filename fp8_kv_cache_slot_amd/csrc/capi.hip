@@ -345,3 +345,27 @@ FP8KV_API void fp8kv_get_tiling(int32_t* waves_per_block, int32_t* slots_per_wav
   if (waves_per_block) *waves_per_block = t >> 16;
   if (slots_per_wave) *slots_per_wave = t & 0xFFFF;
 }
+
+FP8KV_API int fp8kv_stream_copy(void* dst, const void* src, int64_t bytes,
+                                void* stream) {
+  using namespace fp8kv;
+  if (bytes < 0 || bytes % 16 != 0) return FP8KV_ERR_SHAPE;
+  if (bytes == 0) return FP8KV_OK;
+  if (!dst || !src) return FP8KV_ERR_NULL;
+  if (!aligned(dst, 16) || !aligned(src, 16)) return FP8KV_ERR_ALIGN;
+  int st = check_device();
+  if (st != FP8KV_OK) return st;
+  return launch_stream_copy(dst, src, bytes / 16, static_cast<hipStream_t>(stream));
+}
+
+FP8KV_API int fp8kv_stream_rmw(void* buf, int64_t bytes, uint32_t mask,
+                               void* stream) {
+  using namespace fp8kv;
+  if (bytes < 0 || bytes % 16 != 0) return FP8KV_ERR_SHAPE;
+  if (bytes == 0) return FP8KV_OK;
+  if (!buf) return FP8KV_ERR_NULL;
+  if (!aligned(buf, 16)) return FP8KV_ERR_ALIGN;
+  int st = check_device();
+  if (st != FP8KV_OK) return st;
+  return launch_stream_rmw(buf, bytes / 16, mask, static_cast<hipStream_t>(stream));
+}

@@ -90,4 +90,8 @@ int launch_kv_quant_insert(const uint16_t* kv, const int64_t* slot_mapping,
                            uint8_t* kv_cache, uint8_t* kv_scale, int32_t num_tokens,
                            int64_t num_cache_slots, hipStream_t stream);
 
+// Reference streaming kernels (16-byte vectors; n16 = number of vectors).
+int launch_stream_copy(void* dst, const void* src, int64_t n16, hipStream_t stream);
+int launch_stream_rmw(void* buf, int64_t n16, uint32_t mask, hipStream_t stream);
+
 }  // namespace fp8kv

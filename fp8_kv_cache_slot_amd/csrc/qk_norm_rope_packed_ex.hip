@@ -11,7 +11,8 @@
 //
 // Layout of the work.  One wave per token; a head is D/8 lanes of one 16-byte
 // vector each, so a wave covers 512/D heads per access and loops over the
-// token's Q and K heads with four accesses' loads issued ahead.  The sum of
+// token's Q and K heads with four accesses' loads issued ahead (the first
+// four before the token's position is read).  The sum of
 // squares is reduced over the head's lanes (DPP row steps, plus one lane
 // shuffle across rows for D = 256).  Interleaved pairs sit inside a lane;
 // a NeoX partner sits R/16 lanes away within the head and arrives through
@@ -80,11 +81,27 @@ __global__ void __launch_bounds__(256) qk_norm_rope_packed_ex_kernel(
   const int lane = lane_id();
   const int32_t t = static_cast<int32_t>(blockIdx.x) * 4 + wave_id();
   if (t >= num_tokens) return;
-  const int64_t pos = position_ids[t];
-  if (pos < 0 || pos >= max_position) return;
   const int g = lane / LPH;    // head slot within an access
   const int lh = lane % LPH;   // lane within the head: dims 8lh .. 8lh+7
   const int32_t nh = num_heads_q + num_heads_k;
+  uint16_t* base = qkv + static_cast<int64_t>(t) * row_elems + lh * 8;
+
+  // The first batch of head loads goes out before the position load, so the
+  // position and cos/sin loads overlap it.  A position out of range makes the
+  // token's stores, not an early return, conditional, so that no branch on
+  // the position sits in front of the loads; its cos/sin reads use row 0.
+  u32x4_t x[U];
+  auto load_batch = [&](int32_t h0) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int32_t h = h0 + u * HPW + g;
+      x[u] = load16<true>(base + static_cast<int64_t>(h < nh ? h : 0) * D);
+    }
+  };
+  load_batch(0);
+  const int64_t pos_in = position_ids[t];
+  const bool valid = pos_in >= 0 && pos_in < max_position;
+  const int64_t pos = valid ? pos_in : 0;
 
   float wq[8], wk[8];
 #pragma unroll
@@ -134,14 +151,8 @@ __global__ void __launch_bounds__(256) qk_norm_rope_packed_ex_kernel(
   }
   const int partner_addr = partner * 4;  // ds_bpermute byte address
 
-  uint16_t* base = qkv + static_cast<int64_t>(t) * row_elems + lh * 8;
   for (int32_t h0 = 0; h0 < nh; h0 += U * HPW) {
-    u32x4_t x[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int32_t h = h0 + u * HPW + g;
-      x[u] = load16<true>(base + static_cast<int64_t>(h < nh ? h : 0) * D);
-    }
+    if (h0 > 0) load_batch(h0);
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int32_t h = h0 + u * HPW + g;
@@ -168,7 +179,7 @@ __global__ void __launch_bounds__(256) qk_norm_rope_packed_ex_kernel(
           o[2 * k + 1] = n[2 * k + 1] * c[2 * k + 1] + n[2 * k] * s[2 * k + 1];
         }
       }
-      if (h < nh) {
+      if (valid && h < nh) {
         u32x4_t v = {pack2_any<FP16>(o[0], o[1]), pack2_any<FP16>(o[2], o[3]),
                      pack2_any<FP16>(o[4], o[5]), pack2_any<FP16>(o[6], o[7])};
         store16<true>(base + static_cast<int64_t>(h) * D, v);

@@ -1,0 +1,65 @@
+// Reference streaming kernels for the bandwidth ceiling the prologue is
+// measured against.  Both move 16 bytes per lane, one vector per lane, in
+// 256-lane blocks, with the same non-temporal load/store policy as the
+// prologue's q stream:
+//   stream_copy  dst[i] = src[i]                       (read n + write n bytes)
+//   stream_rmw   buf[i] = buf[i] ^ mask, in place      (read n + write n bytes)
+// The in-place form is the access pattern of the prologue's Q heads, which
+// are read and written back at the same address, without the arithmetic.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "prologue_launch.hpp"
+#include "wave_ops.hpp"
+
+namespace fp8kv {
+namespace {
+
+constexpr int kThreads = 256;
+
+__global__ void __launch_bounds__(kThreads) stream_copy_kernel(
+    u32x4_t* __restrict__ dst, const u32x4_t* __restrict__ src, int64_t n16) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
+  if (i < n16) store16<true>(dst + i, load16<true>(src + i));
+}
+
+__global__ void __launch_bounds__(kThreads) stream_rmw_kernel(
+    u32x4_t* __restrict__ buf, int64_t n16, uint32_t mask) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
+  if (i < n16) store16<true>(buf + i, load16<true>(buf + i) ^ mask);
+}
+
+int grid_for(int64_t n16, uint32_t* blocks) {
+  const int64_t b = (n16 + kThreads - 1) / kThreads;
+  if (b > 0x7FFFFFFF) return FP8KV_ERR_SHAPE;
+  *blocks = static_cast<uint32_t>(b);
+  return FP8KV_OK;
+}
+
+}  // namespace
+
+int launch_stream_copy(void* dst, const void* src, int64_t n16, hipStream_t stream) {
+  uint32_t blocks = 0;
+  if (int st = grid_for(n16, &blocks)) return st;
+  u32x4_t* d = static_cast<u32x4_t*>(dst);
+  const u32x4_t* s = static_cast<const u32x4_t*>(src);
+  void* args[] = {&d, &s, &n16};
+  return hipLaunchKernel(reinterpret_cast<const void*>(&stream_copy_kernel),
+                         dim3(blocks), dim3(kThreads), args, 0, stream) == hipSuccess
+             ? FP8KV_OK
+             : FP8KV_ERR_LAUNCH;
+}
+
+int launch_stream_rmw(void* buf, int64_t n16, uint32_t mask, hipStream_t stream) {
+  uint32_t blocks = 0;
+  if (int st = grid_for(n16, &blocks)) return st;
+  u32x4_t* b = static_cast<u32x4_t*>(buf);
+  void* args[] = {&b, &n16, &mask};
+  return hipLaunchKernel(reinterpret_cast<const void*>(&stream_rmw_kernel),
+                         dim3(blocks), dim3(kThreads), args, 0, stream) == hipSuccess
+             ? FP8KV_OK
+             : FP8KV_ERR_LAUNCH;
+}
+
+}  // namespace fp8kv

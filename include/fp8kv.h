@@ -293,6 +293,26 @@ int64_t fp8kv_get_dispatch_threshold(void);
 int fp8kv_set_tiling(int32_t waves_per_block, int32_t slots_per_wave);
 void fp8kv_get_tiling(int32_t* waves_per_block, int32_t* slots_per_wave);
 
+/*
+ * Measurement aids: the hand-written streaming kernels the prologue's HBM
+ * bandwidth is compared with (a bandwidth-bound operator is judged against
+ * the rate of a plain copy on the same device; FlagGems PR #5449
+ * "Performance" reports its kernel as a share of a measured copy peak).
+ * Both move one 16-byte vector per lane, 256 lanes per block, with
+ * non-temporal loads and stores; neither is part of the prologue.
+ *
+ *   fp8kv_stream_copy  dst[0:bytes) = src[0:bytes)
+ *   fp8kv_stream_rmw   buf[i] ^= mask for every 32-bit word i, in place
+ *                      (mask 0 leaves the bytes unchanged; the pattern of
+ *                      the prologue's in-place Q heads)
+ *
+ * bytes: a multiple of 16, >= 0 (FP8KV_ERR_SHAPE otherwise); 0 launches
+ * nothing.  Pointers: device, 16-byte aligned (FP8KV_ERR_ALIGN), non-NULL
+ * when bytes > 0 (FP8KV_ERR_NULL).  dst and src must not overlap.
+ */
+int fp8kv_stream_copy(void* dst, const void* src, int64_t bytes, void* stream);
+int fp8kv_stream_rmw(void* buf, int64_t bytes, uint32_t mask, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

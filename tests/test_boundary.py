@@ -199,6 +199,29 @@ def test_stage_argument_errors(fn, over, want):
     assert fn(**over) == want
 
 
+def _copy(**over):
+    a = dict(dst=FAKE, src=FAKE + 4096, nb=4096, stream=None)
+    a.update(over)
+    return K.lib().fp8kv_stream_copy(*a.values())
+
+
+def _rmw(**over):
+    a = dict(buf=FAKE, nb=4096, mask=0, stream=None)
+    a.update(over)
+    return K.lib().fp8kv_stream_rmw(*a.values())
+
+
+@pytest.mark.parametrize("fn,over,want", [
+    (_copy, dict(nb=-16), 2), (_copy, dict(nb=24), 2), (_copy, dict(dst=None), 1),
+    (_copy, dict(src=None), 1), (_copy, dict(dst=FAKE + 8), 4),
+    (_copy, dict(src=FAKE + 4), 4), (_copy, dict(nb=0, dst=None, src=None), 0),
+    (_rmw, dict(nb=-16), 2), (_rmw, dict(nb=8), 2), (_rmw, dict(buf=None), 1),
+    (_rmw, dict(buf=FAKE + 2), 4), (_rmw, dict(nb=0, buf=None), 0),
+])
+def test_stream_reference_argument_errors(fn, over, want):
+    assert fn(**over) == want
+
+
 @pytest.mark.skipif(torch.cuda.device_count() > 0, reason="a GPU is present")
 def test_no_device_is_reported_not_launched():
     # valid-looking arguments reach the device check, which fails without a
@@ -211,6 +234,7 @@ def test_no_device_is_reported_not_launched():
     assert _packed_ex() == 5 and _packed_ex(R=0, cs=None) == 5
     assert _prologue_scalar() == 5 and _dequant_scalar() == 5
     assert _prologue_scalar(pages=0, cache=None, scale=None) == 5
+    assert _copy() == 5 and _rmw() == 5
 
 
 def test_knobs():

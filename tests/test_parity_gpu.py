@@ -327,7 +327,8 @@ def test_packed_workloads(name):
 
 
 @pytest.mark.parametrize("heads", [(16, 0, 8), (0, 8, 8), (5, 3, 1), (1, 1, 0),
-                                   (32, 8, 8), (40, 4, 4)])
+                                   (32, 8, 8), (40, 4, 4), (7, 6, 2), (20, 5, 0),
+                                   (12, 0, 3)])
 def test_packed_head_mixes(heads):
     hq, hk, hv = heads
     w = I.PackedWorkload("mix", 33, hq, hk, hv, seed=5000 + hq * 7 + hk)
