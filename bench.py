@@ -22,9 +22,10 @@ Prints ONE JSON line:
                read side over all 131072 slots of the 131072 x 64 cache, and
                the same prologue as five separate launches, the unfused
                baseline, with the fusion speedup).  Each of these launches is
-               timed alone after a 1 GiB cache-flushing write (median and
+               timed alone after a 1 GiB cache-flushing read (median and
                minimum), so no working set starts in the 256 MB Infinity
-               Cache; prefill_flushed is the headline kernel timed that way.
+               Cache and no dirty line is left to write back;
+               prefill_flushed is the headline kernel timed that way.
 
 Usage: python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--quick]
 """
@@ -168,19 +169,23 @@ def main():
     del rbuf
     log(f"16 B/lane copy kernel {copy_gbps:.1f} GB/s, in-place RMW {rmw_gbps:.1f} GB/s")
 
-    # 1 GiB written between timed launches: more than the 256 MB Infinity
-    # Cache plus the L2s, so every timed launch starts from cold caches
-    flush_buf = torch.empty(2 ** 30, dtype=torch.uint8, device=dev)
+    # 1 GiB read between timed launches: more than the 256 MB Infinity Cache
+    # plus the L2s, so every timed launch starts from cold caches.  A read,
+    # not a write, leaves the caches clean: after a 1 GiB write the timed
+    # launch would also pay for writing back up to 256 MB of the flush's own
+    # dirty lines (measured: the 212 MB read side took 59 us after a write
+    # flush, 47 us after a read flush).
+    flush_buf = torch.ones(2 ** 28, dtype=torch.float32, device=dev)
 
     def time_flushed(fn, iters=20, warmup=3):
         """Per-launch seconds of `iters` launches, each preceded (outside its
-        events) by a 1 GiB cache-flushing write."""
+        events) by a 1 GiB cache-flushing read."""
         for _ in range(warmup):
             fn()
         ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
               for _ in range(iters)]
-        for i, (a, b) in enumerate(ev):
-            flush_buf.fill_(i & 0xFF)
+        for a, b in ev:
+            flush_buf.sum()
             a.record(stream)
             fn()
             b.record(stream)

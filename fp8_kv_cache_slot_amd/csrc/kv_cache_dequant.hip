@@ -6,13 +6,14 @@
 //   out[i, d]       = E4M3(code[s, d]) * 2^(scale[s, d / 64] - 127), d < 448
 //   out[i, 448 + j] = stored bf16 rotary value j
 //
-// Layout of the work.  One 64-lane wave per output row (1 KiB of bf16 = one
-// 16-byte vector per lane, as in the prologue).  Lane l < 56 reads the 8 code
-// bytes of dims 8l..8l+7 (one 8-byte load) and the row's 8-byte scale word
-// (one address for the whole wave), decodes with v_cvt_pk_f32_fp8, scales
-// exactly with v_ldexp and packs with v_cvt_pk_bf16_f32; lanes 56..63 move the
-// 128 stored rotary bytes unchanged.  Each wave gathers RS rows and issues all
-// of their loads before any arithmetic.  The output is written non-temporally.
+// Layout of the work.  A 64-lane wave writes one output row (1 KiB of bf16 =
+// one 16-byte vector per lane, as in the prologue): lane l < 56 decodes the 8
+// code bytes of dims 8l..8l+7 with v_cvt_pk_f32_fp8, scales them exactly by
+// the block's power of two with v_ldexp and packs with v_cvt_pk_bf16_f32;
+// lanes 56..63 pass the 128 stored rotary bytes through.  Rows come in groups
+// of RS, and each wave loops over its share of the groups with the loads of
+// the next group in flight while the current one is stored (see the kernel).
+// The output is written non-temporally.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -25,94 +26,194 @@ namespace {
 
 constexpr int kRopeLane0 = 56;
 
+// One group of RS rows as loaded.  Every lane issues the same three loads per
+// row, with no branch around them (so they stay in flight while other work
+// runs): 8 code bytes at dims 8 min(l, 55).., the rotary vector of lane
+// 56 + (l & 7), and the exponent byte of block l >> 3 (lanes 56..63 read the
+// unused byte 7 of the 8-byte exponent row).  Each lane keeps what it needs.
+// A row whose slot is invalid reads slot 0 (the cache has pages here) and is
+// stored as zeros.
+template <int RS>
+struct Rows {
+  u32x2_t codes[RS];
+  u32x4_t rope[RS];
+  uint32_t ebyte[RS];
+};
+
+__device__ __forceinline__ bool slot_valid(int64_t s, int64_t num_cache_slots) {
+  return s >= 0 && s < num_cache_slots;
+}
+
+template <int RS, bool SCALAR>
+__device__ __forceinline__ void load_rows(const uint8_t* __restrict__ kv_cache,
+                                          const uint8_t* __restrict__ kv_scale,
+                                          const int64_t* s, int64_t num_cache_slots,
+                                          int lane, Rows<RS>& d) {
+  const int cl = lane < kRopeLane0 ? lane : kRopeLane0 - 1;
+#pragma unroll
+  for (int r = 0; r < RS; ++r) {
+    const int64_t slot = slot_valid(s[r], num_cache_slots) ? s[r] : 0;
+    const uint8_t* row = kv_cache + slot * 576;
+    d.codes[r] = *reinterpret_cast<const u32x2_t*>(row + cl * 8);
+    d.rope[r] = *reinterpret_cast<const u32x4_t*>(row + 448 + (lane & 7) * 16);
+    if constexpr (SCALAR)
+      d.ebyte[r] = 0u;
+    else
+      d.ebyte[r] = kv_scale[slot * 8 + (lane >> 3)];
+  }
+}
+
+// Dequantise and store the RS rows of group grp (rows grp*RS ..); fs is the
+// scalar scale (SCALAR) or unused.
+template <int RS, bool SCALAR>
+__device__ __forceinline__ void store_rows(const Rows<RS>& d, const int64_t* s,
+                                           float fs, uint16_t* __restrict__ out,
+                                           int32_t grp, int32_t num_rows,
+                                           int64_t num_cache_slots, int lane) {
+#pragma unroll
+  for (int r = 0; r < RS; ++r) {
+    const int32_t i = grp * RS + r;
+    if (i >= num_rows) break;
+    const int e = static_cast<int>(d.ebyte[r]) - 127;
+    const int lo = static_cast<int>(d.codes[r][0]);
+    const int hi = static_cast<int>(d.codes[r][1]);
+    const float2_t p[4] = {__builtin_amdgcn_cvt_pk_f32_fp8(lo, false),
+                           __builtin_amdgcn_cvt_pk_f32_fp8(lo, true),
+                           __builtin_amdgcn_cvt_pk_f32_fp8(hi, false),
+                           __builtin_amdgcn_cvt_pk_f32_fp8(hi, true)};
+    float v[8];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      if constexpr (SCALAR) {
+        v[2 * k] = p[k][0] * fs;
+        v[2 * k + 1] = p[k][1] * fs;
+      } else {
+        v[2 * k] = __builtin_ldexpf(p[k][0], e);
+        v[2 * k + 1] = __builtin_ldexpf(p[k][1], e);
+      }
+    }
+    const u32x4_t q = {pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3]),
+                       pack_bf16(v[4], v[5]), pack_bf16(v[6], v[7])};
+    const u32x4_t z = {0u, 0u, 0u, 0u};
+    const u32x4_t o = slot_valid(s[r], num_cache_slots)
+                          ? (lane < kRopeLane0 ? q : d.rope[r])
+                          : z;
+    store16<true>(out + static_cast<int64_t>(i) * 512 + lane * 8, o);
+  }
+}
+
+// A VALU copy (DPP move with the identity lane pattern): the result is
+// defined by an ALU instruction, not by the load that produced the source.
+__device__ __forceinline__ uint32_t valu_copy(uint32_t x) {
+  return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(
+      0, static_cast<int>(x), 0xE4, 0xF, 0xF, false));
+}
+
 // SCALAR: the scalar-scale convention, out = E4M3(code) * scalar_scale[0]
 // (rounded once to fp32, then to bf16) and no exponent bytes are read.
+//
+// The gather is a chain of two dependent loads (slot, then row), so the work
+// is pipelined inside each wave.  Wave w of the grid takes the row groups
+// w, w + stride, w + 2 stride, ... (stride = waves in the grid; the grid is
+// capped at about eight waves per SIMD).  The slots of 64 / RS consecutive
+// groups of the wave (a batch) arrive with one vector load, lane L holding
+// row L % RS of group L / RS, and are read out with v_readlane; the next
+// batch is loaded while the current one is processed.  Inside a batch the
+// rows of group k + 1 are loaded before group k is dequantised and stored,
+// into two row buffers used in turn (the loop is unrolled by two, so no
+// buffer is copied while its loads are in flight).  No load sits behind a
+// branch, which lets the compiler count outstanding loads exactly instead of
+// waiting for all of them.
 template <int WAVES, int RS, bool SCALAR>
 __global__ void __launch_bounds__(WAVES * 64) kv_cache_gather_dequant_kernel(
     const uint8_t* __restrict__ kv_cache, const uint8_t* __restrict__ kv_scale,
     const float* __restrict__ scalar_scale, const int64_t* __restrict__ slots,
     uint16_t* __restrict__ out, int32_t num_rows, int64_t num_cache_slots) {
+  constexpr int GPB = 64 / RS;  // groups per slot batch
   const int lane = lane_id();
-  const int32_t first = (static_cast<int32_t>(blockIdx.x) * WAVES + wave_id()) * RS;
-  if (first >= num_rows) return;
+  const int32_t num_groups = (num_rows + RS - 1) / RS;
+  const int32_t stride = static_cast<int32_t>(gridDim.x) * WAVES;
+  const int32_t w = static_cast<int32_t>(blockIdx.x) * WAVES + wave_id();
+  if (w >= num_groups) return;
+  const int32_t n_my = (num_groups - 1 - w) / stride + 1;  // groups of this wave
 
-  int64_t slot[RS];
-  bool ok[RS];
+  if (num_cache_slots <= 0) {  // a cache without pages: every row is zero
+    const u32x4_t z = {0u, 0u, 0u, 0u};
+    for (int32_t q = 0; q < n_my; ++q) {
 #pragma unroll
-  for (int r = 0; r < RS; ++r) {
-    const int32_t i = first + r < num_rows ? first + r : num_rows - 1;
-    slot[r] = slots[i];
-    ok[r] = first + r < num_rows && slot[r] >= 0 && slot[r] < num_cache_slots;
-  }
-  u32x2_t codes[RS], sc[RS];
-  u32x4_t rope[RS];
-#pragma unroll
-  for (int r = 0; r < RS; ++r) {
-    codes[r] = u32x2_t{0u, 0u};
-    sc[r] = u32x2_t{0u, 0u};
-    rope[r] = u32x4_t{0u, 0u, 0u, 0u};
-    if (ok[r]) {
-      const uint8_t* row = kv_cache + slot[r] * 576;
-      if constexpr (!SCALAR)
-        sc[r] = *reinterpret_cast<const u32x2_t*>(kv_scale + slot[r] * 8);
-      if (lane < kRopeLane0)
-        codes[r] = *reinterpret_cast<const u32x2_t*>(row + lane * 8);
-      else
-        rope[r] = *reinterpret_cast<const u32x4_t*>(row + 448 + (lane - kRopeLane0) * 16);
-    }
-  }
-
-  const int b = lane >> 3;  // quantisation block of this lane's dims
-#pragma unroll
-  for (int r = 0; r < RS; ++r) {
-    if (first + r >= num_rows) break;
-    uint16_t* dst = out + static_cast<int64_t>(first + r) * 512 + lane * 8;
-    u32x4_t o = {0u, 0u, 0u, 0u};
-    if (ok[r]) {
-      if (lane < kRopeLane0) {
-        // a valid slot exists only when the cache has pages, and then the
-        // scalar scale pointer is a checked device pointer
-        float fs = 1.0f;
-        if constexpr (SCALAR) fs = *scalar_scale;
-        const uint32_t word = b < 4 ? sc[r][0] : sc[r][1];
-        const int e = static_cast<int>((word >> (8 * (b & 3))) & 0xFFu) - 127;
-        const int lo = static_cast<int>(codes[r][0]);
-        const int hi = static_cast<int>(codes[r][1]);
-        const float2_t p[4] = {__builtin_amdgcn_cvt_pk_f32_fp8(lo, false),
-                               __builtin_amdgcn_cvt_pk_f32_fp8(lo, true),
-                               __builtin_amdgcn_cvt_pk_f32_fp8(hi, false),
-                               __builtin_amdgcn_cvt_pk_f32_fp8(hi, true)};
-        float v[8];
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          if constexpr (SCALAR) {
-            v[2 * k] = p[k][0] * fs;
-            v[2 * k + 1] = p[k][1] * fs;
-          } else {
-            v[2 * k] = __builtin_ldexpf(p[k][0], e);
-            v[2 * k + 1] = __builtin_ldexpf(p[k][1], e);
-          }
-        }
-        o = u32x4_t{pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3]),
-                    pack_bf16(v[4], v[5]), pack_bf16(v[6], v[7])};
-      } else {
-        o = rope[r];
+      for (int r = 0; r < RS; ++r) {
+        const int32_t i = (w + q * stride) * RS + r;
+        if (i < num_rows) store16<true>(out + static_cast<int64_t>(i) * 512 + lane * 8, z);
       }
     }
-    store16<true>(dst, o);
+    return;
+  }
+  // with pages, the scalar scale pointer is a checked device pointer
+  float fs = 1.0f;
+  if constexpr (SCALAR) fs = *scalar_scale;
+
+  // Slot batch b: lane L loads the slot of row L % RS of this wave's group
+  // b * GPB + L / RS.  Indices past the last row re-read the last slot (in
+  // bounds); such rows are never stored.
+  auto load_batch = [&](int32_t b) {
+    const int64_t grp = w + (static_cast<int64_t>(b) * GPB + lane / RS) * stride;
+    int64_t i = grp * RS + lane % RS;
+    if (i > num_rows - 1) i = num_rows - 1;
+    return *reinterpret_cast<const u32x2_t*>(slots + i);
+  };
+  auto slots_of = [&](const u32x2_t& cb, int32_t k, int64_t* s) {
+#pragma unroll
+    for (int r = 0; r < RS; ++r) {
+      const uint32_t lo = __builtin_amdgcn_readlane(static_cast<int>(cb[0]), k * RS + r);
+      const uint32_t hi = __builtin_amdgcn_readlane(static_cast<int>(cb[1]), k * RS + r);
+      s[r] = static_cast<int64_t>((static_cast<uint64_t>(hi) << 32) | lo);
+    }
+  };
+
+  const int32_t n_batches = (n_my + GPB - 1) / GPB;
+  u32x2_t nb = load_batch(0);
+  for (int32_t b = 0; b < n_batches; ++b) {
+    const u32x2_t cb = {valu_copy(nb[0]), valu_copy(nb[1])};
+    nb = load_batch(b + 1 < n_batches ? b + 1 : b);  // the last batch re-reads itself
+    const int32_t q0 = b * GPB;
+    const int32_t cnt = n_my - q0 < GPB ? n_my - q0 : GPB;  // groups in this batch
+    Rows<RS> A, B;
+    int64_t sa[RS], sb[RS];
+    slots_of(cb, 0, sa);
+    load_rows<RS, SCALAR>(kv_cache, kv_scale, sa, num_cache_slots, lane, A);
+    for (int32_t k = 0; k < cnt; k += 2) {
+      // group k + 1 (the last group again when there is none: loaded, not stored)
+      slots_of(cb, k + 1 < cnt ? k + 1 : k, sb);
+      load_rows<RS, SCALAR>(kv_cache, kv_scale, sb, num_cache_slots, lane, B);
+      store_rows<RS, SCALAR>(A, sa, fs, out, w + (q0 + k) * stride, num_rows,
+                             num_cache_slots, lane);
+      if (k + 1 >= cnt) break;
+      slots_of(cb, k + 2 < cnt ? k + 2 : k + 1, sa);
+      load_rows<RS, SCALAR>(kv_cache, kv_scale, sa, num_cache_slots, lane, A);
+      store_rows<RS, SCALAR>(B, sb, fs, out, w + (q0 + k + 1) * stride, num_rows,
+                             num_cache_slots, lane);
+    }
   }
 }
 
+// 4 rows per group, at most 1024 blocks of 4 waves (four waves per SIMD of
+// the 256 CUs, each with two groups = 8 rows in flight).  Measured on MI355X
+// over all 131072 slots of a 2048-page cache, caches cold and clean: 43.9 us
+// in random slot order and 42.8 us in page order, against 50.9 / 51.0 us for
+// one group of 2 rows per wave without the loop; 2 rows per group and 2048 or
+// 4096 blocks came within 2-3%.
 constexpr int kDequantWaves = 4;
-constexpr int kDequantRows = 2;
+constexpr int kDequantRows = 4;
+constexpr int64_t kDequantMaxBlocks = 1024;
 
 }  // namespace
 
 int launch_gather_dequant(const DequantArgs& a, hipStream_t stream) {
   const int64_t rows_per_block = static_cast<int64_t>(kDequantWaves) * kDequantRows;
-  const int64_t blocks = (static_cast<int64_t>(a.num_rows) + rows_per_block - 1) /
-                         rows_per_block;
-  if (blocks > 0x7FFFFFFF) return FP8KV_ERR_SHAPE;
+  int64_t blocks = (static_cast<int64_t>(a.num_rows) + rows_per_block - 1) /
+                   rows_per_block;
+  if (blocks > kDequantMaxBlocks) blocks = kDequantMaxBlocks;
+  if (a.num_rows > 0x7FFFFFFF - kDequantRows) return FP8KV_ERR_SHAPE;  // row indices fit int32
   void* args[] = {const_cast<const uint8_t**>(&a.kv_cache),
                   const_cast<const uint8_t**>(&a.kv_scale),
                   const_cast<const float**>(&a.scalar_scale),

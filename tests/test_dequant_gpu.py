@@ -84,6 +84,21 @@ def test_full_size_permutation_of_long_cache():
     np.testing.assert_array_equal(got, O.kv_cache_gather_dequant(cache, scale, slots))
 
 
+def test_many_rows_per_wave():
+    # 600,001 rows from a 256-slot cache (slots repeat; some are invalid):
+    # beyond 524,288 rows every wave of the capped grid walks more than one
+    # batch of slots.  The oracle decodes each distinct slot once; a repeated
+    # slot has the same row by definition, an invalid one a zero row.
+    cache, scale = _random_cache(4, seed=44)
+    rng = np.random.default_rng(45)
+    slots = rng.integers(-3, 4 * 64 + 3, 600_001).astype(np.int64)
+    table = O.kv_cache_gather_dequant(cache, scale, np.arange(256, dtype=np.int64))
+    table = np.concatenate([table, np.zeros((1, 512), table.dtype)])
+    idx = np.where((slots >= 0) & (slots < 256), slots, 256)
+    got = _gpu(cache, scale, slots)
+    np.testing.assert_array_equal(got, table[idx])
+
+
 def test_exponent_range_and_empty_inputs():
     # exponents over [-110, +100]: every product is a normal or zero bf16
     cache, scale = _random_cache(2, seed=43, e_lo=17, e_hi=228)

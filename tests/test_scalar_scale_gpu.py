@@ -111,6 +111,37 @@ def test_read_side(s):
     P.check_bf16(got[:, :448], ref[:, :448], "scalar read side")
 
 
+def test_read_side_many_rows_per_wave():
+    # as the blockwise test: more than one batch of slots per wave
+    rng = np.random.default_rng(46)
+    cache = rng.integers(0, 256, (4, 64, 576), dtype=np.uint8)
+    codes = cache[..., :448]
+    codes[(codes & 0x7F) == 0x7F] ^= 0x01
+    slots = rng.integers(-3, 4 * 64 + 3, 600_001).astype(np.int64)
+    s = 0.0173
+    table = O.kv_cache_gather_dequant_scalar(cache, s, np.arange(256, dtype=np.int64))
+    table = np.concatenate([table, np.zeros((1, 512), table.dtype)])
+    idx = np.where((slots >= 0) & (slots < 256), slots, 256)
+    out = K.kv_cache_gather_dequant_scalar_scale(
+        torch.from_numpy(cache).to(DEV), torch.tensor([s], device=DEV),
+        torch.from_numpy(slots).to(DEV))
+    torch.cuda.synchronize()
+    got = I.bits(out)
+    # every row is one of the 257 table rows: compare the distinct ones to
+    # the oracle within the bf16 bound, and every row bit-exactly to its
+    # table row as the kernel produced it for the first occurrence
+    first = {}
+    for k, v in enumerate(idx[:20000]):
+        first.setdefault(int(v), k)
+    rows = np.array(sorted(first.values()))
+    np.testing.assert_array_equal(got[rows][:, 448:], table[idx[rows]][:, 448:])
+    P.check_bf16(got[rows][:, :448], table[idx[rows]][:, :448], "scalar read side rows")
+    kernel_table = np.zeros((257, 512), got.dtype)
+    kernel_table[idx[rows]] = got[rows]
+    assert len(first) == 257
+    np.testing.assert_array_equal(got, kernel_table[idx])
+
+
 def test_zero_pages():
     w = I.custom_dsv4(9, 3, seed=99)
     x = I.make_dsv4(w, DEV)
