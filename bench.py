@@ -282,7 +282,7 @@ def main():
         K.unfused_prologue(q, x["kv"], x["q_weight"], x["kv_weight"],
                            x["cos_sin_cache"], x["positions"], x["slot_mapping"],
                            cache, scale, x["eps"], kv_work=kv_work)
-    fper = time_flushed(lambda: call(x, q, cache, scale))
+    fper = time_flushed(lambda: call(x, q, cache, scale), args.steps, args.warmup)
     prefill_flushed = {"median_us": round(statistics.median(fper) * 1e6, 1),
                        "min_us": round(min(fper) * 1e6, 1),
                        "gbps": round(nbytes / statistics.median(fper) / 1e9, 1)}
@@ -435,6 +435,19 @@ def main():
                            "gbps": round(nb / m / 1e9, 1),
                            "unfused_median_us": round(um * 1e6, 2),
                            "fusion_speedup": round(um / m, 3)}
+            log(f"{name}: {extra[name]}")
+        # packed at 1 and 17 tokens: launch-bound, reported as latency
+        for name in ("packed_t1", "packed_t17"):
+            sw = I.PACKED_WORKLOADS[name]
+            sx = I.make_packed(sw, dev)
+            sq = sx["qkv"].clone()
+            per = time_flushed(lambda: K.qk_norm_rope_packed(
+                sq, sw.num_heads_q, sw.num_heads_k, sw.num_heads_v, sw.head_dim,
+                sw.eps, sx["q_weight"], sx["k_weight"], sx["cos_sin_cache"], True,
+                sx["position_ids"]), 50, 10)
+            extra[name] = {"tokens": sw.num_tokens, "heads": "16q/8k/8v x 128",
+                           "median_us": round(statistics.median(per) * 1e6, 2),
+                           "min_us": round(min(per) * 1e6, 2)}
             log(f"{name}: {extra[name]}")
         pw = I.PACKED_WORKLOADS["packed_t8192"]
         px = I.make_packed(pw, dev)
