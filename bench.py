@@ -258,6 +258,9 @@ def main():
             "tiling": list(K.get_tiling()),
             "dispatch_threshold_programs": K.get_dispatch_threshold(),
         },
+        "device": {"name": props.name, "arch": getattr(props, "gcnArchName", ""),
+                   "hip": torch.version.hip, "torch": torch.__version__,
+                   "cus": props.multi_processor_count},
         "pct_of_d2d": round(value / d2d_gbps, 4),
         "d2d_copy_gbps": round(d2d_gbps, 1),
         "copy_kernel_gbps": round(copy_gbps, 1),

@@ -4,7 +4,9 @@
 #include <hip/hip_runtime.h>
 
 #include <atomic>
+#include <cerrno>
 #include <cstdint>
+#include <cstdlib>
 #include <cstring>
 
 #include "fp8kv.h"
@@ -29,7 +31,19 @@ constexpr int64_t kDefaultThreshold = 8192;
 constexpr int kDefaultWaves = 4;
 constexpr int kDefaultSlots = 2;
 
-std::atomic<int64_t> g_threshold{kDefaultThreshold};
+// The threshold in force when the library loads: FP8KV_DISPATCH_THRESHOLD
+// if it holds a non-negative decimal integer, else the built-in default.
+int64_t initial_threshold() {
+  const char* e = std::getenv("FP8KV_DISPATCH_THRESHOLD");
+  if (!e || !*e) return kDefaultThreshold;
+  char* end = nullptr;
+  errno = 0;
+  const long long v = std::strtoll(e, &end, 10);
+  if (errno != 0 || *end != '\0' || v < 0) return kDefaultThreshold;
+  return static_cast<int64_t>(v);
+}
+
+std::atomic<int64_t> g_threshold{initial_threshold()};
 std::atomic<int32_t> g_tiling{(kDefaultWaves << 16) | kDefaultSlots};
 
 constexpr int kMaxDevices = 64;

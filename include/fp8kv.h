@@ -278,7 +278,9 @@ int fp8kv_abi_version(void);
  * (one (token, head) slot per 64-lane block); calls at or above it the tiled
  * kernel.  programs < 0 restores the built-in default; 0 sends everything to
  * the tiled kernel; INT64_MAX everything to the small-batch kernel.
- * Process-wide; returns FP8KV_OK.
+ * Process-wide; returns FP8KV_OK.  When the library is loaded, the threshold
+ * starts at the value of the environment variable FP8KV_DISPATCH_THRESHOLD if
+ * that is a non-negative decimal integer, else at the built-in default.
  */
 int fp8kv_set_dispatch_threshold(int64_t programs);
 int64_t fp8kv_get_dispatch_threshold(void);

@@ -251,6 +251,24 @@ def test_knobs():
     K.set_tiling(0, 0)
 
 
+@pytest.mark.parametrize("value,want", [("4096", 4096), ("0", 0), ("-5", None),
+                                        ("12x", None), ("", None)])
+def test_threshold_from_environment(value, want):
+    # a fresh process loads the library with the variable set
+    import subprocess
+    import sys
+    code = ("import ctypes,sys; L=ctypes.CDLL(sys.argv[1]); "
+            "L.fp8kv_get_dispatch_threshold.restype=ctypes.c_int64; "
+            "print(L.fp8kv_get_dispatch_threshold())")
+    env = dict(os.environ, FP8KV_DISPATCH_THRESHOLD=value)
+    out = subprocess.run([sys.executable, "-c", code, K.LIB_PATH], env=env,
+                         capture_output=True, text=True, check=True).stdout
+    env.pop("FP8KV_DISPATCH_THRESHOLD")
+    default = subprocess.run([sys.executable, "-c", code, K.LIB_PATH], env=env,
+                             capture_output=True, text=True, check=True).stdout
+    assert int(out) == (int(default) if want is None else want)
+
+
 def test_binding_rejects_host_tensors():
     x = I.make_dsv4(I.DSV4_WORKLOADS["tiny"], "cpu")
     with pytest.raises(ValueError, match="device tensor"):
