@@ -1,0 +1,83 @@
+"""The entry points under HIP graph capture: each call is captured once on
+torch's capture stream and replayed several times, with eager work (input
+resets) and a synchronisation between replays; every replay must equal the
+eager result bit for bit.  The library enqueues kernels only (no allocation,
+memset or synchronisation), which is what capture needs."""
+
+import pytest
+import torch
+
+import fp8_kv_cache_slot_amd as K
+from fp8_kv_cache_slot_amd import inputs as I
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+REPLAYS = 3
+
+
+def _capture(fn):
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fn()                      # warm-up outside capture
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    torch.cuda.synchronize()
+    return g
+
+
+@pytest.mark.parametrize("name", ["tiny", "decode"])
+def test_prologue(name):
+    w = I.DSV4_WORKLOADS[name]
+    x = I.make_dsv4(w, DEV)
+    q, c, s = x["q"].clone(), x["kv_cache"].clone(), x["kv_scale"].clone()
+
+    def run():
+        K.qnorm_rope_kv_quant_insert(q, x["kv"], x["q_weight"], x["kv_weight"],
+                                     x["cos_sin_cache"], x["positions"],
+                                     x["slot_mapping"], c, s, x["eps"])
+    run()
+    ref = [t.clone() for t in (q, c, s)]
+    g = _capture(run)
+    for _ in range(REPLAYS):
+        q.copy_(x["q"])
+        c.copy_(x["kv_cache"])
+        s.copy_(x["kv_scale"])
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for got, want in zip((q, c, s), ref):
+            assert torch.equal(got, want)
+
+
+def test_packed_and_read_side():
+    pw = I.PACKED_WORKLOADS["packed_t17"]
+    px = I.make_packed(pw, DEV)
+    qkv = px["qkv"].clone()
+    w = I.DSV4_WORKLOADS["decode"]
+    x = I.make_dsv4(w, DEV)
+    cache, scale = x["kv_cache"].clone(), x["kv_scale"].clone()
+    K.qnorm_rope_kv_quant_insert(x["q"].clone(), x["kv"], x["q_weight"],
+                                 x["kv_weight"], x["cos_sin_cache"], x["positions"],
+                                 x["slot_mapping"], cache, scale, x["eps"])
+    out = torch.empty((w.num_tokens, 512), dtype=torch.bfloat16, device=DEV)
+
+    def run():
+        K.qk_norm_rope_packed(qkv, pw.num_heads_q, pw.num_heads_k, pw.num_heads_v,
+                              pw.head_dim, pw.eps, px["q_weight"], px["k_weight"],
+                              px["cos_sin_cache"], True, px["position_ids"])
+        K.kv_cache_gather_dequant(cache, scale, x["slot_mapping"], out=out)
+    run()
+    ref_qkv, ref_out = qkv.clone(), out.clone()
+    g = _capture(run)
+    for _ in range(REPLAYS):
+        qkv.copy_(px["qkv"])
+        out.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(qkv, ref_qkv)
+        assert torch.equal(out, ref_out)
