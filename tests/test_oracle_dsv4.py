@@ -259,3 +259,34 @@ def test_cos_sin_generator_row_zero():
     cs = I.cos_sin_cache(16, 64).numpy()
     assert np.all(cs[0, :32] == 1.0) and np.all(cs[0, 32:] == 0.0)
     np.testing.assert_allclose(cs[:, :32] ** 2 + cs[:, 32:] ** 2, 1.0, atol=1e-6)
+
+
+def test_kv_normalised_is_the_unrounded_kv_row():
+    # The unrounded KV values the bound checks compare against: rounding them
+    # as the operator does must give the fused oracle's stored bytes exactly
+    # (bf16 rotary dims; the exponent of each block's maximum; E4M3 codes of
+    # y 2^-e), and with a constant row and eps = 0 the non-rotary dims are
+    # exactly kv_weight.
+    x = _host(I.custom_dsv4(12, 3, seed=77))
+    y = O.kv_normalised(x["kv"].copy(), x["kv_weight"], x["cos_sin_cache"],
+                        x["positions"], x["eps"])
+    out = _run(x)
+    rows = out["kv_cache"].reshape(-1, 576)
+    scales = out["kv_scale"].reshape(-1, 8)
+    for t, s in enumerate(x["slot_mapping"]):
+        if not 0 <= s < rows.shape[0]:
+            continue
+        rot = _bf16(y[t, 448:])
+        np.testing.assert_array_equal(rows[s, 448:].view(np.uint16), rot)
+        for b in range(7):
+            blk = y[t, 64 * b:64 * b + 64]
+            e = O.ue8m0_exponent(float(np.abs(blk).max()))
+            assert scales[s, b] == e + 127
+            codes = [O.e4m3_encode(float(v) * 2.0 ** -e) for v in blk]
+            np.testing.assert_array_equal(rows[s, 64 * b:64 * b + 64], codes)
+    rng = np.random.default_rng(78)
+    kw = _bf16(rng.uniform(0.5, 1.5, 512))
+    kv = np.full((2, 512), O.bf16_rne(0.75), np.uint16)
+    cs = rng.uniform(-1, 1, (4, 64)).astype(np.float32)
+    yc = O.kv_normalised(kv, kw, cs, np.array([3, 1], np.int64), 0.0)
+    np.testing.assert_array_equal(yc[:, :448], np.broadcast_to(_val(kw[:448]), (2, 448)))
