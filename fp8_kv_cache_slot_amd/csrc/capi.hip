@@ -20,11 +20,12 @@ namespace {
 
 // Programs = num_tokens * (num_heads + 1) below which the small-batch kernel
 // runs (the quantity FlagGems PR #5449 "Dispatch threshold" dispatches on).
-// Measured on MI355X with the caches flushed between launches: below ~8k
-// programs both kernels sit on the same ~6 us launch floor; the tiled kernel
-// is ahead from 8320 programs at 64 heads (128 tokens) and from 8256 at 128
-// heads (64 tokens), so one program count serves both head counts.
-constexpr int64_t kDefaultThreshold = 8192;
+// Measured on MI355X, each launch timed after a cache-flushing read: below
+// ~2k programs both kernels sit on the same ~6.1 us launch floor (within
+// 0.1 us); the tiled kernel is ahead from 2080 programs at 64 heads (32
+// tokens) and from 2064 at 128 heads (16 tokens), by up to 10% in the range
+// to 8k programs, so one program count serves both head counts.
+constexpr int64_t kDefaultThreshold = 2048;
 // Tiled shape: 4 waves per block, 2 Q heads per wave.  2x2, 4x2 and 8x2 all
 // reach ~6.1-6.2 TB/s on the large workloads; 4x2 is the most even across
 // 32768x64, 131072x64, 32768x128 and the mid-size (128..2048 token) range.
