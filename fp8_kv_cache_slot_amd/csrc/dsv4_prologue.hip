@@ -55,6 +55,14 @@ __device__ __forceinline__ void rotate4(float* y, f32x4_t c, f32x4_t s) {
   }
 }
 
+// The row load goes out first and the slot and position loads overlap it.
+// A skipped token (slot or position out of range) turns off the stores, not
+// the loads: with an early return on a loaded index in front of them, hipcc
+// moves the loads below the branch and the wave waits for the index, then
+// for the row, one memory round trip after the other.  The cos/sin row index
+// depends on the slot as well (a skipped token rotates with row 0, and stores
+// nothing), so the slot load is issued with the position load instead of
+// being sunk to the stores at the end.
 template <bool SCALAR>
 __device__ __forceinline__ void kv_row(
     int32_t t, const uint16_t* __restrict__ kv,
@@ -64,14 +72,14 @@ __device__ __forceinline__ void kv_row(
     uint8_t* __restrict__ kv_scale, const float* __restrict__ scalar_scale,
     int64_t num_cache_slots, int64_t max_position, float eps) {
   const int lane = lane_id();
-  const int64_t slot = slot_mapping[t];
-  if (slot < 0 || slot >= num_cache_slots) return;  // skipped token
-  const int64_t pos = positions[t];
-  if (pos < 0 || pos >= max_position) return;
-
   const u32x4_t x = load16<true>(kv + static_cast<int64_t>(t) * 512 + lane * 8);
   float w[8];
   unpack8(load16<false>(kv_weight + lane * 8), w);
+  const int64_t slot = slot_mapping[t];
+  const int64_t pos_in = positions[t];
+  const bool write = pos_in >= 0 && pos_in < max_position && slot >= 0 &&
+                     slot < num_cache_slots;
+  const int64_t pos = write ? pos_in : 0;
   f32x4_t c = {1.f, 1.f, 1.f, 1.f}, s = {0.f, 0.f, 0.f, 0.f};
   if (lane >= kRopeLane0) {
     const float* row = cos_sin + pos * 64 + (lane - kRopeLane0) * 4;
@@ -82,10 +90,15 @@ __device__ __forceinline__ void kv_row(
   rms_normalise(x, w, eps, y);
   if (lane >= kRopeLane0) rotate4(y, c, s);
 
-  if constexpr (SCALAR)
-    quantise_store_row_scalar(y, lane, kv_cache + slot * 576, *scalar_scale);
-  else
-    quantise_store_row(y, lane, kv_cache + slot * 576, kv_scale + slot * 8);
+  if constexpr (SCALAR) {
+    // read only for a token that is written (the pointer may be NULL when
+    // the cache has no pages, and then no token is written)
+    if (write)
+      quantise_store_row_scalar(y, lane, kv_cache + slot * 576, *scalar_scale);
+  } else {
+    if (write)
+      quantise_store_row(y, lane, kv_cache + slot * 576, kv_scale + slot * 8);
+  }
 }
 
 template <int WAVES, int QS, bool SCALAR>
@@ -143,8 +156,11 @@ __global__ void __launch_bounds__(WAVES * 64) dsv4_prologue_kernel(
     t = qwave / waves_per_token;
     h0 = (qwave - t * waves_per_token) * QS;
   }
-  const int64_t pos = positions[t];
-  if (pos < 0 || pos >= max_position) return;
+  // An out-of-range position turns off the token's stores, not an early
+  // return, so that no branch on it sits in front of the loads above.
+  const int64_t pos_in = positions[t];
+  const bool pos_ok = pos_in >= 0 && pos_in < max_position;
+  const int64_t pos = pos_ok ? pos_in : 0;
   f32x4_t c = {1.f, 1.f, 1.f, 1.f}, sn = {0.f, 0.f, 0.f, 0.f};
   if (lane >= kRopeLane0) {
     const float* row = cos_sin + pos * 64 + (lane - kRopeLane0) * 4;
@@ -160,7 +176,7 @@ __global__ void __launch_bounds__(WAVES * 64) dsv4_prologue_kernel(
     if (lane >= kRopeLane0) rotate4(y, c, sn);
     u32x4_t o = {pack_bf16(y[0], y[1]), pack_bf16(y[2], y[3]),
                  pack_bf16(y[4], y[5]), pack_bf16(y[6], y[7])};
-    store16<true>(base + s * 512, o);
+    if (pos_ok) store16<true>(base + s * 512, o);
   }
 }
 
