@@ -134,6 +134,21 @@ def test_every_built_tiling():
         K.set_tiling(3, 3)
 
 
+@pytest.mark.parametrize("heads", [3, 5, 6, 7, 9, 11])
+def test_ragged_heads_every_tiling(heads):
+    # head counts that are not a multiple of the heads per wave: the last
+    # wave of each token holds fewer heads (re-reads the first, stores none)
+    w = I.custom_dsv4(37, heads, seed=3100 + heads, max_position=8192)
+    x = I.make_dsv4(w, DEV)
+    h = _host(x)
+    ref = _oracle(h)
+    for wv, qs in [(1, 2), (2, 2), (4, 2), (4, 4), (8, 2), (8, 4), (16, 2)]:
+        _say(f"H={heads} tiling {wv}x{qs}")
+        K.set_tiling(wv, qs)
+        _compare_full(h, ref, _run(x, TILED), f"H={heads} tiling {wv}x{qs}")
+    K.set_tiling(0, 0)
+
+
 def _sampled_tokens(T, rng, n_random=192):
     picks = set(range(min(64, T))) | set(range(max(0, T - 64), T))
     picks |= set(rng.choice(T, size=min(n_random, T), replace=False).tolist())

@@ -92,6 +92,28 @@ def test_workloads(name, s):
             assert np.all(gc[mask] == I.CACHE_CANARY)
 
 
+@pytest.mark.parametrize("heads", [3, 7])
+def test_ragged_heads(heads):
+    # the tiled kernel's last wave of each token holds one head (of two)
+    w = I.custom_dsv4(29, heads, seed=3200 + heads, max_position=8192)
+    x = I.make_dsv4(w, DEV)
+    h = {k: (I.bits(v).copy() if isinstance(v, torch.Tensor) else v)
+         for k, v in x.items()}
+    s = 0.0173
+    rq, rc = _oracle(h, s)
+    v = P.valid_slots(h["slot_mapping"], w.num_pages * 64)
+    slots = h["slot_mapping"][v]
+    for label, thr in [("small", SMALL), ("tiled", TILED)]:
+        q, cache = _run(x, s, thr)
+        P.check_bf16(I.bits(q), rq, f"H={heads} {label} q")
+        gc = I.bits(cache).reshape(-1, 576)
+        rcc = rc.reshape(-1, 576)
+        P.check_codes(gc[slots, :448], rcc[slots, :448], f"H={heads} {label} codes")
+        mask = np.ones(gc.shape[0], bool)
+        mask[slots] = False
+        assert np.all(gc[mask] == I.CACHE_CANARY)
+
+
 @pytest.mark.parametrize("s", [0.0173, 3.5, 2.0 ** -10])
 def test_read_side(s):
     rng = np.random.default_rng(int(s * 1000) + 7)
