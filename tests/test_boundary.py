@@ -269,6 +269,16 @@ def test_threshold_from_environment(value, want):
     assert int(out) == (int(default) if want is None else want)
 
 
+def test_c_driver_builds_and_links():
+    # the plain C caller of the library compiles against include/fp8kv.h and
+    # resolves libfp8kv.so and the HIP runtime (usage error: no GPU touched)
+    import subprocess
+    from tests import build_c_driver
+    exe = build_c_driver.build()
+    r = subprocess.run([exe], capture_output=True, text=True)
+    assert r.returncode == 1 and "usage" in r.stderr
+
+
 def test_binding_rejects_host_tensors():
     x = I.make_dsv4(I.DSV4_WORKLOADS["tiny"], "cpu")
     with pytest.raises(ValueError, match="device tensor"):

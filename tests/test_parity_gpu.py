@@ -109,7 +109,7 @@ def test_small_workloads_all_paths(name):
 def test_page_token_counts_both_paths(heads):
     # Token counts that are not multiples of a plausible tiling, plus 1, 4 and
     # 17 tokens pushed through the tiled kernel.
-    for T in [1, 4, 17, 511, 512, 777, 1000]:
+    for T in [1, 4, 17, 511, 512, 777, 1000, 4096]:
         _say(f"T={T} H={heads}")
         w = I.custom_dsv4(T, heads, seed=2000 + T + heads, max_position=8192)
         x = I.make_dsv4(w, DEV)
