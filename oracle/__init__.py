@@ -63,6 +63,9 @@ def _load():
     lib.oracle_kv_quant_insert.argtypes = [P, P, P, P, I64, I64]
     lib.oracle_kv_quant_insert.restype = None
     lib.oracle_kv_cache_gather_dequant.argtypes = [P, P, P, I64, I64, P]
+    lib.oracle_kv_cache_gather_dequant_paged.argtypes = [
+        P, P, I64, P, I32, I32, P, P, I64, P]
+    lib.oracle_kv_cache_gather_dequant_paged.restype = None
     lib.oracle_kv_cache_gather_dequant_scalar.argtypes = [
         P, ctypes.c_float, P, I64, I64, P]
     lib.oracle_kv_cache_gather_dequant_scalar.restype = None
@@ -230,6 +233,31 @@ def kv_cache_gather_dequant(kv_cache, kv_scale, slots):
     _load().oracle_kv_cache_gather_dequant(
         _ptr(kv_cache, np.uint8), _ptr(kv_scale, np.uint8), _ptr(slots, np.int64),
         slots.shape[0], pages, _ptr(out, np.uint16, True))
+    return out
+
+
+def kv_cache_gather_dequant_paged(kv_cache, kv_scale, block_table, seq_lens,
+                                  out_offsets, out):
+    """Block-table read side, in place on ``out`` (uint16 [N, 512]): token j
+    of sequence s (slot block_table[s, j // 64] * 64 + j % 64) goes to row
+    out_offsets[s] + j; rows no sequence covers are left as they are."""
+    pages = kv_cache.shape[0]
+    if kv_cache.shape != (pages, 64, 576) or kv_scale.shape != (pages, 64, 8):
+        raise ValueError("cache must be [pages,64,576], scale [pages,64,8]")
+    block_table = np.ascontiguousarray(block_table, np.int32)
+    if block_table.ndim != 2:
+        raise ValueError("block_table must be [num_seqs, max_blocks_per_seq]")
+    S, M = block_table.shape
+    seq_lens = np.ascontiguousarray(seq_lens, np.int32)
+    out_offsets = np.ascontiguousarray(out_offsets, np.int64)
+    if seq_lens.shape != (S,) or out_offsets.shape != (S,):
+        raise ValueError("seq_lens and out_offsets must be [num_seqs]")
+    if out.ndim != 2 or out.shape[1] != 512:
+        raise ValueError("out must be [N, 512]")
+    _load().oracle_kv_cache_gather_dequant_paged(
+        _ptr(kv_cache, np.uint8), _ptr(kv_scale, np.uint8), pages,
+        _ptr(block_table, np.int32), S, M, _ptr(seq_lens, np.int32),
+        _ptr(out_offsets, np.int64), out.shape[0], _ptr(out, np.uint16, True))
     return out
 
 

@@ -379,27 +379,49 @@ void oracle_kv_quant_insert(const uint16_t* kv, const int64_t* slot_mapping,
   }
 }
 
+// One cache row dequantised (blockwise exponents), or a zero row for a slot
+// outside [0, num_slots).
+static void dequant_row(const uint8_t* kv_cache, const uint8_t* kv_scale,
+                        int64_t slot, int64_t num_slots, uint16_t* dst) {
+  if (slot < 0 || slot >= num_slots) {
+    for (int d = 0; d < kHeadDim; ++d) dst[d] = 0;
+    return;
+  }
+  const uint8_t* row = kv_cache + slot * kRowBytes;
+  const uint8_t* scale = kv_scale + slot * kScaleBytes;
+  for (int d = 0; d < kRopeStart; ++d) {
+    const int e = static_cast<int>(scale[d / kQuantBlock]) - 127;
+    dst[d] = oracle_bf16_rne(std::ldexp(oracle_e4m3_decode(row[d]), e));
+  }
+  for (int j = 0; j < kRopeDim; ++j)
+    dst[kRopeStart + j] = static_cast<uint16_t>(
+        row[kRopeStart + 2 * j] | (row[kRopeStart + 2 * j + 1] << 8));
+}
+
 void oracle_kv_cache_gather_dequant(const uint8_t* kv_cache,
                                     const uint8_t* kv_scale,
                                     const int64_t* slots, int64_t num_rows,
                                     int64_t num_pages, uint16_t* out) {
   const int64_t num_slots = num_pages * kPageSize;
-  for (int64_t i = 0; i < num_rows; ++i) {
-    uint16_t* dst = out + i * kHeadDim;
-    const int64_t slot = slots[i];
-    if (slot < 0 || slot >= num_slots) {
-      for (int d = 0; d < kHeadDim; ++d) dst[d] = 0;
-      continue;
+  for (int64_t i = 0; i < num_rows; ++i)
+    dequant_row(kv_cache, kv_scale, slots[i], num_slots, out + i * kHeadDim);
+}
+
+void oracle_kv_cache_gather_dequant_paged(
+    const uint8_t* kv_cache, const uint8_t* kv_scale, int64_t num_pages,
+    const int32_t* block_table, int32_t num_seqs, int32_t max_blocks_per_seq,
+    const int32_t* seq_lens, const int64_t* out_offsets, int64_t num_rows,
+    uint16_t* out) {
+  const int64_t num_slots = num_pages * kPageSize;
+  for (int32_t s = 0; s < num_seqs; ++s) {
+    const int64_t len = seq_lens[s];
+    for (int64_t j = 0; j < len && j < int64_t{max_blocks_per_seq} * kPageSize; ++j) {
+      const int64_t row = out_offsets[s] + j;
+      if (row < 0 || row >= num_rows) continue;
+      const int64_t page = block_table[int64_t{s} * max_blocks_per_seq + j / kPageSize];
+      const int64_t slot = page < 0 || page >= num_pages ? -1 : page * kPageSize + j % kPageSize;
+      dequant_row(kv_cache, kv_scale, slot, num_slots, out + row * kHeadDim);
     }
-    const uint8_t* row = kv_cache + slot * kRowBytes;
-    const uint8_t* scale = kv_scale + slot * kScaleBytes;
-    for (int d = 0; d < kRopeStart; ++d) {
-      const int e = static_cast<int>(scale[d / kQuantBlock]) - 127;
-      dst[d] = oracle_bf16_rne(std::ldexp(oracle_e4m3_decode(row[d]), e));
-    }
-    for (int j = 0; j < kRopeDim; ++j)
-      dst[kRopeStart + j] = static_cast<uint16_t>(
-          row[kRopeStart + 2 * j] | (row[kRopeStart + 2 * j + 1] << 8));
   }
 }
 

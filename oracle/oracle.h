@@ -156,6 +156,22 @@ void oracle_kv_cache_gather_dequant(const uint8_t* kv_cache,
                                     const int64_t* slots, int64_t num_rows,
                                     int64_t num_pages, uint16_t* out);
 
+/*
+ * The read side through block tables, as an attention consumer indexes the
+ * cache: sequence s holds seq_lens[s] tokens, 64 to a page, in the pages
+ * block_table[s * max_blocks_per_seq + 0, 1, ...] in order, so its token j
+ * is slot block_table[s * max_blocks_per_seq + j / 64] * 64 + j % 64.  That
+ * row, dequantised as by oracle_kv_cache_gather_dequant (a page id outside
+ * [0, num_pages) gives a zero row), is written to out[out_offsets[s] + j].
+ * Tokens j >= max_blocks_per_seq * 64 and rows outside [0, num_rows) are not
+ * written; nor is any row of out no sequence covers.
+ */
+void oracle_kv_cache_gather_dequant_paged(
+    const uint8_t* kv_cache, const uint8_t* kv_scale, int64_t num_pages,
+    const int32_t* block_table, int32_t num_seqs, int32_t max_blocks_per_seq,
+    const int32_t* seq_lens, const int64_t* out_offsets, int64_t num_rows,
+    uint16_t* out);
+
 /* Read side of the scalar-scale convention: out[i, d] =
  * bf16(E4M3(code[s, d]) * kv_cache_scale) for d < 448, rotary part copied,
  * invalid slots give +0 rows.  The product is rounded once from double. */

@@ -74,3 +74,68 @@ def test_round_trip_error_bound():
     assert np.all(np.abs(out[:, :448] - yq) <= bound * (1 + 1e-12))
     yr = y[:, 448:]
     assert np.all(np.abs(out[:, 448:] - yr) <= np.abs(yr) * 2.0 ** -8 + 1e-300)
+
+
+def _random_cache(pages, seed):
+    rng = np.random.default_rng(seed)
+    cache = rng.integers(0, 256, (pages, 64, 576), dtype=np.uint8)
+    codes = cache[..., :448]
+    codes[(codes & 0x7F) == 0x7F] ^= 0x01
+    scale = rng.integers(127 - 30, 127 + 8, (pages, 64, 8), dtype=np.uint8)
+    return cache, scale
+
+
+def test_paged_read_returns_what_the_writer_wrote():
+    # The writer's view: each sequence takes whole pages from a shuffled free
+    # list and its tokens fill them in order, 64 per page; its slot map is
+    # the concatenation of those pages' slot ranges.  The prologue writes the
+    # tokens there.  The reader's view: the block table and the lengths.
+    # Reading every sequence back must give, row for row, the flat read of
+    # the writer's slots (token order = out_offsets order).
+    rng = np.random.default_rng(90)
+    lens = [70, 1, 128, 33, 0, 64]
+    M = 3
+    pages = 10
+    free = iter(rng.permutation(pages).tolist())
+    table = np.full((len(lens), M), -1, np.int32)
+    slots = []
+    for s, L in enumerate(lens):
+        own = [next(free) for _ in range(-(-L // 64))]
+        table[s, :len(own)] = own
+        ranges = [np.arange(p * 64, p * 64 + 64) for p in own]
+        slots.append(np.concatenate(ranges)[:L] if ranges else np.zeros(0, np.int64))
+    slot_mapping = np.concatenate(slots).astype(np.int64)
+    T = slot_mapping.shape[0]
+    x = {k: (I.bits(v).copy() if isinstance(v, torch.Tensor) else v)
+         for k, v in I.make_dsv4(I.custom_dsv4(T, 2, seed=91, num_pages=pages),
+                                 "cpu").items()}
+    x["slot_mapping"] = slot_mapping
+    O.qnorm_rope_kv_quant_insert(x["q"], x["kv"], x["q_weight"], x["kv_weight"],
+                                 x["cos_sin_cache"], x["positions"], slot_mapping,
+                                 x["kv_cache"], x["kv_scale"], x["eps"])
+    offsets = np.concatenate([[0], np.cumsum(lens)[:-1]]).astype(np.int64)
+    out = np.full((T, 512), 0x7777, np.uint16)
+    O.kv_cache_gather_dequant_paged(x["kv_cache"], x["kv_scale"], table, lens,
+                                    offsets, out)
+    np.testing.assert_array_equal(
+        out, O.kv_cache_gather_dequant(x["kv_cache"], x["kv_scale"], slot_mapping))
+
+
+def test_paged_read_edge_semantics():
+    cache, scale = _random_cache(4, 92)
+    flat = O.kv_cache_gather_dequant(cache, scale, np.arange(4 * 64, dtype=np.int64))
+    table = np.array([[0, -1, 9], [3, 2, 1], [1, 2, 3], [2, 0, 0]], np.int32)
+    lens = np.array([150, 0, 300, 5], np.int32)      # 300 > 3 pages: capped at 192
+    offsets = np.array([10, 0, 170, 395], np.int64)  # the last one runs past N
+    N = 398
+    canary = 0x7777
+    out = np.full((N, 512), canary, np.uint16)
+    O.kv_cache_gather_dequant_paged(cache, scale, table, lens, offsets, out)
+    want = np.full((N, 512), canary, np.uint16)
+    want[10:74] = flat[0:64]                 # page 0
+    want[74:160] = 0                         # page -1, then page 9 (>= 4 pages)
+    want[170:234] = flat[64:128]             # sequence 2: pages 1, 2, 3
+    want[234:298] = flat[128:192]
+    want[298:362] = flat[192:256]            # tokens 192..299 are past 3 pages
+    want[395:398] = flat[128:131]            # sequence 3: rows 398, 399 are past N
+    np.testing.assert_array_equal(out, want)
