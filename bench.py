@@ -413,7 +413,25 @@ def main():
                     "median_us": round(m * 1e6, 1), "min_us": round(min(per) * 1e6, 1),
                     "gbps": round(nb / m / 1e9, 1)}
                 log(f"dequant_long64: {extra['dequant_long64']}")
-                del slots, out
+                # the same cache read through block tables: 32 sequences of
+                # 4096 tokens over all 2048 pages, pages in a seeded order
+                S = 32
+                pages = wl.num_pages
+                table = torch.randperm(pages, generator=g, device=dev).to(
+                    torch.int32).view(S, pages // S).contiguous()
+                L = pages // S * 64
+                lens = torch.full((S,), L, dtype=torch.int32, device=dev)
+                offs = torch.arange(S, dtype=torch.int64, device=dev) * L
+                per = time_flushed(lambda: K.kv_cache_gather_dequant_paged(
+                    cc, ss, table, lens, offs, out))
+                m = statistics.median(per)
+                nb = A.dequant_paged_bytes(S * L, S * L, pages, S)
+                extra["dequant_paged_long64"] = {
+                    "rows": S * L, "sequences": S, "bytes": nb,
+                    "median_us": round(m * 1e6, 1), "min_us": round(min(per) * 1e6, 1),
+                    "gbps": round(nb / m / 1e9, 1)}
+                log(f"dequant_paged_long64: {extra['dequant_paged_long64']}")
+                del slots, out, table, lens, offs
             del xx, qq, cc, ss
             torch.cuda.empty_cache()
         extra["prefill_flushed"] = prefill_flushed

@@ -52,5 +52,14 @@ def dequant_bytes(num_rows: int, num_valid: int) -> int:
     return num_rows * (8 + 2 * HEAD_DIM) + num_valid * (448 + 2 * ROPE_DIM + 7)
 
 
+def dequant_paged_bytes(num_rows: int, num_valid: int, table_entries: int,
+                        num_seqs: int) -> int:
+    """Block-table read side: per row the bf16 output (and the cache row and
+    exponents when its page is valid); the block table (4 B per entry read)
+    and a length (4 B) and output offset (8 B) per sequence."""
+    return (num_rows * 2 * HEAD_DIM + num_valid * (448 + 2 * ROPE_DIM + 7)
+            + 4 * table_entries + 12 * num_seqs)
+
+
 def dsv4_scalar_bytes(num_tokens: int, num_heads: int, num_written: int) -> int:
     return dsv4_bytes(num_tokens, num_heads, num_written) - 7 * num_written + 4

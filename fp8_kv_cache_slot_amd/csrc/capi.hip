@@ -248,6 +248,33 @@ FP8KV_API int kv_cache_gather_dequant(const uint8_t* kv_cache,
   return launch_gather_dequant(a, static_cast<hipStream_t>(stream));
 }
 
+FP8KV_API int kv_cache_gather_dequant_paged(
+    const uint8_t* kv_cache, const uint8_t* kv_scale, int64_t num_pages,
+    int32_t page_size, const int32_t* block_table, int32_t num_seqs,
+    int32_t max_blocks_per_seq, const int32_t* seq_lens,
+    const int64_t* out_offsets, int64_t num_rows, void* out, void* stream) {
+  using namespace fp8kv;
+  int st = validate_gather_dequant_paged(kv_cache, kv_scale, num_pages, page_size,
+                                         block_table, num_seqs, max_blocks_per_seq,
+                                         seq_lens, out_offsets, num_rows, out);
+  if (st != FP8KV_OK || num_seqs == 0 || max_blocks_per_seq == 0 || num_rows == 0)
+    return st;
+  st = check_device();
+  if (st != FP8KV_OK) return st;
+  PagedDequantArgs a;
+  a.kv_cache = kv_cache;
+  a.kv_scale = kv_scale;
+  a.block_table = block_table;
+  a.seq_lens = seq_lens;
+  a.out_offsets = out_offsets;
+  a.out = static_cast<uint16_t*>(out);
+  a.num_seqs = num_seqs;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.num_pages = num_pages;
+  a.num_rows = num_rows;
+  return launch_gather_dequant_paged(a, static_cast<hipStream_t>(stream));
+}
+
 FP8KV_API int rms_norm_rows(const void* x, void* out, const void* weight,
                             int64_t num_rows, int32_t row_dim, float eps,
                             void* stream) {

@@ -206,7 +206,104 @@ constexpr int kDequantWaves = 4;
 constexpr int kDequantRows = 4;
 constexpr int64_t kDequantMaxBlocks = 1024;
 
+// The read side through block tables, as an attention consumer indexes the
+// cache: token j of sequence s sits in slot
+// block_table[s, j / 64] * 64 + j % 64 and its row goes to
+// out[out_offsets[s] + j].  Grid: x = groups of PRS consecutive tokens of a
+// sequence (covering max_blocks_per_seq pages), y = sequence.  PRS divides 64,
+// so a wave's rows are consecutive slots of one page (PRS * 576 contiguous
+// bytes).  The page id, length and output offset are three independent
+// loads; every lane then issues its row loads with no branch in front of
+// them (an invalid page reads slot 0 and stores zero rows, as in the slot-list
+// kernel), and only the stores depend on the length and the output bounds.
+template <int WAVES, int PRS>
+__global__ void __launch_bounds__(WAVES * 64) kv_cache_gather_dequant_paged_kernel(
+    const uint8_t* __restrict__ kv_cache, const uint8_t* __restrict__ kv_scale,
+    const int32_t* __restrict__ block_table, const int32_t* __restrict__ seq_lens,
+    const int64_t* __restrict__ out_offsets, uint16_t* __restrict__ out,
+    int32_t max_blocks_per_seq, int64_t num_pages, int64_t num_rows) {
+  static_assert(64 % PRS == 0, "a group must not straddle a page");
+  const int lane = lane_id();
+  const int32_t seq = static_cast<int32_t>(blockIdx.y);
+  // j0 < max_blocks_per_seq * 64: the grid covers exactly that many tokens
+  const int32_t j0 = (static_cast<int32_t>(blockIdx.x) * WAVES + wave_id()) * PRS;
+  const int64_t page =
+      block_table[static_cast<int64_t>(seq) * max_blocks_per_seq + j0 / 64];
+  const int32_t len = seq_lens[seq];
+  const int64_t first = out_offsets[seq] + j0;
+  if (j0 >= len) return;
+
+  const u32x4_t z = {0u, 0u, 0u, 0u};
+  if (num_pages <= 0) {  // a cache without pages: every row is zero
+#pragma unroll
+    for (int r = 0; r < PRS; ++r) {
+      const int64_t i = first + r;
+      if (j0 + r < len && i >= 0 && i < num_rows)
+        store16<true>(out + i * 512 + lane * 8, z);
+    }
+    return;
+  }
+  const bool page_ok = page >= 0 && page < num_pages;
+  const int64_t slot0 = (page_ok ? page : 0) * 64 + j0 % 64;
+  int64_t sl[PRS];
+#pragma unroll
+  for (int r = 0; r < PRS; ++r) sl[r] = page_ok ? slot0 + r : -1;
+  Rows<PRS> d;
+  load_rows<PRS, false>(kv_cache, kv_scale, sl, num_pages * 64, lane, d);
+#pragma unroll
+  for (int r = 0; r < PRS; ++r) {
+    const int64_t i = first + r;
+    if (j0 + r >= len || i < 0 || i >= num_rows) continue;
+    const int e = static_cast<int>(d.ebyte[r]) - 127;
+    const int lo = static_cast<int>(d.codes[r][0]);
+    const int hi = static_cast<int>(d.codes[r][1]);
+    const float2_t p[4] = {__builtin_amdgcn_cvt_pk_f32_fp8(lo, false),
+                           __builtin_amdgcn_cvt_pk_f32_fp8(lo, true),
+                           __builtin_amdgcn_cvt_pk_f32_fp8(hi, false),
+                           __builtin_amdgcn_cvt_pk_f32_fp8(hi, true)};
+    float v[8];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      v[2 * k] = __builtin_ldexpf(p[k][0], e);
+      v[2 * k + 1] = __builtin_ldexpf(p[k][1], e);
+    }
+    const u32x4_t q = {pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3]),
+                       pack_bf16(v[4], v[5]), pack_bf16(v[6], v[7])};
+    const u32x4_t o = page_ok ? (lane < kRopeLane0 ? q : d.rope[r]) : z;
+    store16<true>(out + i * 512 + lane * 8, o);
+  }
+}
+
+// 2 waves of 8 rows (4.6 KiB of contiguous cache rows per wave).  Measured
+// on MI355X over all 2048 pages of a cache in a random page order, caches
+// cold and clean: 42.5 us for 32 x 4096 and for 256 x 512 tokens, against
+// 43.5-44.7 us for 4 x 4, 43.5-43.9 for 4 x 8, 44.5-45.5 for 8 x 4 and
+// 46-49 us for 4 x 2 and 4 x 16 (waves x rows per wave).
+constexpr int kPagedWaves = 2;
+constexpr int kPagedRows = 8;
+
 }  // namespace
+
+int launch_gather_dequant_paged(const PagedDequantArgs& a, hipStream_t stream) {
+  constexpr int64_t kTokensPerBlock = int64_t{kPagedWaves} * kPagedRows;
+  const int64_t blocks_x = int64_t{a.max_blocks_per_seq} * 64 / kTokensPerBlock;
+  if (blocks_x > 0x7FFFFFFF || a.num_seqs > 65535) return FP8KV_ERR_SHAPE;
+  void* args[] = {const_cast<const uint8_t**>(&a.kv_cache),
+                  const_cast<const uint8_t**>(&a.kv_scale),
+                  const_cast<const int32_t**>(&a.block_table),
+                  const_cast<const int32_t**>(&a.seq_lens),
+                  const_cast<const int64_t**>(&a.out_offsets),
+                  const_cast<uint16_t**>(&a.out),
+                  const_cast<int32_t*>(&a.max_blocks_per_seq),
+                  const_cast<int64_t*>(&a.num_pages),
+                  const_cast<int64_t*>(&a.num_rows)};
+  hipError_t err = hipLaunchKernel(
+      reinterpret_cast<const void*>(
+          &kv_cache_gather_dequant_paged_kernel<kPagedWaves, kPagedRows>),
+      dim3(static_cast<uint32_t>(blocks_x), static_cast<uint32_t>(a.num_seqs)),
+      dim3(kPagedWaves * 64), args, 0, stream);
+  return err == hipSuccess ? FP8KV_OK : FP8KV_ERR_LAUNCH;
+}
 
 int launch_gather_dequant(const DequantArgs& a, hipStream_t stream) {
   const int64_t rows_per_block = static_cast<int64_t>(kDequantWaves) * kDequantRows;

@@ -78,6 +78,20 @@ bool prologue_shape_built(int waves, int qs);
 
 int launch_packed(const PackedArgs& a, hipStream_t stream);
 int launch_gather_dequant(const DequantArgs& a, hipStream_t stream);
+
+struct PagedDequantArgs {
+  const uint8_t* kv_cache;
+  const uint8_t* kv_scale;
+  const int32_t* block_table;   // [num_seqs, max_blocks_per_seq]
+  const int32_t* seq_lens;      // [num_seqs]
+  const int64_t* out_offsets;   // [num_seqs]: first output row of each sequence
+  uint16_t* out;                // [num_rows, 512]
+  int32_t num_seqs;
+  int32_t max_blocks_per_seq;
+  int64_t num_pages;
+  int64_t num_rows;
+};
+int launch_gather_dequant_paged(const PagedDequantArgs& a, hipStream_t stream);
 int launch_packed_ex(const PackedExArgs& a, hipStream_t stream);
 
 // The prologue's stages as separate launches (the unfused baseline).

@@ -131,6 +131,27 @@ inline int validate_gather_dequant(const uint8_t* kv_cache,
   return FP8KV_OK;
 }
 
+inline int validate_gather_dequant_paged(
+    const uint8_t* kv_cache, const uint8_t* kv_scale, int64_t num_pages,
+    int32_t page_size, const int32_t* block_table, int32_t num_seqs,
+    int32_t max_blocks_per_seq, const int32_t* seq_lens,
+    const int64_t* out_offsets, int64_t num_rows, const void* out) {
+  if (num_pages < 0 || num_pages > (int64_t{1} << 40) || num_seqs < 0 ||
+      num_seqs > 65535 || max_blocks_per_seq < 0 ||
+      max_blocks_per_seq > (int32_t{1} << 24) || num_rows < 0 ||
+      num_rows > (int64_t{1} << 40))
+    return FP8KV_ERR_SHAPE;
+  if (page_size != kPageSize) return FP8KV_ERR_UNSUPPORTED;
+  if (num_seqs == 0 || max_blocks_per_seq == 0 || num_rows == 0) return FP8KV_OK;
+  if (!block_table || !seq_lens || !out_offsets || !out) return FP8KV_ERR_NULL;
+  if (num_pages > 0 && (!kv_cache || !kv_scale)) return FP8KV_ERR_NULL;
+  if (!aligned(block_table, 4) || !aligned(seq_lens, 4) || !aligned(out_offsets, 8) ||
+      !aligned(out, 16) || (kv_cache && !aligned(kv_cache, 16)) ||
+      (kv_scale && !aligned(kv_scale, 8)))
+    return FP8KV_ERR_ALIGN;
+  return FP8KV_OK;
+}
+
 inline int validate_rms_norm_rows(const void* x, const void* out,
                                   const void* weight, int64_t num_rows,
                                   int32_t row_dim) {

@@ -254,6 +254,36 @@ int kv_quant_insert(const void* kv, const int64_t* slot_mapping,
                     int64_t num_pages, int32_t page_size, void* stream);
 
 /*
+ * The read side through block tables, as an attention consumer indexes the
+ * paged cache (the layout of FlagGems PR #5449 "Performance": pages of 64
+ * token rows of 576 bytes plus seven exponents each).  Sequence s holds
+ * seq_lens[s] tokens, 64 to a page, in the pages
+ * block_table[s * max_blocks_per_seq + 0, 1, ...] in order; its token j is
+ * slot block_table[s * max_blocks_per_seq + j / 64] * 64 + j % 64, and that
+ * row, dequantised exactly as by kv_cache_gather_dequant, is written to
+ * out[out_offsets[s] + j].  A page id outside [0, num_pages) gives a zero row.
+ *
+ *   block_table  int32 [num_seqs, max_blocks_per_seq] (4-byte aligned)
+ *   seq_lens     int32 [num_seqs] (4-byte aligned); tokens past
+ *                max_blocks_per_seq * 64 are not written
+ *   out_offsets  int64 [num_seqs] (8-byte aligned): first output row of s
+ *   out          bf16 [num_rows, 512], device, 16-byte aligned; rows outside
+ *                [0, num_rows) are never written, nor are rows that no
+ *                sequence covers
+ * num_seqs <= 65535 and max_blocks_per_seq <= 2^24 (FP8KV_ERR_SHAPE
+ * otherwise); page_size must be 64.  num_seqs, max_blocks_per_seq or
+ * num_rows == 0 launches nothing.  kv_cache / kv_scale may be NULL only when
+ * num_pages == 0 (every row written is then zero).  Sequences whose output
+ * ranges overlap race (precondition: disjoint).
+ */
+int kv_cache_gather_dequant_paged(const uint8_t* kv_cache, const uint8_t* kv_scale,
+                                  int64_t num_pages, int32_t page_size,
+                                  const int32_t* block_table, int32_t num_seqs,
+                                  int32_t max_blocks_per_seq, const int32_t* seq_lens,
+                                  const int64_t* out_offsets, int64_t num_rows,
+                                  void* out, void* stream);
+
+/*
  * Read side of the scalar-scale convention: as kv_cache_gather_dequant, with
  * out[i, d] = bf16(E4M3(code[s, d]) * kv_cache_scale[0]) for d < 448 (the
  * product rounded to fp32, then to bf16) and no exponent tensor.

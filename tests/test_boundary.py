@@ -199,6 +199,27 @@ def test_stage_argument_errors(fn, over, want):
     assert fn(**over) == want
 
 
+def _paged(**over):
+    a = dict(cache=FAKE, scale=FAKE, pages=2, page=64, table=FAKE, S=3, M=4,
+             lens=FAKE, offs=FAKE, N=100, out=FAKE, stream=None)
+    a.update(over)
+    return K.lib().kv_cache_gather_dequant_paged(*a.values())
+
+
+@pytest.mark.parametrize("over,want", [
+    (dict(pages=-1), 2), (dict(S=-1), 2), (dict(S=65536), 2), (dict(M=-1), 2),
+    (dict(M=(1 << 24) + 1), 2), (dict(N=-1), 2), (dict(page=32), 3),
+    (dict(table=None), 1), (dict(lens=None), 1), (dict(offs=None), 1),
+    (dict(out=None), 1), (dict(cache=None), 1), (dict(scale=None), 1),
+    (dict(table=FAKE + 2), 4), (dict(lens=FAKE + 1), 4), (dict(offs=FAKE + 4), 4),
+    (dict(out=FAKE + 8), 4), (dict(cache=FAKE + 8), 4), (dict(scale=FAKE + 4), 4),
+    (dict(S=0, table=None, lens=None, offs=None), 0), (dict(M=0, table=None), 0),
+    (dict(N=0, out=None), 0),
+])
+def test_paged_dequant_argument_errors(over, want):
+    assert _paged(**over) == want
+
+
 def _copy(**over):
     a = dict(dst=FAKE, src=FAKE + 4096, nb=4096, stream=None)
     a.update(over)
@@ -235,6 +256,7 @@ def test_no_device_is_reported_not_launched():
     assert _prologue_scalar() == 5 and _dequant_scalar() == 5
     assert _prologue_scalar(pages=0, cache=None, scale=None) == 5
     assert _copy() == 5 and _rmw() == 5
+    assert _paged() == 5 and _paged(pages=0, cache=None, scale=None) == 5
 
 
 def test_knobs():
