@@ -64,20 +64,28 @@ def test_packed_and_read_side():
                                  x["kv_weight"], x["cos_sin_cache"], x["positions"],
                                  x["slot_mapping"], cache, scale, x["eps"])
     out = torch.empty((w.num_tokens, 512), dtype=torch.bfloat16, device=DEV)
+    table = torch.arange(w.num_pages, dtype=torch.int32, device=DEV).view(4, -1).contiguous()
+    lens = torch.tensor([100, 0, 64, 3000], dtype=torch.int32, device=DEV)
+    offs = torch.tensor([0, 100, 100, 164], dtype=torch.int64, device=DEV)
+    pout = torch.empty((2000, 512), dtype=torch.bfloat16, device=DEV)
 
     def run():
         K.qk_norm_rope_packed(qkv, pw.num_heads_q, pw.num_heads_k, pw.num_heads_v,
                               pw.head_dim, pw.eps, px["q_weight"], px["k_weight"],
                               px["cos_sin_cache"], True, px["position_ids"])
         K.kv_cache_gather_dequant(cache, scale, x["slot_mapping"], out=out)
+        K.kv_cache_gather_dequant_paged(cache, scale, table, lens, offs, pout)
+    pout.zero_()
     run()
-    ref_qkv, ref_out = qkv.clone(), out.clone()
+    ref_qkv, ref_out, ref_pout = qkv.clone(), out.clone(), pout.clone()
     g = _capture(run)
     for _ in range(REPLAYS):
         qkv.copy_(px["qkv"])
         out.zero_()
+        pout.zero_()
         torch.cuda.synchronize()
         g.replay()
         torch.cuda.synchronize()
         assert torch.equal(qkv, ref_qkv)
         assert torch.equal(out, ref_out)
+        assert torch.equal(pout, ref_pout)

@@ -130,6 +130,18 @@ def test_read_side_and_stages():
     torch.cuda.synchronize()
     assert torch.equal(_guards(b), before)
     assert torch.equal(out, ref)
+    # the block-table read side into a guarded output: the same rows
+    table = torch.arange(16, dtype=torch.int32, device=DEV).view(2, 8)
+    lens = torch.tensor([300, 170], dtype=torch.int32, device=DEV)
+    offs = torch.tensor([0, 300], dtype=torch.int64, device=DEV)
+    pref = torch.zeros((470, 512), dtype=torch.bfloat16, device=DEV)
+    K.kv_cache_gather_dequant_paged(cache, scale, table, lens, offs, pref)
+    b, pout = _guarded(torch.zeros_like(pref))
+    before = _guards(b)
+    K.kv_cache_gather_dequant_paged(cache, scale, table, lens, offs, pout)
+    torch.cuda.synchronize()
+    assert torch.equal(_guards(b), before)
+    assert torch.equal(pout, pref)
     # a separate RMSNorm stage into a guarded output
     nref = K.rms_norm_rows(x["kv"], x["kv_weight"], x["eps"])
     b, nout = _guarded(torch.zeros_like(nref))
