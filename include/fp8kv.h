@@ -327,7 +327,7 @@ void fp8kv_get_tiling(int32_t* waves_per_block, int32_t* slots_per_wave);
 
 /*
  * Measurement aids: the hand-written streaming kernels the prologue's HBM
- * bandwidth is compared with (a bandwidth-bound operator is judged against
+ * bandwidth is compared with (a bandwidth-bound operator is measured against
  * the rate of a plain copy on the same device; FlagGems PR #5449
  * "Performance" reports its kernel as a share of a measured copy peak).
  * Both move one 16-byte vector per lane, 256 lanes per block, with
