@@ -85,15 +85,17 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def measured_traffic():
+def measured_traffic(tiling):
     """HBM bytes per launch from committed rocprofv3 counter runs, if they were
-    taken on the current kernel sources; else None."""
+    taken on the current kernel sources at the tiling in force; else None."""
     try:
         with open(PROFILE_COUNTERS) as f:
             c = json.load(f)
     except (OSError, ValueError):
         return None
     if c.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    if list(c.get("tiling", [])) != list(tiling):
         return None
     return c.get("traffic_bytes_per_launch")
 
@@ -192,6 +194,81 @@ def main():
         torch.cuda.synchronize()
         return [a.elapsed_time(b) / 1e3 for a, b in ev]
 
+    ref_times = {}
+
+    def stream_ref(nbytes, kind):
+        """Median seconds of the library's 16 B/lane reference kernel moving
+        `nbytes` bytes (read + write), each launch after the same flushing
+        read: the in-place RMW over nbytes/2 ("rmw", the access pattern of
+        the in-place operators) or a copy of nbytes/2 ("copy")."""
+        half = max(16, nbytes // 2 // 16 * 16)
+        if (kind, half) not in ref_times:
+            a = torch.zeros(half, dtype=torch.uint8, device=dev)
+            if kind == "rmw":
+                per = time_flushed(lambda: K.stream_rmw(a, 0))
+            else:
+                b = torch.empty_like(a)
+                per = time_flushed(lambda: K.stream_copy(b, a))
+                del b
+            del a
+            torch.cuda.empty_cache()
+            ref_times[(kind, half)] = (statistics.median(per), 2 * half)
+        return ref_times[(kind, half)]
+
+    def annotate(entry, nb, m, kind):
+        """Roofline fields of one workload timed with cold caches: the
+        fraction of the 8 TB/s HBM peak, and the same-size reference kernel
+        (time ratio: 1.0 = as fast as plain streaming of the same bytes)."""
+        r, rb = stream_ref(nb, kind)
+        entry["frac_of_hbm_peak"] = round(nb / m / 1e9 / HBM_PEAK_GBPS, 4)
+        entry["stream_ref"] = {
+            "kernel": "fp8kv_stream_rmw" if kind == "rmw" else "fp8kv_stream_copy",
+            "bytes": rb, "median_us": round(r * 1e6, 2),
+            "gbps": round(rb / r / 1e9, 1), "frac": round(r / m, 4)}
+
+    cpu_on = not (args.quick or args.no_cpu_baseline)
+
+    def oracle_beside(run, total_units, budget=1.5):
+        """CPU-baseline leg for one workload: the oracle, single-threaded, on
+        the first n units of the workload, n sized to about `budget` seconds.
+        run(n) prepares host copies of the inputs (untimed), times the oracle
+        call alone and returns (seconds, algorithmic bytes of the n units)."""
+        n = min(total_units, 4)
+        dt, _ = run(n)
+        n = int(min(total_units, max(n, n * budget / max(dt, 1e-4))))
+        dt, nb = run(n)
+        return {"gbps": round(nb / dt / 1e9, 4), "units": n,
+                "of_units": total_units, "seconds": round(dt, 3), "cores": 1,
+                "kind": "oracle"}
+
+    def dsv4_oracle_run(xx, wl, scalar_scale=None):
+        """run(n) for oracle_beside: the prologue oracle (blockwise, or the
+        scalar-scale convention) on the first n tokens of workload xx."""
+        import numpy as np
+
+        import oracle as O
+        qw, kw = I.bits(xx["q_weight"]), I.bits(xx["kv_weight"])
+        cs = I.bits(xx["cos_sin_cache"])
+
+        def run(n):
+            qh, kvh = I.bits(xx["q"][:n]).copy(), I.bits(xx["kv"][:n]).copy()
+            ph = I.bits(xx["positions"][:n]).copy()
+            sh = I.bits(xx["slot_mapping"][:n]).copy()
+            c = np.full((wl.num_pages, 64, 576), I.CACHE_CANARY, np.uint8)
+            s = np.full((wl.num_pages, 64, 8), I.SCALE_CANARY, np.uint8)
+            written = int(((sh >= 0) & (sh < wl.num_pages * 64)).sum())
+            t0 = time.perf_counter()
+            if scalar_scale is None:
+                O.qnorm_rope_kv_quant_insert(qh, kvh, qw, kw, cs, ph, sh, c, s,
+                                             wl.eps)
+                nb = A.dsv4_bytes(n, wl.num_heads, written)
+            else:
+                O.qnorm_rope_kv_quant_insert_scalar(qh, kvh, qw, kw, cs, ph, sh,
+                                                    c, scalar_scale, wl.eps)
+                nb = A.dsv4_scalar_bytes(n, wl.num_heads, written)
+            return time.perf_counter() - t0, nb
+        return run
+
     def call(x, q, cache, scale):
         K.qnorm_rope_kv_quant_insert(q, x["kv"], x["q_weight"], x["kv_weight"],
                                      x["cos_sin_cache"], x["positions"],
@@ -233,7 +310,7 @@ def main():
     achieved = nbytes / mean_launch / 1e9
     log(f"prefill: {value:.1f} GB/s whole-job, kernel {achieved:.1f} GB/s "
         f"({mean_launch * 1e6:.1f} us/launch), {value / d2d_gbps:.3f} of D2D")
-    traffic = measured_traffic()
+    traffic = measured_traffic(K.get_tiling())
 
     result = {
         "metric": METRIC,
@@ -273,7 +350,7 @@ def main():
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
             "traffic": traffic,
-            "kernel": "dsv4_prologue_kernel (tiled)",
+            "kernel": "dsv4_prologue_kernel<{}, {}, false>".format(*K.get_tiling()),
             "mean_launch_us": round(mean_launch * 1e6, 2),
             "median_launch_us": round(statistics.median(per) * 1e6, 2),
         },
@@ -289,6 +366,7 @@ def main():
     prefill_flushed = {"median_us": round(statistics.median(fper) * 1e6, 1),
                        "min_us": round(min(fper) * 1e6, 1),
                        "gbps": round(nbytes / statistics.median(fper) / 1e9, 1)}
+    annotate(prefill_flushed, nbytes, statistics.median(fper), "rmw")
     log(f"prefill, caches flushed: {prefill_flushed}")
     uper = time_flushed(unfused)
     unfused_prefill = {"median_us": round(statistics.median(uper) * 1e6, 1),
@@ -309,6 +387,10 @@ def main():
     scalar_prefill = {"median_us": round(statistics.median(sper) * 1e6, 1),
                       "min_us": round(min(sper) * 1e6, 1),
                       "gbps": round(sb / statistics.median(sper) / 1e9, 1)}
+    annotate(scalar_prefill, sb, statistics.median(sper), "rmw")
+    if cpu_on:
+        scalar_prefill["oracle"] = oracle_beside(
+            dsv4_oracle_run(x, w, float(sscale.item())), w.num_tokens)
     log(f"scalar-scale prefill: {scalar_prefill}")
     del q, cache, scale, kv_work
 
@@ -395,6 +477,10 @@ def main():
                            "min_us": round(min(per) * 1e6, 1),
                            "gbps": round(nb / m / 1e9, 1),
                            "pct_of_d2d": round(nb / m / 1e9 / d2d_gbps, 4)}
+            annotate(extra[name], nb, m, "rmw")
+            if cpu_on:
+                extra[name]["oracle"] = oracle_beside(dsv4_oracle_run(xx, wl),
+                                                      wl.num_tokens)
             log(f"{name}: {extra[name]}")
             if name == "long64":
                 # read side: every slot of the cache just written, in a
@@ -412,6 +498,18 @@ def main():
                     "rows": int(slots.shape[0]), "bytes": nb,
                     "median_us": round(m * 1e6, 1), "min_us": round(min(per) * 1e6, 1),
                     "gbps": round(nb / m / 1e9, 1)}
+                annotate(extra["dequant_long64"], nb, m, "copy")
+                if cpu_on:
+                    import oracle as O
+                    ch, sch = I.bits(cc), I.bits(ss)
+
+                    def dq_run(n):
+                        sl = I.bits(slots[:n]).copy()
+                        t0 = time.perf_counter()
+                        O.kv_cache_gather_dequant(ch, sch, sl)
+                        return time.perf_counter() - t0, A.dequant_bytes(n, n)
+                    extra["dequant_long64"]["oracle"] = oracle_beside(
+                        dq_run, int(slots.shape[0]))
                 log(f"dequant_long64: {extra['dequant_long64']}")
                 # the same cache read through block tables: 32 sequences of
                 # 4096 tokens over all 2048 pages, pages in a seeded order
@@ -430,6 +528,20 @@ def main():
                     "rows": S * L, "sequences": S, "bytes": nb,
                     "median_us": round(m * 1e6, 1), "min_us": round(min(per) * 1e6, 1),
                     "gbps": round(nb / m / 1e9, 1)}
+                annotate(extra["dequant_paged_long64"], nb, m, "copy")
+                if cpu_on:
+                    import numpy as np
+                    th, lh, oh = I.bits(table), I.bits(lens), I.bits(offs)
+
+                    def dqp_run(n):
+                        o = np.zeros((n * L, 512), np.uint16)
+                        t0 = time.perf_counter()
+                        O.kv_cache_gather_dequant_paged(ch, sch, th[:n], lh[:n],
+                                                        oh[:n], o)
+                        return (time.perf_counter() - t0,
+                                A.dequant_paged_bytes(n * L, n * L,
+                                                      n * (pages // S), n))
+                    extra["dequant_paged_long64"]["oracle"] = oracle_beside(dqp_run, S)
                 log(f"dequant_paged_long64: {extra['dequant_paged_long64']}")
                 del slots, out, table, lens, offs
             del xx, qq, cc, ss
@@ -456,6 +568,10 @@ def main():
                            "gbps": round(nb / m / 1e9, 1),
                            "unfused_median_us": round(um * 1e6, 2),
                            "fusion_speedup": round(um / m, 3)}
+            annotate(extra[name], nb, m, "rmw")
+            if cpu_on:
+                extra[name]["oracle"] = oracle_beside(dsv4_oracle_run(xx, wl),
+                                                      wl.num_tokens)
             log(f"{name}: {extra[name]}")
         # packed at 1 and 17 tokens: launch-bound, reported as latency
         for name in ("packed_t1", "packed_t17"):
@@ -486,6 +602,22 @@ def main():
                                  "bytes": nb, "median_us": round(m * 1e6, 2),
                                  "min_us": round(min(per) * 1e6, 2),
                                  "gbps": round(nb / m / 1e9, 1)}
+        annotate(extra["packed_t8192"], nb, m, "rmw")
+        if cpu_on:
+            import oracle as O
+            pqw, pkw = I.bits(px["q_weight"]), I.bits(px["k_weight"])
+            pcs, ppos = I.bits(px["cos_sin_cache"]), I.bits(px["position_ids"])
+
+            def pk_run(n):
+                qh = I.bits(px["qkv"][:n]).copy()
+                t0 = time.perf_counter()
+                O.qk_norm_rope_packed(qh, pw.num_heads_q, pw.num_heads_k,
+                                      pw.num_heads_v, pw.head_dim, pw.eps, pqw,
+                                      pkw, pcs, ppos[:n].copy())
+                return (time.perf_counter() - t0,
+                        A.packed_bytes(n, pw.num_heads_q, pw.num_heads_k,
+                                       pw.head_dim))
+            extra["packed_t8192"]["oracle"] = oracle_beside(pk_run, pw.num_tokens)
         log(f"packed_t8192: {extra['packed_t8192']}")
         # packed variants the guarded fast path does not cover
         for label, D, R, neox, dt in [("packed_ex_d64_inter_f16", 64, 64, False, torch.float16),
@@ -508,6 +640,24 @@ def main():
                             "median_us": round(m * 1e6, 2),
                             "min_us": round(min(per) * 1e6, 2),
                             "gbps": round(nb / m / 1e9, 1)}
+            annotate(extra[label], nb, m, "rmw")
+            if cpu_on:
+                import numpy as np
+
+                import oracle as O
+
+                def u16(v):  # bf16 or fp16 bit patterns
+                    return v.detach().cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
+                vwh, vcsh, vph = u16(vw), I.bits(vcs), I.bits(vpos)
+
+                def pex_run(n):
+                    qh = u16(vq[:n]).copy()
+                    t0 = time.perf_counter()
+                    O.qk_norm_rope_packed_ex(qh, hq, hk, hv, D, R, neox,
+                                             dt == torch.float16, 1e-6, vwh, vwh,
+                                             vcsh, vph[:n].copy())
+                    return time.perf_counter() - t0, A.packed_bytes(n, hq, hk, D, R)
+                extra[label]["oracle"] = oracle_beside(pex_run, T)
             log(f"{label}: {extra[label]}")
         result["extra"] = extra
 

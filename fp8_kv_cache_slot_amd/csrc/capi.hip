@@ -20,17 +20,19 @@ namespace {
 
 // Programs = num_tokens * (num_heads + 1) below which the small-batch kernel
 // runs (the quantity FlagGems PR #5449 "Dispatch threshold" dispatches on).
-// Measured on MI355X, each launch timed after a cache-flushing read: below
-// ~2k programs both kernels sit on the same ~6.1 us launch floor (within
-// 0.1 us); the tiled kernel is ahead from 2080 programs at 64 heads (32
-// tokens) and from 2064 at 128 heads (16 tokens), by up to 10% in the range
-// to 8k programs, so one program count serves both head counts.
+// Below ~2k programs every shape sits on the same ~6.1 us launch floor.
 constexpr int64_t kDefaultThreshold = 2048;
-// Tiled shape: 4 waves per block, 2 Q heads per wave.  2x2, 4x2 and 8x2 all
-// reach ~6.1-6.2 TB/s on the large workloads; 4x2 is the most even across
-// 32768x64, 131072x64, 32768x128 and the mid-size (128..2048 token) range.
-constexpr int kDefaultWaves = 4;
-constexpr int kDefaultSlots = 2;
+// Tiled shape: one wave per block, one Q head per wave, which is also the
+// small-batch shape, so by default both sides of the threshold launch the
+// same kernel.  Measured on MI355X, each launch after a cache-flushing read:
+// 672 us at 32768x64, 1322 us at 32768x128 and 2686 us at 131072x64, against
+// 688-690, 1379-1385 and 2792-2825 us for the best multi-head shapes (2x2,
+// 4x2, 8x2) and 710-713 / 1388-1399 / 2843-2893 us for 2-8 waves of one
+// head per block; from 32 to 2048 tokens at 64 and 128 heads the shapes are
+// within +-0.3 us of each other in no consistent order.  A block of one wave
+// is scheduled as soon as any wave slot of a CU frees up.
+constexpr int kDefaultWaves = 1;
+constexpr int kDefaultSlots = 1;
 
 // The threshold in force when the library loads: FP8KV_DISPATCH_THRESHOLD
 // if it holds a non-negative decimal integer, else the built-in default.

@@ -100,13 +100,15 @@ __attribute__((amdgpu_waves_per_eu(8, 8))) qk_norm_rope_packed_kernel(
   }
 }
 
-// 12 heads per wave: the 16 Q + 8 K heads of a token take two waves.
-// Measured on MI355X with cold caches (16/8/8 heads of 128): at 8192 tokens
-// 26.0 us, against 27.3 us for one wave of 24 heads (83 VGPRs, five waves per
-// SIMD) and 27.5 us with the position read before the head loads; at 1 and
-// 17 tokens 6.7 and 7.0 us against 7.7 and 7.9 us.  At 65536 tokens the
-// position-first order was faster (141 against 151 us).
-constexpr int kPackedWaves = 4;
+// 12 heads per wave, one wave per block: the 16 Q + 8 K heads of a token
+// take two single-wave blocks.  Measured on MI355X with cold caches (16/8/8
+// heads of 128) at 8192 tokens: 23.8 us with one wave per block, against 24.9
+// with two, 25.3-25.5 with four, 26.0 with eight and 28.3 with sixteen; with
+// one wave per block, 8 heads per wave took 25.6 us, 16 heads 25.9 us and all
+// 24 heads in one wave 34.7 us (register-limited).  At 17 tokens 6.7 us
+// against 7.0 us with four waves per block.  With four waves per block the
+// position read before the head loads cost 1.5 us at 8192 tokens (27.5 us).
+constexpr int kPackedWaves = 1;
 constexpr int kPackedUnroll = 3;
 
 }  // namespace

@@ -317,8 +317,9 @@ int64_t fp8kv_get_dispatch_threshold(void);
 
 /*
  * Tiling of the tiled prologue kernel: waves (of 64 lanes) per block and
- * Q slots per wave.  The built-in default is the measured best on MI355X;
- * other instantiated shapes exist for measurement.  (0, 0) restores the
+ * Q slots per wave.  The built-in default (1, 1) is the measured best on
+ * MI355X and equals the small-batch shape; the other instantiated shapes
+ * exist for measurement.  (0, 0) restores the
  * default.  Returns FP8KV_ERR_UNSUPPORTED, and changes nothing, for a shape
  * that is not built.  Process-wide.
  */
@@ -330,7 +331,7 @@ void fp8kv_get_tiling(int32_t* waves_per_block, int32_t* slots_per_wave);
  * bandwidth is compared with (a bandwidth-bound operator is measured against
  * the rate of a plain copy on the same device; FlagGems PR #5449
  * "Performance" reports its kernel as a share of a measured copy peak).
- * Both move one 16-byte vector per lane, 256 lanes per block, with
+ * Both move one 16-byte vector per lane, one 64-lane wave per block, with
  * non-temporal loads and stores; neither is part of the prologue.
  *
  *   fp8kv_stream_copy  dst[0:bytes) = src[0:bytes)
