@@ -11,9 +11,8 @@
 // code bytes of dims 8l..8l+7 with v_cvt_pk_f32_fp8, scales them exactly by
 // the block's power of two with v_ldexp and packs with v_cvt_pk_bf16_f32;
 // lanes 56..63 pass the 128 stored rotary bytes through.  Rows come in groups
-// of RS, and each wave loops over its share of the groups with the loads of
-// the next group in flight while the current one is stored (see the kernel).
-// The output is written non-temporally.
+// of RS consecutive rows per wave (see the kernels).  The output is written
+// non-temporally.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -102,109 +101,55 @@ __device__ __forceinline__ void store_rows(const Rows<RS>& d, const int64_t* s,
   }
 }
 
-// A VALU copy (DPP move with the identity lane pattern): the result is
-// defined by an ALU instruction, not by the load that produced the source.
-__device__ __forceinline__ uint32_t valu_copy(uint32_t x) {
-  return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(
-      0, static_cast<int>(x), 0xE4, 0xF, 0xF, false));
-}
-
 // SCALAR: the scalar-scale convention, out = E4M3(code) * scalar_scale[0]
 // (rounded once to fp32, then to bf16) and no exponent bytes are read.
 //
-// The gather is a chain of two dependent loads (slot, then row), so the work
-// is pipelined inside each wave.  Wave w of the grid takes the row groups
-// w, w + stride, w + 2 stride, ... (stride = waves in the grid; the grid is
-// capped at about eight waves per SIMD).  The slots of 64 / RS consecutive
-// groups of the wave (a batch) arrive with one vector load, lane L holding
-// row L % RS of group L / RS, and are read out with v_readlane; the next
-// batch is loaded while the current one is processed.  Inside a batch the
-// rows of group k + 1 are loaded before group k is dequantised and stored,
-// into two row buffers used in turn (the loop is unrolled by two, so no
-// buffer is copied while its loads are in flight).  No load sits behind a
-// branch, which lets the compiler count outstanding loads exactly instead of
-// waiting for all of them.
-template <int WAVES, int RS, bool SCALAR>
-__global__ void __launch_bounds__(WAVES * 64) kv_cache_gather_dequant_kernel(
+// The gather is a chain of two dependent loads: the slots, then the rows.
+// Each one-wave block takes one group of RS consecutive rows: the RS slot
+// indices are wave-uniform (one scalar load), then every lane issues the
+// group's row loads with no branch in front of them, and the rows are
+// dequantised and stored.  Many small one-shot blocks keep enough groups in
+// flight to hide the two round trips.  Measured on MI355X over all 131072
+// slots of a 2048-page cache in random order, caches cold and clean: 41.9 us
+// with 4 rows per one-wave block, against 43.6 us with 2 rows, 42.8 with 8,
+// 52.2 with 1, 42.3 with two waves of 4 rows and 44.1 with four waves of 2;
+// and against 43.9 us for a persistent form in which each wave looped over
+// its share of the groups with the next group's loads in flight.
+template <int RS, bool SCALAR>
+__global__ void __launch_bounds__(64) kv_cache_gather_dequant_kernel(
     const uint8_t* __restrict__ kv_cache, const uint8_t* __restrict__ kv_scale,
     const float* __restrict__ scalar_scale, const int64_t* __restrict__ slots,
     uint16_t* __restrict__ out, int32_t num_rows, int64_t num_cache_slots) {
-  constexpr int GPB = 64 / RS;  // groups per slot batch
   const int lane = lane_id();
-  const int32_t num_groups = (num_rows + RS - 1) / RS;
-  const int32_t stride = static_cast<int32_t>(gridDim.x) * WAVES;
-  const int32_t w = static_cast<int32_t>(blockIdx.x) * WAVES + wave_id();
-  if (w >= num_groups) return;
-  const int32_t n_my = (num_groups - 1 - w) / stride + 1;  // groups of this wave
-
+  const int32_t grp = static_cast<int32_t>(blockIdx.x);
+  if (grp * RS >= num_rows) return;
   if (num_cache_slots <= 0) {  // a cache without pages: every row is zero
     const u32x4_t z = {0u, 0u, 0u, 0u};
-    for (int32_t q = 0; q < n_my; ++q) {
 #pragma unroll
-      for (int r = 0; r < RS; ++r) {
-        const int32_t i = (w + q * stride) * RS + r;
-        if (i < num_rows) store16<true>(out + static_cast<int64_t>(i) * 512 + lane * 8, z);
-      }
+    for (int r = 0; r < RS; ++r) {
+      const int32_t i = grp * RS + r;
+      if (i < num_rows) store16<true>(out + static_cast<int64_t>(i) * 512 + lane * 8, z);
     }
     return;
+  }
+  // Rows past the last one re-read the last slot (in bounds) and are not
+  // stored.
+  int64_t s[RS];
+#pragma unroll
+  for (int r = 0; r < RS; ++r) {
+    int32_t i = grp * RS + r;
+    if (i > num_rows - 1) i = num_rows - 1;
+    s[r] = slots[i];
   }
   // with pages, the scalar scale pointer is a checked device pointer
   float fs = 1.0f;
   if constexpr (SCALAR) fs = *scalar_scale;
-
-  // Slot batch b: lane L loads the slot of row L % RS of this wave's group
-  // b * GPB + L / RS.  Indices past the last row re-read the last slot (in
-  // bounds); such rows are never stored.
-  auto load_batch = [&](int32_t b) {
-    const int64_t grp = w + (static_cast<int64_t>(b) * GPB + lane / RS) * stride;
-    int64_t i = grp * RS + lane % RS;
-    if (i > num_rows - 1) i = num_rows - 1;
-    return *reinterpret_cast<const u32x2_t*>(slots + i);
-  };
-  auto slots_of = [&](const u32x2_t& cb, int32_t k, int64_t* s) {
-#pragma unroll
-    for (int r = 0; r < RS; ++r) {
-      const uint32_t lo = __builtin_amdgcn_readlane(static_cast<int>(cb[0]), k * RS + r);
-      const uint32_t hi = __builtin_amdgcn_readlane(static_cast<int>(cb[1]), k * RS + r);
-      s[r] = static_cast<int64_t>((static_cast<uint64_t>(hi) << 32) | lo);
-    }
-  };
-
-  const int32_t n_batches = (n_my + GPB - 1) / GPB;
-  u32x2_t nb = load_batch(0);
-  for (int32_t b = 0; b < n_batches; ++b) {
-    const u32x2_t cb = {valu_copy(nb[0]), valu_copy(nb[1])};
-    nb = load_batch(b + 1 < n_batches ? b + 1 : b);  // the last batch re-reads itself
-    const int32_t q0 = b * GPB;
-    const int32_t cnt = n_my - q0 < GPB ? n_my - q0 : GPB;  // groups in this batch
-    Rows<RS> A, B;
-    int64_t sa[RS], sb[RS];
-    slots_of(cb, 0, sa);
-    load_rows<RS, SCALAR>(kv_cache, kv_scale, sa, num_cache_slots, lane, A);
-    for (int32_t k = 0; k < cnt; k += 2) {
-      // group k + 1 (the last group again when there is none: loaded, not stored)
-      slots_of(cb, k + 1 < cnt ? k + 1 : k, sb);
-      load_rows<RS, SCALAR>(kv_cache, kv_scale, sb, num_cache_slots, lane, B);
-      store_rows<RS, SCALAR>(A, sa, fs, out, w + (q0 + k) * stride, num_rows,
-                             num_cache_slots, lane);
-      if (k + 1 >= cnt) break;
-      slots_of(cb, k + 2 < cnt ? k + 2 : k + 1, sa);
-      load_rows<RS, SCALAR>(kv_cache, kv_scale, sa, num_cache_slots, lane, A);
-      store_rows<RS, SCALAR>(B, sb, fs, out, w + (q0 + k + 1) * stride, num_rows,
-                             num_cache_slots, lane);
-    }
-  }
+  Rows<RS> d;
+  load_rows<RS, SCALAR>(kv_cache, kv_scale, s, num_cache_slots, lane, d);
+  store_rows<RS, SCALAR>(d, s, fs, out, grp, num_rows, num_cache_slots, lane);
 }
 
-// 4 rows per group, at most 1024 blocks of 4 waves (four waves per SIMD of
-// the 256 CUs, each with two groups = 8 rows in flight).  Measured on MI355X
-// over all 131072 slots of a 2048-page cache, caches cold and clean: 43.9 us
-// in random slot order and 42.8 us in page order, against 50.9 / 51.0 us for
-// one group of 2 rows per wave without the loop; 2 rows per group and 2048 or
-// 4096 blocks came within 2-3%.
-constexpr int kDequantWaves = 4;
 constexpr int kDequantRows = 4;
-constexpr int64_t kDequantMaxBlocks = 1024;
 
 // The read side through block tables, as an attention consumer indexes the
 // cache: token j of sequence s sits in slot
@@ -306,11 +251,10 @@ int launch_gather_dequant_paged(const PagedDequantArgs& a, hipStream_t stream) {
 }
 
 int launch_gather_dequant(const DequantArgs& a, hipStream_t stream) {
-  const int64_t rows_per_block = static_cast<int64_t>(kDequantWaves) * kDequantRows;
-  int64_t blocks = (static_cast<int64_t>(a.num_rows) + rows_per_block - 1) /
-                   rows_per_block;
-  if (blocks > kDequantMaxBlocks) blocks = kDequantMaxBlocks;
-  if (a.num_rows > 0x7FFFFFFF - kDequantRows) return FP8KV_ERR_SHAPE;  // row indices fit int32
+  // row indices (and grp * RS + RS - 1) fit int32
+  if (a.num_rows > 0x7FFFFFFF - kDequantRows) return FP8KV_ERR_SHAPE;
+  const int64_t blocks = (static_cast<int64_t>(a.num_rows) + kDequantRows - 1) /
+                         kDequantRows;
   void* args[] = {const_cast<const uint8_t**>(&a.kv_cache),
                   const_cast<const uint8_t**>(&a.kv_scale),
                   const_cast<const float**>(&a.scalar_scale),
@@ -321,12 +265,11 @@ int launch_gather_dequant(const DequantArgs& a, hipStream_t stream) {
   const void* fn =
       a.scalar
           ? reinterpret_cast<const void*>(
-                &kv_cache_gather_dequant_kernel<kDequantWaves, kDequantRows, true>)
+                &kv_cache_gather_dequant_kernel<kDequantRows, true>)
           : reinterpret_cast<const void*>(
-                &kv_cache_gather_dequant_kernel<kDequantWaves, kDequantRows, false>);
-  hipError_t err = hipLaunchKernel(fn,
-      dim3(static_cast<uint32_t>(blocks)), dim3(kDequantWaves * 64), args, 0,
-      stream);
+                &kv_cache_gather_dequant_kernel<kDequantRows, false>);
+  hipError_t err = hipLaunchKernel(fn, dim3(static_cast<uint32_t>(blocks)),
+                                   dim3(64), args, 0, stream);
   return err == hipSuccess ? FP8KV_OK : FP8KV_ERR_LAUNCH;
 }
 

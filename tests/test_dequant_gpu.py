@@ -85,10 +85,10 @@ def test_full_size_permutation_of_long_cache():
 
 
 def test_many_rows_per_wave():
-    # 600,001 rows from a 256-slot cache (slots repeat; some are invalid):
-    # beyond 524,288 rows every wave of the capped grid walks more than one
-    # batch of slots.  The oracle decodes each distinct slot once; a repeated
-    # slot has the same row by definition, an invalid one a zero row.
+    # 600,001 rows from a 256-slot cache (slots repeat; some are invalid): a
+    # grid of 150,001 blocks whose last group is partial (one row).  The
+    # oracle decodes each distinct slot once; a repeated slot has the same row
+    # by definition, an invalid one a zero row.
     cache, scale = _random_cache(4, seed=44)
     rng = np.random.default_rng(45)
     slots = rng.integers(-3, 4 * 64 + 3, 600_001).astype(np.int64)

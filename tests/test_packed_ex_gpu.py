@@ -71,6 +71,23 @@ def test_variants(D, R, neox, dtype):
                f"D={D} R={R} neox={neox} {dtype} T={T} heads={hq},{hk},{hv}")
 
 
+@pytest.mark.parametrize("D", [64, 128, 256])
+@pytest.mark.parametrize("neox", [True, False], ids=["neox", "inter"])
+def test_partial_access_in_the_last_wave_of_a_token(D, neox):
+    # 7 + 6 = 13 Q/K heads: at every head width the token's last wave has an
+    # access whose upper head slots do not exist (re-read head 0, not stored);
+    # at D=128 and D=256 a token spans several waves.  777 tokens.
+    hq, hk, hv, T, R = 7, 6, 3, 777, D // 2
+    for dtype in (torch.bfloat16, torch.float16):
+        qkv, qw, kw, cs, pos = _make(T, hq, hk, hv, D, R, dtype, seed=95 + D)
+        out = qkv.clone()
+        K.qk_norm_rope_packed_ex(out, hq, hk, hv, D, 1e-6, qw, kw, cs, neox, pos,
+                                 rotary_dim=R)
+        torch.cuda.synchronize()
+        _check(qkv, out, hq, hk, hv, D, R, neox, dtype, qw, kw, cs, pos,
+               f"D={D} R={R} neox={neox} {dtype} T={T} heads=7,6,3")
+
+
 def test_no_rotation_and_large_token_count():
     qkv, qw, kw, cs, pos = _make(2048, 16, 8, 8, 128, 0, torch.float16, seed=91)
     out = qkv.clone()

@@ -134,7 +134,7 @@ def test_read_side(s):
 
 
 def test_read_side_many_rows_per_wave():
-    # as the blockwise test: more than one batch of slots per wave
+    # as the blockwise test: 600,001 rows, the last group partial
     rng = np.random.default_rng(46)
     cache = rng.integers(0, 256, (4, 64, 576), dtype=np.uint8)
     codes = cache[..., :448]
