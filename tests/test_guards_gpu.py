@@ -31,8 +31,27 @@ def _guards(buf):
     return torch.cat([buf[:GUARD_BYTES], buf[-GUARD_BYTES:]]).clone()
 
 
+@pytest.fixture
+def tiling():
+    """Select a prologue tiling for the test (every call through it) and
+    restore the defaults afterwards."""
+    def use(shape):
+        K.set_dispatch_threshold(0 if shape else -1)
+        K.set_tiling(*(shape or (0, 0)))
+    yield use
+    K.set_dispatch_threshold(-1)
+    K.set_tiling(0, 0)
+
+
+# default dispatch (one head per one-wave block) and a multi-head shape
+SHAPES = [None, (4, 2), (8, 4)]
+SHAPE_IDS = ["default", "4x2", "8x4"]
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=SHAPE_IDS)
 @pytest.mark.parametrize("name", ["tiny", "decode"])
-def test_prologue(name):
+def test_prologue(name, shape, tiling):
+    tiling(shape)
     w = I.DSV4_WORKLOADS[name]
     x = I.make_dsv4(w, DEV)
     q0, c0, s0 = x["q"].clone(), x["kv_cache"].clone(), x["kv_scale"].clone()
@@ -52,7 +71,9 @@ def test_prologue(name):
     assert torch.equal(q, q0) and torch.equal(c, c0) and torch.equal(s, s0)
 
 
-def test_scalar_scale_prologue():
+@pytest.mark.parametrize("shape", [None, (4, 2)], ids=["default", "4x2"])
+def test_scalar_scale_prologue(shape, tiling):
+    tiling(shape)
     w = I.DSV4_WORKLOADS["decode"]
     x = I.make_dsv4(w, DEV)
     sc = torch.tensor([0.02], device=DEV)

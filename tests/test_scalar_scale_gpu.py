@@ -14,15 +14,24 @@ from tests import parity as P
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
 SMALL, TILED = 2 ** 63 - 1, 0
+# The scalar-scale prologue is built in two shapes: one head per one-wave
+# block (the small-batch shape and the default tiled shape) and 4 waves x 2
+# heads, reached by selecting that tiling.
+TILED_4X2 = (TILED, (4, 2))
 
 
 @pytest.fixture(autouse=True)
 def _restore():
     yield
     K.set_dispatch_threshold(-1)
+    K.set_tiling(0, 0)
 
 
 def _run(x, s, thr):
+    tiling = (0, 0)
+    if isinstance(thr, tuple):
+        thr, tiling = thr
+    K.set_tiling(*tiling)
     K.set_dispatch_threshold(thr)
     q, cache = x["q"].clone(), x["kv_cache"].clone()
     scale = torch.tensor([s], dtype=torch.float32, device=DEV)
@@ -41,7 +50,8 @@ def _oracle(h, s):
     return q, cache
 
 
-@pytest.mark.parametrize("thr", [SMALL, TILED], ids=["small", "tiled"])
+@pytest.mark.parametrize("thr", [SMALL, TILED, TILED_4X2],
+                         ids=["small", "tiled", "tiled-4x2"])
 def test_worked_example(thr):
     g = golden_case.load()
     h = golden_case.inputs(g)
@@ -58,7 +68,8 @@ def test_worked_example(thr):
 def test_workloads(name, s):
     w = I.DSV4_WORKLOADS[name]
     x = I.make_dsv4(w, DEV)
-    paths = [("small", SMALL), ("tiled", TILED)] if name != "prefill" else [("default", -1)]
+    paths = ([("small", SMALL), ("tiled", TILED), ("tiled-4x2", TILED_4X2)]
+             if name != "prefill" else [("default", -1)])
     if name == "prefill":
         # sampled tokens at full size
         toks = np.array(sorted(set(range(64)) | set(range(w.num_tokens - 64, w.num_tokens)) |
@@ -94,7 +105,7 @@ def test_workloads(name, s):
 
 @pytest.mark.parametrize("heads", [3, 7])
 def test_ragged_heads(heads):
-    # the tiled kernel's last wave of each token holds one head (of two)
+    # in the 4 x 2 shape the last wave of each token holds one head (of two)
     w = I.custom_dsv4(29, heads, seed=3200 + heads, max_position=8192)
     x = I.make_dsv4(w, DEV)
     h = {k: (I.bits(v).copy() if isinstance(v, torch.Tensor) else v)
@@ -103,7 +114,7 @@ def test_ragged_heads(heads):
     rq, rc = _oracle(h, s)
     v = P.valid_slots(h["slot_mapping"], w.num_pages * 64)
     slots = h["slot_mapping"][v]
-    for label, thr in [("small", SMALL), ("tiled", TILED)]:
+    for label, thr in [("small", SMALL), ("tiled", TILED), ("tiled-4x2", TILED_4X2)]:
         q, cache = _run(x, s, thr)
         P.check_bf16(I.bits(q), rq, f"H={heads} {label} q")
         gc = I.bits(cache).reshape(-1, 576)
