@@ -25,7 +25,13 @@
 namespace fp8kv {
 namespace {
 
-constexpr int kWaves = 4;
+// One wave per block, two rows per wave for the RMSNorm stage: the five-launch
+// pipeline took 800 us at 32768 x 64 with this shape on MI355X (caches cold),
+// against 816 us with four waves of two rows, 824 us with one row per
+// one-wave block and 834 us with two waves of one row; within 1 us of each
+// other at 1024 x 64 (38.3-39.5 us).  The baseline is tuned like the fused
+// kernel it is compared with.
+constexpr int kWaves = 1;
 constexpr int kRowsPerWave = 2;
 
 template <int RS>
@@ -76,8 +82,11 @@ __global__ void __launch_bounds__(kWaves * 64) rope_rows_kernel(
   uint16_t* p = x + row * 512 + 448 + j * 8;
   const u32x4_t v = *reinterpret_cast<const u32x4_t*>(p);
   const int64_t t = row / rows_per_token;
-  const int64_t pos = positions[t];
-  if (pos < 0 || pos >= max_position) return;
+  // An out-of-range position turns off the store (row 0's angles are read
+  // instead), so no branch on the loaded position sits behind the row load.
+  const int64_t pos_in = positions[t];
+  const bool ok = pos_in >= 0 && pos_in < max_position;
+  const int64_t pos = ok ? pos_in : 0;
   const f32x4_t c = load16f(cos_sin + pos * 64 + j * 4);
   const f32x4_t s = load16f(cos_sin + pos * 64 + 32 + j * 4);
   float y[8];
@@ -88,9 +97,10 @@ __global__ void __launch_bounds__(kWaves * 64) rope_rows_kernel(
     y[2 * k] = a * c[k] - b * s[k];
     y[2 * k + 1] = b * c[k] + a * s[k];
   }
-  *reinterpret_cast<u32x4_t*>(p) =
-      u32x4_t{pack_bf16(y[0], y[1]), pack_bf16(y[2], y[3]),
-              pack_bf16(y[4], y[5]), pack_bf16(y[6], y[7])};
+  if (ok)
+    *reinterpret_cast<u32x4_t*>(p) =
+        u32x4_t{pack_bf16(y[0], y[1]), pack_bf16(y[2], y[3]),
+                pack_bf16(y[4], y[5]), pack_bf16(y[6], y[7])};
 }
 
 __global__ void __launch_bounds__(kWaves * 64) kv_quant_insert_kernel(
@@ -100,11 +110,13 @@ __global__ void __launch_bounds__(kWaves * 64) kv_quant_insert_kernel(
   const int lane = lane_id();
   const int32_t t = static_cast<int32_t>(blockIdx.x) * kWaves + wave_id();
   if (t >= num_tokens) return;
-  const int64_t slot = slot_mapping[t];
-  if (slot < 0 || slot >= num_cache_slots) return;
+  // The row load goes out with the slot load; a skipped slot turns off the
+  // stores rather than returning in front of the row load.
   float y[8];
   unpack8(load16<true>(kv + static_cast<int64_t>(t) * 512 + lane * 8), y);
-  quantise_store_row(y, lane, kv_cache + slot * 576, kv_scale + slot * 8);
+  const int64_t slot = slot_mapping[t];
+  if (slot >= 0 && slot < num_cache_slots)
+    quantise_store_row(y, lane, kv_cache + slot * 576, kv_scale + slot * 8);
 }
 
 int to_status(hipError_t e) { return e == hipSuccess ? FP8KV_OK : FP8KV_ERR_LAUNCH; }
