@@ -161,7 +161,19 @@ def test_full_size_workloads(name):
     # sampled tokens against the oracle, and at full size the properties the
     # oracle need not recompute: every valid slot written, every other byte
     # untouched.
-    w = I.DSV4_WORKLOADS[name]
+    _check_full_size(I.DSV4_WORKLOADS[name])
+
+
+def test_twice_the_largest_workload():
+    # 262144 tokens x 64 heads: 2^33 q elements (16 GiB), twice the largest
+    # workload, so q offsets, slot rows and block indices all run past 2^32
+    # bytes (4096 pages, every slot written once in a random order).
+    _check_full_size(I.Dsv4Workload("max64", 262144, 64, 131072, 4096, False,
+                                     "uniform", "permutation", 0, 1023))
+
+
+def _check_full_size(w):
+    name = w.name
     _say(f"workload {name} T={w.num_tokens} H={w.num_heads}")
     x = I.make_dsv4(w, DEV)
     q, cache, scale = _run(x)
