@@ -123,12 +123,36 @@ def _check(t: torch.Tensor, name: str, dtype, shape=None):
         raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
 
 
-def _stream(stream) -> int:
+def _device(*tensors) -> torch.device:
+    """The one device every tensor of a call is on (the library launches on
+    the current device, so a pointer from another device must never reach
+    it)."""
+    dev = tensors[0].device
+    for t in tensors[1:]:
+        if t.device != dev:
+            raise ValueError(f"all tensors of a call must be on one device, got "
+                             f"{dev} and {t.device}")
+    return dev
+
+
+def _stream(stream, dev) -> int:
     if stream is None:
-        return torch.cuda.current_stream().cuda_stream
+        return torch.cuda.current_stream(dev).cuda_stream
     if isinstance(stream, torch.cuda.Stream):
+        if stream.device != dev:
+            raise ValueError(f"stream is on {stream.device}, tensors on {dev}")
         return stream.cuda_stream
     return int(stream)
+
+
+def _call(name: str, tensors, stream, *args) -> None:
+    """Call C entry point ``name`` with ``args`` and the stream, with the
+    tensors' device current; raise on a non-zero status."""
+    dev = _device(*tensors)
+    with torch.cuda.device(dev):
+        st = getattr(lib(), name)(*args, _stream(stream, dev))
+    if st:
+        raise Fp8kvError(st, name)
 
 
 def qnorm_rope_kv_quant_insert(q, kv, q_weight, kv_weight, cos_sin_cache,
@@ -156,14 +180,14 @@ def qnorm_rope_kv_quant_insert(q, kv, q_weight, kv_weight, cos_sin_cache,
     if row != ROW_BYTES:
         raise ValueError("kv_cache rows must be 576 bytes")
     _check(kv_scale, "kv_scale", torch.uint8, (pages, page_size, SCALE_BYTES))
-    st = lib().qnorm_rope_kv_quant_insert(
-        q.data_ptr(), kv.data_ptr(), q_weight.data_ptr(), kv_weight.data_ptr(),
-        cos_sin_cache.data_ptr(), positions.data_ptr(), slot_mapping.data_ptr(),
-        kv_cache.data_ptr(), kv_scale.data_ptr(), T, H, D,
-        cos_sin_cache.shape[1], cos_sin_cache.shape[0], pages, page_size,
-        float(eps), _stream(stream))
-    if st:
-        raise Fp8kvError(st, "qnorm_rope_kv_quant_insert")
+    _call("qnorm_rope_kv_quant_insert",
+          (q, kv, q_weight, kv_weight, cos_sin_cache, positions, slot_mapping,
+           kv_cache, kv_scale), stream,
+          q.data_ptr(), kv.data_ptr(), q_weight.data_ptr(), kv_weight.data_ptr(),
+          cos_sin_cache.data_ptr(), positions.data_ptr(), slot_mapping.data_ptr(),
+          kv_cache.data_ptr(), kv_scale.data_ptr(), T, H, D,
+          cos_sin_cache.shape[1], cos_sin_cache.shape[0], pages, page_size,
+          float(eps))
 
 
 def qnorm_rope_kv_quant_insert_scalar_scale(q, kv, q_weight, kv_weight,
@@ -190,14 +214,14 @@ def qnorm_rope_kv_quant_insert_scalar_scale(q, kv, q_weight, kv_weight,
         raise ValueError("kv_cache must be [num_pages, page_size, 576]")
     pages, page_size, _ = kv_cache.shape
     _check(kv_cache_scale, "kv_cache_scale", torch.float32, (1,))
-    st = lib().qnorm_rope_kv_quant_insert_scalar_scale(
-        q.data_ptr(), kv.data_ptr(), q_weight.data_ptr(), kv_weight.data_ptr(),
-        cos_sin_cache.data_ptr(), positions.data_ptr(), slot_mapping.data_ptr(),
-        kv_cache.data_ptr(), kv_cache_scale.data_ptr(), T, H, D,
-        cos_sin_cache.shape[1], cos_sin_cache.shape[0], pages, page_size,
-        float(eps), _stream(stream))
-    if st:
-        raise Fp8kvError(st, "qnorm_rope_kv_quant_insert_scalar_scale")
+    _call("qnorm_rope_kv_quant_insert_scalar_scale",
+          (q, kv, q_weight, kv_weight, cos_sin_cache, positions, slot_mapping,
+           kv_cache, kv_cache_scale), stream,
+          q.data_ptr(), kv.data_ptr(), q_weight.data_ptr(), kv_weight.data_ptr(),
+          cos_sin_cache.data_ptr(), positions.data_ptr(), slot_mapping.data_ptr(),
+          kv_cache.data_ptr(), kv_cache_scale.data_ptr(), T, H, D,
+          cos_sin_cache.shape[1], cos_sin_cache.shape[0], pages, page_size,
+          float(eps))
 
 
 def kv_cache_gather_dequant_scalar_scale(kv_cache, kv_cache_scale, slots,
@@ -215,11 +239,10 @@ def kv_cache_gather_dequant_scalar_scale(kv_cache, kv_cache_scale, slots,
     if out is None:
         out = torch.empty((n, HEAD_DIM), dtype=torch.bfloat16, device=slots.device)
     _check(out, "out", torch.bfloat16, (n, HEAD_DIM))
-    st = lib().kv_cache_gather_dequant_scalar_scale(
-        kv_cache.data_ptr(), kv_cache_scale.data_ptr(), pages, page_size,
-        slots.data_ptr(), n, out.data_ptr(), _stream(stream))
-    if st:
-        raise Fp8kvError(st, "kv_cache_gather_dequant_scalar_scale")
+    _call("kv_cache_gather_dequant_scalar_scale",
+          (kv_cache, kv_cache_scale, slots, out), stream,
+          kv_cache.data_ptr(), kv_cache_scale.data_ptr(), pages, page_size,
+          slots.data_ptr(), n, out.data_ptr())
     return out
 
 
@@ -242,14 +265,12 @@ def qk_norm_rope_packed(qkv, num_heads_q: int, num_heads_k: int,
     if cos_sin_cache.dim() != 2 or cos_sin_cache.shape[1] != head_dim:
         raise ValueError("cos_sin_cache must be [max_position, head_dim]")
     _check(position_ids, "position_ids", torch.int64, (T,))
-    st = lib().qk_norm_rope_packed(
-        qkv.data_ptr(), T, num_heads_q, num_heads_k, num_heads_v, head_dim,
-        float(eps), q_weight.data_ptr(), k_weight.data_ptr(),
-        cos_sin_cache.data_ptr(), int(bool(is_neox)), position_ids.data_ptr(),
-        int(forced_token_heads_per_warp), cos_sin_cache.shape[0],
-        _stream(stream))
-    if st:
-        raise Fp8kvError(st, "qk_norm_rope_packed")
+    _call("qk_norm_rope_packed",
+          (qkv, q_weight, k_weight, cos_sin_cache, position_ids), stream,
+          qkv.data_ptr(), T, num_heads_q, num_heads_k, num_heads_v, head_dim,
+          float(eps), q_weight.data_ptr(), k_weight.data_ptr(),
+          cos_sin_cache.data_ptr(), int(bool(is_neox)), position_ids.data_ptr(),
+          int(forced_token_heads_per_warp), cos_sin_cache.shape[0])
 
 
 def qk_norm_rope_packed_ex(qkv, num_heads_q: int, num_heads_k: int,
@@ -275,14 +296,13 @@ def qk_norm_rope_packed_ex(qkv, num_heads_q: int, num_heads_k: int,
     if cos_sin_cache.dim() != 2 or cos_sin_cache.shape[1] != R:
         raise ValueError("cos_sin_cache must be [max_position, rotary_dim]")
     _check(position_ids, "position_ids", torch.int64, (T,))
-    st = lib().qk_norm_rope_packed_ex(
-        qkv.data_ptr(), T, num_heads_q, num_heads_k, num_heads_v, head_dim,
-        float(eps), q_weight.data_ptr(), k_weight.data_ptr(),
-        cos_sin_cache.data_ptr() if R else None, int(bool(is_neox)),
-        position_ids.data_ptr(), R, dtypes[qkv.dtype],
-        max(1, cos_sin_cache.shape[0]), _stream(stream))
-    if st:
-        raise Fp8kvError(st, "qk_norm_rope_packed_ex")
+    _call("qk_norm_rope_packed_ex",
+          (qkv, q_weight, k_weight, cos_sin_cache, position_ids), stream,
+          qkv.data_ptr(), T, num_heads_q, num_heads_k, num_heads_v, head_dim,
+          float(eps), q_weight.data_ptr(), k_weight.data_ptr(),
+          cos_sin_cache.data_ptr() if R else None, int(bool(is_neox)),
+          position_ids.data_ptr(), R, dtypes[qkv.dtype],
+          max(1, cos_sin_cache.shape[0]))
 
 
 def kv_cache_gather_dequant(kv_cache, kv_scale, slots, out=None,
@@ -301,11 +321,9 @@ def kv_cache_gather_dequant(kv_cache, kv_scale, slots, out=None,
     if out is None:
         out = torch.empty((n, HEAD_DIM), dtype=torch.bfloat16, device=slots.device)
     _check(out, "out", torch.bfloat16, (n, HEAD_DIM))
-    st = lib().kv_cache_gather_dequant(
-        kv_cache.data_ptr(), kv_scale.data_ptr(), pages, page_size,
-        slots.data_ptr(), n, out.data_ptr(), _stream(stream))
-    if st:
-        raise Fp8kvError(st, "kv_cache_gather_dequant")
+    _call("kv_cache_gather_dequant", (kv_cache, kv_scale, slots, out), stream,
+          kv_cache.data_ptr(), kv_scale.data_ptr(), pages, page_size,
+          slots.data_ptr(), n, out.data_ptr())
     return out
 
 
@@ -329,12 +347,11 @@ def kv_cache_gather_dequant_paged(kv_cache, kv_scale, block_table, seq_lens,
     _check(out, "out", torch.bfloat16)
     if out.dim() != 2 or out.shape[1] != HEAD_DIM:
         raise ValueError("out must be [N, 512]")
-    st = lib().kv_cache_gather_dequant_paged(
-        kv_cache.data_ptr(), kv_scale.data_ptr(), pages, page_size,
-        block_table.data_ptr(), S, M, seq_lens.data_ptr(), out_offsets.data_ptr(),
-        out.shape[0], out.data_ptr(), _stream(stream))
-    if st:
-        raise Fp8kvError(st, "kv_cache_gather_dequant_paged")
+    _call("kv_cache_gather_dequant_paged",
+          (kv_cache, kv_scale, block_table, seq_lens, out_offsets, out), stream,
+          kv_cache.data_ptr(), kv_scale.data_ptr(), pages, page_size,
+          block_table.data_ptr(), S, M, seq_lens.data_ptr(), out_offsets.data_ptr(),
+          out.shape[0], out.data_ptr())
     return out
 
 
@@ -348,11 +365,9 @@ def rms_norm_rows(x, weight, eps: float = 1e-6, out=None, stream=None):
     if out is None:
         out = torch.empty_like(x)
     _check(out, "out", torch.bfloat16, tuple(x.shape))
-    st = lib().rms_norm_rows(x.data_ptr(), out.data_ptr(), weight.data_ptr(),
-                             x.numel() // HEAD_DIM, HEAD_DIM, float(eps),
-                             _stream(stream))
-    if st:
-        raise Fp8kvError(st, "rms_norm_rows")
+    _call("rms_norm_rows", (x, weight, out), stream,
+          x.data_ptr(), out.data_ptr(), weight.data_ptr(),
+          x.numel() // HEAD_DIM, HEAD_DIM, float(eps))
     return out
 
 
@@ -366,11 +381,10 @@ def rope_rows(x, cos_sin_cache, positions, stream=None) -> None:
     if cos_sin_cache.dim() != 2:
         raise ValueError("cos_sin_cache must be [max_position, 64]")
     _check(positions, "positions", torch.int64, (T,))
-    st = lib().rope_rows(x.data_ptr(), cos_sin_cache.data_ptr(),
-                         positions.data_ptr(), T, R, D, cos_sin_cache.shape[1],
-                         cos_sin_cache.shape[0], _stream(stream))
-    if st:
-        raise Fp8kvError(st, "rope_rows")
+    _call("rope_rows", (x, cos_sin_cache, positions), stream,
+          x.data_ptr(), cos_sin_cache.data_ptr(),
+          positions.data_ptr(), T, R, D, cos_sin_cache.shape[1],
+          cos_sin_cache.shape[0])
 
 
 def kv_quant_insert(kv, slot_mapping, kv_cache, kv_scale, stream=None) -> None:
@@ -386,11 +400,10 @@ def kv_quant_insert(kv, slot_mapping, kv_cache, kv_scale, stream=None) -> None:
         raise ValueError("kv_cache must be [num_pages, page_size, 576]")
     pages, page_size, _ = kv_cache.shape
     _check(kv_scale, "kv_scale", torch.uint8, (pages, page_size, SCALE_BYTES))
-    st = lib().kv_quant_insert(kv.data_ptr(), slot_mapping.data_ptr(),
-                               kv_cache.data_ptr(), kv_scale.data_ptr(), T,
-                               pages, page_size, _stream(stream))
-    if st:
-        raise Fp8kvError(st, "kv_quant_insert")
+    _call("kv_quant_insert", (kv, slot_mapping, kv_cache, kv_scale), stream,
+          kv.data_ptr(), slot_mapping.data_ptr(),
+          kv_cache.data_ptr(), kv_scale.data_ptr(), T,
+          pages, page_size)
 
 
 def unfused_prologue(q, kv, q_weight, kv_weight, cos_sin_cache, positions,
@@ -444,9 +457,8 @@ def stream_copy(dst, src, stream=None) -> None:
     nb = dst.numel() * dst.element_size()
     if src.numel() * src.element_size() != nb:
         raise ValueError("dst and src must have the same byte size")
-    st = lib().fp8kv_stream_copy(dst.data_ptr(), src.data_ptr(), nb, _stream(stream))
-    if st:
-        raise Fp8kvError(st, "stream_copy")
+    _call("fp8kv_stream_copy", (dst, src), stream,
+          dst.data_ptr(), src.data_ptr(), nb)
 
 
 def stream_rmw(buf, mask: int = 0, stream=None) -> None:
@@ -455,7 +467,6 @@ def stream_rmw(buf, mask: int = 0, stream=None) -> None:
     if not (isinstance(buf, torch.Tensor) and buf.device.type == "cuda"
             and buf.is_contiguous()):
         raise ValueError("buf must be a contiguous device tensor")
-    st = lib().fp8kv_stream_rmw(buf.data_ptr(), buf.numel() * buf.element_size(),
-                                int(mask) & 0xFFFFFFFF, _stream(stream))
-    if st:
-        raise Fp8kvError(st, "stream_rmw")
+    _call("fp8kv_stream_rmw", (buf,), stream,
+          buf.data_ptr(), buf.numel() * buf.element_size(),
+          int(mask) & 0xFFFFFFFF)

@@ -310,6 +310,15 @@ def test_binding_rejects_host_tensors():
                                      x["kv_cache"], x["kv_scale"], x["eps"])
 
 
+def test_binding_requires_one_device_per_call():
+    # tensors on two different devices never reach the library (it launches on
+    # the current device); the check runs before any device is touched
+    a, b = torch.zeros(4), torch.zeros(4, device="meta")
+    with pytest.raises(ValueError, match="one device"):
+        K._call("fp8kv_stream_rmw", (a, b), None, 0, 0, 0)
+    assert K._device(a, torch.ones(2)) == a.device
+
+
 def test_byte_accounting_totals():
     # per-token formula applied to each workload's actual slot mapping
     expect = {"tiny": 553_186, "prefill": 4_356_540_416,
