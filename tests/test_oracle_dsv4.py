@@ -290,3 +290,10 @@ def test_kv_normalised_is_the_unrounded_kv_row():
     cs = rng.uniform(-1, 1, (4, 64)).astype(np.float32)
     yc = O.kv_normalised(kv, kw, cs, np.array([3, 1], np.int64), 0.0)
     np.testing.assert_array_equal(yc[:, :448], np.broadcast_to(_val(kw[:448]), (2, 448)))
+    # with a large eps the closed form c / sqrt(c^2 + eps) * w (eps inside the
+    # root, mean over all 512 dims) separates a dropped or misplaced eps
+    for eps in (0.25, 4.0):
+        ye = O.kv_normalised(kv, kw, cs, np.array([3, 1], np.int64), eps)
+        want = 0.75 / np.sqrt(0.75 ** 2 + eps) * _val(kw[:448])
+        np.testing.assert_allclose(ye[:, :448], np.broadcast_to(want, (2, 448)),
+                                   rtol=1e-14, atol=0)

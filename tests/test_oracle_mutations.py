@@ -151,6 +151,63 @@ MUTATIONS = [
      "rotate_pair(&y[2 * i], &y[2 * i + 1], row[half + i], row[i]);"),
     ("packed_ex_fp16_weight_as_bf16", "y[d] = decode(xh[d]) * inv_rms * decode(w[d]);",
      "y[d] = decode(xh[d]) * inv_rms * oracle_bf16_to_double(w[d]);"),
+    ("packed_ex_partial_rotary_short",
+     "      for (int i = 0; i < half; ++i) {\n        if (is_neox)",
+     "      for (int i = 0; i < half - 1; ++i) {\n        if (is_neox)"),
+    ("packed_sin_offset", "    const float* sinv = row + half;",
+     "    const float* sinv = row + half - 1;"),
+    # decoders
+    ("bf16_decode_shift", "uint32_t u = static_cast<uint32_t>(bits) << 16;",
+     "uint32_t u = static_cast<uint32_t>(bits) << 15;"),
+    ("fp16_decode_subnormal", "mag = std::ldexp(static_cast<double>(mant), -24);",
+     "mag = std::ldexp(static_cast<double>(mant), -25);"),
+    ("fp16_decode_bias", "mag = std::ldexp(1.0 + mant / 1024.0, exp_field - 15);",
+     "mag = std::ldexp(1.0 + mant / 1024.0, exp_field - 14);"),
+    ("e4m3_decode_no_nan", "if (exp_field == 0xF && mant == 0x7) return std::nan(\"\");", ""),
+    ("e4m3_encode_bias",
+     "int exp_field = (k - 1) + 7;\n    int mant = static_cast<int>((2.0 * m - 1.0) * 8.0);",
+     "int exp_field = (k - 1) + 8;\n    int mant = static_cast<int>((2.0 * m - 1.0) * 8.0);"),
+    # scalar-scale convention
+    ("scalar_read_divides",
+     "dst[d] = oracle_bf16_rne(oracle_e4m3_decode(row[d]) *\n"
+     "                               static_cast<double>(kv_cache_scale));",
+     "dst[d] = oracle_bf16_rne(oracle_e4m3_decode(row[d]) /\n"
+     "                               static_cast<double>(kv_cache_scale));"),
+    ("scalar_read_rope_bytes_swapped",
+     "          row[kRopeStart + 2 * j] | (row[kRopeStart + 2 * j + 1] << 8));\n  }\n}\n\n"
+     "void oracle_rms_norm_rows",
+     "          row[kRopeStart + 2 * j + 1] | (row[kRopeStart + 2 * j] << 8));\n  }\n}\n\n"
+     "void oracle_rms_norm_rows"),
+    ("scalar_q_uses_kv_weight",
+     "      rms_norm(qh, q_weight, kHeadDim, eps, y);\n"
+     "      for (int i = 0; i < kRopeDim / 2; ++i)\n"
+     "        rotate_pair(&y[kRopeStart + 2 * i], &y[kRopeStart + 2 * i + 1],\n"
+     "                    cosv[i], sinv[i]);\n"
+     "      for (int d = 0; d < kHeadDim; ++d) qh[d] = oracle_bf16_rne(y[d]);\n"
+     "    }\n    const int64_t slot",
+     "      rms_norm(qh, kv_weight, kHeadDim, eps, y);\n"
+     "      for (int i = 0; i < kRopeDim / 2; ++i)\n"
+     "        rotate_pair(&y[kRopeStart + 2 * i], &y[kRopeStart + 2 * i + 1],\n"
+     "                    cosv[i], sinv[i]);\n"
+     "      for (int d = 0; d < kHeadDim; ++d) qh[d] = oracle_bf16_rne(y[d]);\n"
+     "    }\n    const int64_t slot"),
+    ("scalar_drops_sign",
+     "dst[d] = oracle_e4m3_encode(y[d] / static_cast<double>(kv_cache_scale));",
+     "dst[d] = oracle_e4m3_encode(std::fabs(y[d]) / static_cast<double>(kv_cache_scale));"),
+    # read side through block tables, unrounded KV, separate quantiser
+    ("paged_page_zero_invalid",
+     "const int64_t slot = page < 0 || page >= num_pages ? -1 : page * kPageSize + j % kPageSize;",
+     "const int64_t slot = page <= 0 || page >= num_pages ? -1 : page * kPageSize + j % kPageSize;"),
+    ("paged_row_bound", "if (row < 0 || row >= num_rows) continue;",
+     "if (row < 0 || row >= num_rows - 1) continue;"),
+    ("kv_normalised_eps_dropped",
+     "    kv_head(kv + t * kHeadDim, kv_weight, row, row + kRopeDim / 2, eps,\n"
+     "            y_out + t * kHeadDim);",
+     "    kv_head(kv + t * kHeadDim, kv_weight, row, row + kRopeDim / 2, 0.0,\n"
+     "            y_out + t * kHeadDim);"),
+    ("quant_insert_stage_bound",
+     "    if (slot < 0 || slot >= num_slots) continue;\n    for (int d = 0; d < kHeadDim; ++d) y[d]",
+     "    if (slot < 0 || slot >= num_slots - 1) continue;\n    for (int d = 0; d < kHeadDim; ++d) y[d]"),
 ]
 
 # Runs the pin tests in a fresh interpreter with the oracle package pointed at
