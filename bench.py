@@ -269,6 +269,32 @@ def main():
             return time.perf_counter() - t0, nb
         return run
 
+    def unfused_oracle_run(xx, wl):
+        """run(n) for oracle_beside: the oracle's separate stages composed as
+        the unfused launches are (RMSNorm of q and of kv, RoPE of both,
+        quantise+insert), on the first n tokens; bytes are the operator's."""
+        import numpy as np
+
+        import oracle as O
+        qw, kw = I.bits(xx["q_weight"]), I.bits(xx["kv_weight"])
+        cs = I.bits(xx["cos_sin_cache"])
+
+        def run(n):
+            qh, kvh = I.bits(xx["q"][:n]).copy(), I.bits(xx["kv"][:n]).copy()
+            ph = I.bits(xx["positions"][:n]).copy()
+            sh = I.bits(xx["slot_mapping"][:n]).copy()
+            c = np.full((wl.num_pages, 64, 576), I.CACHE_CANARY, np.uint8)
+            s = np.full((wl.num_pages, 64, 8), I.SCALE_CANARY, np.uint8)
+            written = int(((sh >= 0) & (sh < wl.num_pages * 64)).sum())
+            t0 = time.perf_counter()
+            qn = O.rms_norm_rows(qh, qw, wl.eps)
+            kn = O.rms_norm_rows(kvh, kw, wl.eps)
+            O.rope_rows(qn, cs, ph)
+            O.rope_rows(kn.reshape(n, 1, 512), cs, ph)
+            O.kv_quant_insert(kn, sh, c, s)
+            return time.perf_counter() - t0, A.dsv4_bytes(n, wl.num_heads, written)
+        return run
+
     def call(x, q, cache, scale):
         K.qnorm_rope_kv_quant_insert(q, x["kv"], x["q_weight"], x["kv_weight"],
                                      x["cos_sin_cache"], x["positions"],
@@ -374,6 +400,9 @@ def main():
                        "fused_median_us": round(statistics.median(fper) * 1e6, 1),
                        "fusion_speedup": round(statistics.median(uper) /
                                                statistics.median(fper), 3)}
+    if cpu_on:
+        unfused_prefill["oracle"] = oracle_beside(unfused_oracle_run(x, w),
+                                                  w.num_tokens)
     log(f"unfused prefill: {unfused_prefill}")
 
     # ---- the scalar-scale cache convention on the same workload ----------
