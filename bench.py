@@ -540,6 +540,26 @@ def main():
                     extra["dequant_long64"]["oracle"] = oracle_beside(
                         dq_run, int(slots.shape[0]))
                 log(f"dequant_long64: {extra['dequant_long64']}")
+                # the scalar-scale read side over the same cache and slots
+                rscale = torch.tensor([0.0173], dtype=torch.float32, device=dev)
+                per = time_flushed(lambda: K.kv_cache_gather_dequant_scalar_scale(
+                    cc, rscale, slots, out))
+                m = statistics.median(per)
+                nb = A.dequant_scalar_bytes(slots.shape[0], slots.shape[0])
+                extra["dequant_scalar_long64"] = {
+                    "rows": int(slots.shape[0]), "bytes": nb,
+                    "median_us": round(m * 1e6, 1), "min_us": round(min(per) * 1e6, 1),
+                    "gbps": round(nb / m / 1e9, 1)}
+                annotate(extra["dequant_scalar_long64"], nb, m, "copy")
+                if cpu_on:
+                    def dqs_run(n):
+                        sl = I.bits(slots[:n]).copy()
+                        t0 = time.perf_counter()
+                        O.kv_cache_gather_dequant_scalar(ch, 0.0173, sl)
+                        return time.perf_counter() - t0, A.dequant_scalar_bytes(n, n)
+                    extra["dequant_scalar_long64"]["oracle"] = oracle_beside(
+                        dqs_run, int(slots.shape[0]))
+                log(f"dequant_scalar_long64: {extra['dequant_scalar_long64']}")
                 # the same cache read through block tables: 32 sequences of
                 # 4096 tokens over all 2048 pages, pages in a seeded order
                 S = 32

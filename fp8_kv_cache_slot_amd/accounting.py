@@ -8,7 +8,7 @@ the 64 bf16 rotary dims (128 B) and 7 exponent bytes; plus both weight vectors
 once (2 * 1024 B).
 
 The scalar-scale cache convention moves the same bytes minus the 7
-exponent bytes per written token (plus one 4-byte scale).
+exponent bytes per written token or read row (plus one 4-byte scale).
 
 Cache read side (gather + dequantise), per output row: the slot index (8 B)
 and the bf16 row written (1024 B); per row whose slot is valid also the 576
@@ -63,3 +63,9 @@ def dequant_paged_bytes(num_rows: int, num_valid: int, table_entries: int,
 
 def dsv4_scalar_bytes(num_tokens: int, num_heads: int, num_written: int) -> int:
     return dsv4_bytes(num_tokens, num_heads, num_written) - 7 * num_written + 4
+
+
+def dequant_scalar_bytes(num_rows: int, num_valid: int) -> int:
+    """Scalar-scale read side: as the blockwise one without the 7 exponent
+    bytes per valid row, plus the one 4-byte scale."""
+    return dequant_bytes(num_rows, num_valid) - 7 * num_valid + 4

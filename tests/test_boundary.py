@@ -319,6 +319,13 @@ def test_binding_requires_one_device_per_call():
     assert K._device(a, torch.ones(2)) == a.device
 
 
+def test_scalar_read_side_bytes():
+    # the blockwise count without the 7 exponent bytes per valid row, plus
+    # the 4-byte scale
+    assert A.dequant_scalar_bytes(10, 7) == A.dequant_bytes(10, 7) - 49 + 4
+    assert A.dequant_scalar_bytes(131072, 131072) == 131072 * (8 + 1024 + 576) + 4
+
+
 def test_byte_accounting_totals():
     # per-token formula applied to each workload's actual slot mapping
     expect = {"tiny": 553_186, "prefill": 4_356_540_416,
