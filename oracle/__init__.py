@@ -69,6 +69,9 @@ def _load():
     lib.oracle_kv_cache_gather_dequant_scalar.argtypes = [
         P, ctypes.c_float, P, I64, I64, P]
     lib.oracle_kv_cache_gather_dequant_scalar.restype = None
+    lib.oracle_kv_cache_gather_dequant_paged_scalar.argtypes = [
+        P, ctypes.c_float, I64, P, I32, I32, P, P, I64, P]
+    lib.oracle_kv_cache_gather_dequant_paged_scalar.restype = None
     lib.oracle_kv_cache_gather_dequant.restype = None
     lib.oracle_qk_norm_rope_packed.argtypes = [
         P, I64, I32, I32, I32, I32, D, P, P, P, P]
@@ -271,6 +274,30 @@ def kv_cache_gather_dequant_scalar(kv_cache, kv_cache_scale, slots):
     _load().oracle_kv_cache_gather_dequant_scalar(
         _ptr(kv_cache, np.uint8), float(kv_cache_scale), _ptr(slots, np.int64),
         slots.shape[0], pages, _ptr(out, np.uint16, True))
+    return out
+
+
+def kv_cache_gather_dequant_paged_scalar(kv_cache, kv_cache_scale, block_table,
+                                         seq_lens, out_offsets, out):
+    """Scalar-scale read side through block tables, in place on ``out``
+    (uint16 [N, 512]); the walk of :func:`kv_cache_gather_dequant_paged`."""
+    pages = kv_cache.shape[0]
+    if kv_cache.shape != (pages, 64, 576):
+        raise ValueError("cache must be [pages,64,576]")
+    block_table = np.ascontiguousarray(block_table, np.int32)
+    if block_table.ndim != 2:
+        raise ValueError("block_table must be [num_seqs, max_blocks_per_seq]")
+    S, M = block_table.shape
+    seq_lens = np.ascontiguousarray(seq_lens, np.int32)
+    out_offsets = np.ascontiguousarray(out_offsets, np.int64)
+    if seq_lens.shape != (S,) or out_offsets.shape != (S,):
+        raise ValueError("seq_lens and out_offsets must be [num_seqs]")
+    if out.ndim != 2 or out.shape[1] != 512:
+        raise ValueError("out must be [N, 512]")
+    _load().oracle_kv_cache_gather_dequant_paged_scalar(
+        _ptr(kv_cache, np.uint8), float(kv_cache_scale), pages,
+        _ptr(block_table, np.int32), S, M, _ptr(seq_lens, np.int32),
+        _ptr(out_offsets, np.int64), out.shape[0], _ptr(out, np.uint16, True))
     return out
 
 

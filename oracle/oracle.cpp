@@ -104,6 +104,28 @@ void quantise_insert(const double* y, uint8_t* dst, uint8_t* scale) {
   }
 }
 
+// The walk of the read side through block tables: token j of sequence s is
+// slot block_table[s][j / 64] * 64 + j % 64 (or -1 for a page id outside the
+// cache) and goes to output row out_offsets[s] + j; tokens past the table's
+// width and rows outside [0, num_rows) are skipped.  Calls row_fn(slot, row)
+// for every row written.
+template <class RowFn>
+void for_each_table_row(int64_t num_pages, const int32_t* block_table,
+                        int32_t num_seqs, int32_t max_blocks_per_seq,
+                        const int32_t* seq_lens, const int64_t* out_offsets,
+                        int64_t num_rows, RowFn row_fn) {
+  for (int32_t s = 0; s < num_seqs; ++s) {
+    const int64_t len = seq_lens[s];
+    for (int64_t j = 0; j < len && j < int64_t{max_blocks_per_seq} * kPageSize; ++j) {
+      const int64_t row = out_offsets[s] + j;
+      if (row < 0 || row >= num_rows) continue;
+      const int64_t page = block_table[int64_t{s} * max_blocks_per_seq + j / kPageSize];
+      const int64_t slot = page < 0 || page >= num_pages ? -1 : page * kPageSize + j % kPageSize;
+      row_fn(slot, row);
+    }
+  }
+}
+
 }  // namespace
 
 extern "C" {
@@ -413,16 +435,26 @@ void oracle_kv_cache_gather_dequant_paged(
     const int32_t* seq_lens, const int64_t* out_offsets, int64_t num_rows,
     uint16_t* out) {
   const int64_t num_slots = num_pages * kPageSize;
-  for (int32_t s = 0; s < num_seqs; ++s) {
-    const int64_t len = seq_lens[s];
-    for (int64_t j = 0; j < len && j < int64_t{max_blocks_per_seq} * kPageSize; ++j) {
-      const int64_t row = out_offsets[s] + j;
-      if (row < 0 || row >= num_rows) continue;
-      const int64_t page = block_table[int64_t{s} * max_blocks_per_seq + j / kPageSize];
-      const int64_t slot = page < 0 || page >= num_pages ? -1 : page * kPageSize + j % kPageSize;
-      dequant_row(kv_cache, kv_scale, slot, num_slots, out + row * kHeadDim);
-    }
-  }
+  for_each_table_row(num_pages, block_table, num_seqs, max_blocks_per_seq,
+                     seq_lens, out_offsets, num_rows,
+                     [&](int64_t slot, int64_t row) {
+                       dequant_row(kv_cache, kv_scale, slot, num_slots,
+                                   out + row * kHeadDim);
+                     });
+}
+
+void oracle_kv_cache_gather_dequant_paged_scalar(
+    const uint8_t* kv_cache, float kv_cache_scale, int64_t num_pages,
+    const int32_t* block_table, int32_t num_seqs, int32_t max_blocks_per_seq,
+    const int32_t* seq_lens, const int64_t* out_offsets, int64_t num_rows,
+    uint16_t* out) {
+  for_each_table_row(num_pages, block_table, num_seqs, max_blocks_per_seq,
+                     seq_lens, out_offsets, num_rows,
+                     [&](int64_t slot, int64_t row) {
+                       oracle_kv_cache_gather_dequant_scalar(
+                           kv_cache, kv_cache_scale, &slot, 1, num_pages,
+                           out + row * kHeadDim);
+                     });
 }
 
 void oracle_qk_norm_rope_packed(

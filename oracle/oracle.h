@@ -181,6 +181,15 @@ void oracle_kv_cache_gather_dequant_scalar(const uint8_t* kv_cache,
                                            int64_t num_rows, int64_t num_pages,
                                            uint16_t* out);
 
+/* The scalar-scale read side through block tables: the rows of
+ * oracle_kv_cache_gather_dequant_paged (same walk over sequences, pages and
+ * output rows), each dequantised as by oracle_kv_cache_gather_dequant_scalar. */
+void oracle_kv_cache_gather_dequant_paged_scalar(
+    const uint8_t* kv_cache, float kv_cache_scale, int64_t num_pages,
+    const int32_t* block_table, int32_t num_seqs, int32_t max_blocks_per_seq,
+    const int32_t* seq_lens, const int64_t* out_offsets, int64_t num_rows,
+    uint16_t* out);
+
 /* ---- entry 2: packed-QKV FusedQkNormRope ([P3] "Summary") ---------------- */
 /*
  *   qkv           bf16 [T, (Hq + Hk + Hv) * D], Q and K heads rewritten in

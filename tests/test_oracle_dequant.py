@@ -139,3 +139,66 @@ def test_paged_read_edge_semantics():
     want[298:362] = flat[192:256]            # tokens 192..299 are past 3 pages
     want[395:398] = flat[128:131]            # sequence 3: rows 398, 399 are past N
     np.testing.assert_array_equal(out, want)
+
+
+def test_scalar_paged_read_edge_semantics():
+    # the same tables as above through the scalar-scale reader: rows are the
+    # scalar slot-list read of the named slots, zero for invalid pages, and
+    # the length cap, rows past N and uncovered gaps are left alone
+    cache, _ = _random_cache(4, 93)
+    s = 0.0173
+    flat = O.kv_cache_gather_dequant_scalar(cache, s, np.arange(4 * 64, dtype=np.int64))
+    table = np.array([[0, -1, 9], [3, 2, 1], [1, 2, 3], [2, 0, 0]], np.int32)
+    lens = np.array([150, 0, 300, 5], np.int32)
+    offsets = np.array([10, 0, 170, 395], np.int64)
+    N = 398
+    canary = 0x7777
+    out = np.full((N, 512), canary, np.uint16)
+    O.kv_cache_gather_dequant_paged_scalar(cache, s, table, lens, offsets, out)
+    want = np.full((N, 512), canary, np.uint16)
+    want[10:74] = flat[0:64]
+    want[74:160] = 0
+    want[170:234] = flat[64:128]
+    want[234:298] = flat[128:192]
+    want[298:362] = flat[192:256]
+    want[395:398] = flat[128:131]
+    np.testing.assert_array_equal(out, want)
+
+
+def test_scalar_paged_read_equals_slot_list_read_of_the_table():
+    # random tables: the slots the definition names (page * 64 + j % 64, or
+    # -1 for an id outside the cache), read through the slot-list reader
+    rng = np.random.default_rng(94)
+    pages = 7
+    cache, _ = _random_cache(pages, 95)
+    s = 3.25
+    S, M = 5, 3
+    table = rng.integers(-2, pages + 2, (S, M)).astype(np.int32)
+    lens = rng.integers(0, M * 64 + 1, S).astype(np.int32)
+    offsets = np.concatenate([[0], np.cumsum(lens)[:-1]]).astype(np.int64)
+    N = int(lens.sum())
+    out = np.full((N, 512), 0x7777, np.uint16)
+    O.kv_cache_gather_dequant_paged_scalar(cache, s, table, lens, offsets, out)
+    slots = []
+    for q in range(S):
+        for j in range(lens[q]):
+            p = int(table[q, j // 64])
+            slots.append(p * 64 + j % 64 if 0 <= p < pages else -1)
+    np.testing.assert_array_equal(
+        out, O.kv_cache_gather_dequant_scalar(cache, s, np.array(slots, np.int64)))
+
+
+def test_scalar_paged_read_equals_blockwise_read_at_a_power_of_two():
+    # every exponent byte 127 + k and a scalar scale of 2^k: E4M3 * 2^k is
+    # exact both ways, so the two conventions read the same bf16 rows
+    cache, _ = _random_cache(5, 96)
+    for k in (-6, 0, 3):
+        scale = np.full((5, 64, 8), 127 + k, np.uint8)
+        table = np.array([[4, 0], [2, -1], [1, 3]], np.int32)
+        lens = np.array([100, 90, 128], np.int32)
+        offsets = np.array([0, 100, 190], np.int64)
+        a = np.full((318, 512), 0x7777, np.uint16)
+        b = np.full((318, 512), 0x7777, np.uint16)
+        O.kv_cache_gather_dequant_paged(cache, scale, table, lens, offsets, a)
+        O.kv_cache_gather_dequant_paged_scalar(cache, 2.0 ** k, table, lens, offsets, b)
+        np.testing.assert_array_equal(a, b)

@@ -107,11 +107,11 @@ MUTATIONS = [
      "    uint16_t bits = oracle_bf16_rne(y[kRopeStart + j]);\n"
      "    dst[kRopeStart + 2 * j] = static_cast<uint8_t>(bits & 0xFF);\n"
      "    dst[kRopeStart + 2 * j + 1] = static_cast<uint8_t>(bits >> 8);\n"
-     "  }\n}\n\n}  // namespace",
+     "  }\n}\n\n// The walk of the read side",
      "    uint16_t bits = oracle_bf16_rne(y[kRopeStart + j]);\n"
      "    dst[kRopeStart + 2 * j + 1] = static_cast<uint8_t>(bits & 0xFF);\n"
      "    dst[kRopeStart + 2 * j] = static_cast<uint8_t>(bits >> 8);\n"
-     "  }\n}\n\n}  // namespace"),
+     "  }\n}\n\n// The walk of the read side"),
     ("slot_bound_off_by_one",
      "if (slot < 0 || slot >= num_slots) continue;  // skipped token",
      "if (slot < 0 || slot >= num_slots - 1) continue;  // skipped token"),
@@ -205,6 +205,9 @@ MUTATIONS = [
      "            y_out + t * kHeadDim);",
      "    kv_head(kv + t * kHeadDim, kv_weight, row, row + kRopeDim / 2, 0.0,\n"
      "            y_out + t * kHeadDim);"),
+    ("scalar_paged_scale_doubled",
+     "                           kv_cache, kv_cache_scale, &slot, 1, num_pages,",
+     "                           kv_cache, 2.0f * kv_cache_scale, &slot, 1, num_pages,"),
     ("quant_insert_stage_bound",
      "    if (slot < 0 || slot >= num_slots) continue;\n    for (int d = 0; d < kHeadDim; ++d) y[d]",
      "    if (slot < 0 || slot >= num_slots - 1) continue;\n    for (int d = 0; d < kHeadDim; ++d) y[d]"),
