@@ -592,6 +592,28 @@ def main():
                                                       n * (pages // S), n))
                     extra["dequant_paged_long64"]["oracle"] = oracle_beside(dqp_run, S)
                 log(f"dequant_paged_long64: {extra['dequant_paged_long64']}")
+                # the scalar-scale convention through the same block tables
+                per = time_flushed(lambda: K.kv_cache_gather_dequant_paged_scalar_scale(
+                    cc, rscale, table, lens, offs, out))
+                m = statistics.median(per)
+                nb = A.dequant_paged_bytes(S * L, S * L, pages, S) - 7 * S * L + 4
+                extra["dequant_paged_scalar_long64"] = {
+                    "rows": S * L, "sequences": S, "bytes": nb,
+                    "median_us": round(m * 1e6, 1), "min_us": round(min(per) * 1e6, 1),
+                    "gbps": round(nb / m / 1e9, 1)}
+                annotate(extra["dequant_paged_scalar_long64"], nb, m, "copy")
+                if cpu_on:
+                    def dqps_run(n):
+                        o = np.zeros((n * L, 512), np.uint16)
+                        t0 = time.perf_counter()
+                        O.kv_cache_gather_dequant_paged_scalar(ch, 0.0173, th[:n],
+                                                               lh[:n], oh[:n], o)
+                        return (time.perf_counter() - t0,
+                                A.dequant_paged_bytes(n * L, n * L, n * (pages // S), n)
+                                - 7 * n * L + 4)
+                    extra["dequant_paged_scalar_long64"]["oracle"] = oracle_beside(
+                        dqps_run, S)
+                log(f"dequant_paged_scalar_long64: {extra['dequant_paged_scalar_long64']}")
                 del slots, out, table, lens, offs
             del xx, qq, cc, ss
             torch.cuda.empty_cache()

@@ -41,7 +41,8 @@ EXPORTED = ["qnorm_rope_kv_quant_insert", "qk_norm_rope_packed",
             "fp8kv_set_dispatch_threshold", "fp8kv_get_dispatch_threshold",
             "fp8kv_set_tiling", "fp8kv_get_tiling",
             "fp8kv_stream_copy", "fp8kv_stream_rmw",
-            "kv_cache_gather_dequant_paged"]
+            "kv_cache_gather_dequant_paged",
+            "kv_cache_gather_dequant_paged_scalar_scale"]
 
 
 class Fp8kvError(RuntimeError):
@@ -84,6 +85,9 @@ def lib() -> ctypes.CDLL:
     L.kv_cache_gather_dequant_paged.argtypes = [P, P, I64, I32, P, I32, I32, P, P,
                                                 I64, P, P]
     L.kv_cache_gather_dequant_paged.restype = ctypes.c_int
+    L.kv_cache_gather_dequant_paged_scalar_scale.argtypes = [
+        P, P, I64, I32, P, I32, I32, P, P, I64, P, P]
+    L.kv_cache_gather_dequant_paged_scalar_scale.restype = ctypes.c_int
     L.rms_norm_rows.argtypes = [P, P, P, I64, I32, F, P]
     L.rms_norm_rows.restype = ctypes.c_int
     L.rope_rows.argtypes = [P, P, P, I64, I32, I32, I32, I64, P]
@@ -350,6 +354,34 @@ def kv_cache_gather_dequant_paged(kv_cache, kv_scale, block_table, seq_lens,
     _call("kv_cache_gather_dequant_paged",
           (kv_cache, kv_scale, block_table, seq_lens, out_offsets, out), stream,
           kv_cache.data_ptr(), kv_scale.data_ptr(), pages, page_size,
+          block_table.data_ptr(), S, M, seq_lens.data_ptr(), out_offsets.data_ptr(),
+          out.shape[0], out.data_ptr())
+    return out
+
+
+def kv_cache_gather_dequant_paged_scalar_scale(kv_cache, kv_cache_scale,
+                                               block_table, seq_lens,
+                                               out_offsets, out, stream=None):
+    """The scalar-scale read side through block tables (the walk of
+    :func:`kv_cache_gather_dequant_paged`, rows dequantised with the one
+    fp32 scale in ``kv_cache_scale``).  Returns ``out``."""
+    _check(kv_cache, "kv_cache", torch.uint8)
+    if kv_cache.dim() != 3 or kv_cache.shape[2] != ROW_BYTES:
+        raise ValueError("kv_cache must be [num_pages, page_size, 576]")
+    pages, page_size, _ = kv_cache.shape
+    _check(kv_cache_scale, "kv_cache_scale", torch.float32, (1,))
+    _check(block_table, "block_table", torch.int32)
+    if block_table.dim() != 2:
+        raise ValueError("block_table must be [num_seqs, max_blocks_per_seq]")
+    S, M = block_table.shape
+    _check(seq_lens, "seq_lens", torch.int32, (S,))
+    _check(out_offsets, "out_offsets", torch.int64, (S,))
+    _check(out, "out", torch.bfloat16)
+    if out.dim() != 2 or out.shape[1] != HEAD_DIM:
+        raise ValueError("out must be [N, 512]")
+    _call("kv_cache_gather_dequant_paged_scalar_scale",
+          (kv_cache, kv_cache_scale, block_table, seq_lens, out_offsets, out), stream,
+          kv_cache.data_ptr(), kv_cache_scale.data_ptr(), pages, page_size,
           block_table.data_ptr(), S, M, seq_lens.data_ptr(), out_offsets.data_ptr(),
           out.shape[0], out.data_ptr())
     return out

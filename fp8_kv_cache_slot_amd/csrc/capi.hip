@@ -266,6 +266,39 @@ FP8KV_API int kv_cache_gather_dequant_paged(
   PagedDequantArgs a;
   a.kv_cache = kv_cache;
   a.kv_scale = kv_scale;
+  a.scalar_scale = nullptr;
+  a.scalar = false;
+  a.block_table = block_table;
+  a.seq_lens = seq_lens;
+  a.out_offsets = out_offsets;
+  a.out = static_cast<uint16_t*>(out);
+  a.num_seqs = num_seqs;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.num_pages = num_pages;
+  a.num_rows = num_rows;
+  return launch_gather_dequant_paged(a, static_cast<hipStream_t>(stream));
+}
+
+FP8KV_API int kv_cache_gather_dequant_paged_scalar_scale(
+    const uint8_t* kv_cache, const float* kv_cache_scale, int64_t num_pages,
+    int32_t page_size, const int32_t* block_table, int32_t num_seqs,
+    int32_t max_blocks_per_seq, const int32_t* seq_lens,
+    const int64_t* out_offsets, int64_t num_rows, void* out, void* stream) {
+  using namespace fp8kv;
+  // the scale pointer takes the exponent tensor's place in the NULL check
+  int st = validate_gather_dequant_paged(
+      kv_cache, reinterpret_cast<const uint8_t*>(kv_cache_scale), num_pages,
+      page_size, block_table, num_seqs, max_blocks_per_seq, seq_lens,
+      out_offsets, num_rows, out, 4);
+  if (st != FP8KV_OK || num_seqs == 0 || max_blocks_per_seq == 0 || num_rows == 0)
+    return st;
+  st = check_device();
+  if (st != FP8KV_OK) return st;
+  PagedDequantArgs a;
+  a.kv_cache = kv_cache;
+  a.kv_scale = nullptr;
+  a.scalar_scale = kv_cache_scale;  // read only when num_pages > 0
+  a.scalar = true;
   a.block_table = block_table;
   a.seq_lens = seq_lens;
   a.out_offsets = out_offsets;
@@ -330,9 +363,8 @@ FP8KV_API int kv_cache_gather_dequant_scalar_scale(
   using namespace fp8kv;
   int st = validate_gather_dequant(
       kv_cache, reinterpret_cast<const uint8_t*>(kv_cache_scale), num_pages,
-      page_size, slots, num_rows, out);
+      page_size, slots, num_rows, out, 4);
   if (st != FP8KV_OK || num_rows == 0) return st;
-  if (num_pages > 0 && !aligned(kv_cache_scale, 4)) return FP8KV_ERR_ALIGN;
   st = check_device();
   if (st != FP8KV_OK) return st;
   DequantArgs a;

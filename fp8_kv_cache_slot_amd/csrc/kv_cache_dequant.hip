@@ -161,9 +161,13 @@ constexpr int kDequantRows = 4;
 // loads; every lane then issues its row loads with no branch in front of
 // them (an invalid page reads slot 0 and stores zero rows, as in the slot-list
 // kernel), and only the stores depend on the length and the output bounds.
-template <int WAVES, int PRS>
+//
+// SCALAR: the scalar-scale convention, as in the slot-list kernel (no exponent
+// bytes read; codes times scalar_scale[0], rounded to fp32, then to bf16).
+template <int WAVES, int PRS, bool SCALAR>
 __global__ void __launch_bounds__(WAVES * 64) kv_cache_gather_dequant_paged_kernel(
     const uint8_t* __restrict__ kv_cache, const uint8_t* __restrict__ kv_scale,
+    const float* __restrict__ scalar_scale,
     const int32_t* __restrict__ block_table, const int32_t* __restrict__ seq_lens,
     const int64_t* __restrict__ out_offsets, uint16_t* __restrict__ out,
     int32_t max_blocks_per_seq, int64_t num_pages, int64_t num_rows) {
@@ -193,8 +197,11 @@ __global__ void __launch_bounds__(WAVES * 64) kv_cache_gather_dequant_paged_kern
   int64_t sl[PRS];
 #pragma unroll
   for (int r = 0; r < PRS; ++r) sl[r] = page_ok ? slot0 + r : -1;
+  // with pages, the scalar scale pointer is a checked device pointer
+  float fs = 1.0f;
+  if constexpr (SCALAR) fs = *scalar_scale;
   Rows<PRS> d;
-  load_rows<PRS, false>(kv_cache, kv_scale, sl, num_pages * 64, lane, d);
+  load_rows<PRS, SCALAR>(kv_cache, kv_scale, sl, num_pages * 64, lane, d);
 #pragma unroll
   for (int r = 0; r < PRS; ++r) {
     const int64_t i = first + r;
@@ -209,8 +216,13 @@ __global__ void __launch_bounds__(WAVES * 64) kv_cache_gather_dequant_paged_kern
     float v[8];
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      v[2 * k] = __builtin_ldexpf(p[k][0], e);
-      v[2 * k + 1] = __builtin_ldexpf(p[k][1], e);
+      if constexpr (SCALAR) {
+        v[2 * k] = p[k][0] * fs;
+        v[2 * k + 1] = p[k][1] * fs;
+      } else {
+        v[2 * k] = __builtin_ldexpf(p[k][0], e);
+        v[2 * k + 1] = __builtin_ldexpf(p[k][1], e);
+      }
     }
     const u32x4_t q = {pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3]),
                        pack_bf16(v[4], v[5]), pack_bf16(v[6], v[7])};
@@ -235,6 +247,7 @@ int launch_gather_dequant_paged(const PagedDequantArgs& a, hipStream_t stream) {
   if (blocks_x > 0x7FFFFFFF || a.num_seqs > 65535) return FP8KV_ERR_SHAPE;
   void* args[] = {const_cast<const uint8_t**>(&a.kv_cache),
                   const_cast<const uint8_t**>(&a.kv_scale),
+                  const_cast<const float**>(&a.scalar_scale),
                   const_cast<const int32_t**>(&a.block_table),
                   const_cast<const int32_t**>(&a.seq_lens),
                   const_cast<const int64_t**>(&a.out_offsets),
@@ -242,9 +255,13 @@ int launch_gather_dequant_paged(const PagedDequantArgs& a, hipStream_t stream) {
                   const_cast<int32_t*>(&a.max_blocks_per_seq),
                   const_cast<int64_t*>(&a.num_pages),
                   const_cast<int64_t*>(&a.num_rows)};
+  const void* fn =
+      a.scalar ? reinterpret_cast<const void*>(
+                     &kv_cache_gather_dequant_paged_kernel<kPagedWaves, kPagedRows, true>)
+               : reinterpret_cast<const void*>(
+                     &kv_cache_gather_dequant_paged_kernel<kPagedWaves, kPagedRows, false>);
   hipError_t err = hipLaunchKernel(
-      reinterpret_cast<const void*>(
-          &kv_cache_gather_dequant_paged_kernel<kPagedWaves, kPagedRows>),
+      fn,
       dim3(static_cast<uint32_t>(blocks_x), static_cast<uint32_t>(a.num_seqs)),
       dim3(kPagedWaves * 64), args, 0, stream);
   return err == hipSuccess ? FP8KV_OK : FP8KV_ERR_LAUNCH;

@@ -81,7 +81,9 @@ int launch_gather_dequant(const DequantArgs& a, hipStream_t stream);
 
 struct PagedDequantArgs {
   const uint8_t* kv_cache;
-  const uint8_t* kv_scale;
+  const uint8_t* kv_scale;       // blockwise exponents (unused when scalar)
+  const float* scalar_scale;     // one device float: the scalar-scale convention
+  bool scalar;                   // use scalar_scale instead of kv_scale
   const int32_t* block_table;   // [num_seqs, max_blocks_per_seq]
   const int32_t* seq_lens;      // [num_seqs]
   const int64_t* out_offsets;   // [num_seqs]: first output row of each sequence

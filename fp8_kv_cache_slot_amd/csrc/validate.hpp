@@ -114,10 +114,13 @@ inline int validate_packed_ex(const void* qkv, int64_t num_tokens,
   return FP8KV_OK;
 }
 
+// scale_align: 8 for the exponent tensor, 4 for the scalar-scale float that
+// takes its place.
 inline int validate_gather_dequant(const uint8_t* kv_cache,
                                    const uint8_t* kv_scale, int64_t num_pages,
                                    int32_t page_size, const int64_t* slots,
-                                   int64_t num_rows, const void* out) {
+                                   int64_t num_rows, const void* out,
+                                   uintptr_t scale_align = 8) {
   if (num_pages < 0 || num_rows < 0 || num_rows > 0x7FFFFFFF ||
       num_pages > (int64_t{1} << 40))
     return FP8KV_ERR_SHAPE;
@@ -126,7 +129,8 @@ inline int validate_gather_dequant(const uint8_t* kv_cache,
   if (!slots || !out) return FP8KV_ERR_NULL;
   if (num_pages > 0 && (!kv_cache || !kv_scale)) return FP8KV_ERR_NULL;
   if (!aligned(slots, 8) || !aligned(out, 16) ||
-      (kv_cache && !aligned(kv_cache, 16)) || (kv_scale && !aligned(kv_scale, 8)))
+      (kv_cache && !aligned(kv_cache, 16)) ||
+      (kv_scale && !aligned(kv_scale, scale_align)))
     return FP8KV_ERR_ALIGN;
   return FP8KV_OK;
 }
@@ -135,7 +139,8 @@ inline int validate_gather_dequant_paged(
     const uint8_t* kv_cache, const uint8_t* kv_scale, int64_t num_pages,
     int32_t page_size, const int32_t* block_table, int32_t num_seqs,
     int32_t max_blocks_per_seq, const int32_t* seq_lens,
-    const int64_t* out_offsets, int64_t num_rows, const void* out) {
+    const int64_t* out_offsets, int64_t num_rows, const void* out,
+    uintptr_t scale_align = 8) {
   if (num_pages < 0 || num_pages > (int64_t{1} << 40) || num_seqs < 0 ||
       num_seqs > 65535 || max_blocks_per_seq < 0 ||
       max_blocks_per_seq > (int32_t{1} << 24) || num_rows < 0 ||
@@ -147,7 +152,7 @@ inline int validate_gather_dequant_paged(
   if (num_pages > 0 && (!kv_cache || !kv_scale)) return FP8KV_ERR_NULL;
   if (!aligned(block_table, 4) || !aligned(seq_lens, 4) || !aligned(out_offsets, 8) ||
       !aligned(out, 16) || (kv_cache && !aligned(kv_cache, 16)) ||
-      (kv_scale && !aligned(kv_scale, 8)))
+      (kv_scale && !aligned(kv_scale, scale_align)))
     return FP8KV_ERR_ALIGN;
   return FP8KV_OK;
 }

@@ -295,6 +295,18 @@ int kv_cache_gather_dequant_scalar_scale(const uint8_t* kv_cache,
                                          const int64_t* slots, int64_t num_rows,
                                          void* out, void* stream);
 
+/*
+ * The scalar-scale read side through block tables: the rows, walk, bounds and
+ * errors of kv_cache_gather_dequant_paged, each row dequantised as by
+ * kv_cache_gather_dequant_scalar_scale.  kv_cache_scale is a device pointer
+ * (4-byte aligned), required when num_pages > 0 and then read once per wave.
+ */
+int kv_cache_gather_dequant_paged_scalar_scale(
+    const uint8_t* kv_cache, const float* kv_cache_scale, int64_t num_pages,
+    int32_t page_size, const int32_t* block_table, int32_t num_seqs,
+    int32_t max_blocks_per_seq, const int32_t* seq_lens,
+    const int64_t* out_offsets, int64_t num_rows, void* out, void* stream);
+
 /* Static text for a status code (never NULL). */
 const char* fp8kv_status_string(int status);
 

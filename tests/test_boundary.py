@@ -220,6 +220,23 @@ def test_paged_dequant_argument_errors(over, want):
     assert _paged(**over) == want
 
 
+def _paged_scalar(**over):
+    a = dict(cache=FAKE, scale=FAKE, pages=2, page=64, table=FAKE, S=3, M=4,
+             lens=FAKE, offs=FAKE, N=100, out=FAKE, stream=None)
+    a.update(over)
+    return K.lib().kv_cache_gather_dequant_paged_scalar_scale(*a.values())
+
+
+@pytest.mark.parametrize("over,want", [
+    (dict(pages=-1), 2), (dict(S=65536), 2), (dict(page=32), 3),
+    (dict(table=None), 1), (dict(cache=None), 1), (dict(scale=None), 1),
+    (dict(scale=FAKE + 2), 4), (dict(out=FAKE + 8), 4),
+    (dict(S=0, table=None, lens=None, offs=None), 0), (dict(N=0, out=None), 0),
+])
+def test_paged_scalar_dequant_argument_errors(over, want):
+    assert _paged_scalar(**over) == want
+
+
 def _copy(**over):
     a = dict(dst=FAKE, src=FAKE + 4096, nb=4096, stream=None)
     a.update(over)
@@ -257,6 +274,10 @@ def test_no_device_is_reported_not_launched():
     assert _prologue_scalar(pages=0, cache=None, scale=None) == 5
     assert _copy() == 5 and _rmw() == 5
     assert _paged() == 5 and _paged(pages=0, cache=None, scale=None) == 5
+    assert _paged_scalar() == 5
+    assert _paged_scalar(pages=0, cache=None, scale=None) == 5
+    # the scalar scale is one float: 4-byte alignment is enough
+    assert _paged_scalar(scale=FAKE + 4) == 5 and _dequant_scalar(scale=FAKE + 4) == 5
 
 
 def test_knobs():

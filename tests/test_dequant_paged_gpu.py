@@ -11,6 +11,7 @@ import torch
 import fp8_kv_cache_slot_amd as K
 import oracle as O
 from fp8_kv_cache_slot_amd import inputs as I
+from tests import parity as P
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -129,3 +130,95 @@ def test_gpu_writer_gpu_reader_round_trip():
                                     torch.from_numpy(offs).to(DEV), out)
     torch.cuda.synchronize()
     assert torch.equal(out, flat)
+
+
+# ---------------------------------------------------------------------------
+# the scalar-scale convention through block tables
+# ---------------------------------------------------------------------------
+
+def _both_scalar(cache, s, table, lens, offs, N):
+    ref = np.full((N, 512), CANARY, np.uint16)
+    O.kv_cache_gather_dequant_paged_scalar(cache, s, table, lens, offs, ref)
+    out = torch.full((N, 512), CANARY, dtype=torch.int16, device=DEV).view(torch.bfloat16)
+    d = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+    K.kv_cache_gather_dequant_paged_scalar_scale(
+        d(cache), torch.tensor([s], dtype=torch.float32, device=DEV),
+        d(table.astype(np.int32)), d(lens.astype(np.int32)),
+        d(offs.astype(np.int64)), out)
+    torch.cuda.synchronize()
+    return I.bits(out), ref
+
+
+def _check_scalar_rows(got, ref, what):
+    # rows the oracle left alone (canary) and the rotary part: bit-exact; the
+    # dequantised dims: fp32 product then bf16 against one rounding from double
+    np.testing.assert_array_equal(got[:, 448:], ref[:, 448:], err_msg=what)
+    untouched = np.all(ref == CANARY, axis=1)
+    np.testing.assert_array_equal(got[untouched], ref[untouched], err_msg=what)
+    P.check_bf16(got[~untouched, :448], ref[~untouched, :448], what)
+
+
+def test_scalar_edge_semantics():
+    cache, _ = _random_cache(4, 710)
+    table = np.array([[0, -1, 9], [3, 2, 1], [1, 2, 3], [2, 0, 0]], np.int32)
+    lens = np.array([150, 0, 300, 5], np.int32)
+    offs = np.array([10, 0, 170, 395], np.int64)
+    got, ref = _both_scalar(cache, 0.0173, table, lens, offs, 398)
+    _check_scalar_rows(got, ref, "scalar edge semantics")
+
+
+@pytest.mark.parametrize("seed", [711, 712, 713])
+def test_scalar_random_tables(seed):
+    rng = np.random.default_rng(seed)
+    pages = int(rng.integers(3, 40))
+    cache, _ = _random_cache(pages, seed)
+    s = float(rng.choice([0.0173, 3.5, 2.0 ** -10]))
+    S = int(rng.integers(1, 12))
+    M = int(rng.integers(1, 6))
+    table = rng.integers(-2, pages + 2, (S, M)).astype(np.int32)
+    lens = rng.integers(-1, M * 64 + 20, S).astype(np.int32)
+    start = int(rng.integers(0, 5))
+    offs = start + np.concatenate(
+        [[0], np.cumsum(np.maximum(lens, 0) + rng.integers(0, 7, S))[:-1]])
+    N = int(offs[-1] + max(lens[-1], 0) - rng.integers(0, 3))
+    got, ref = _both_scalar(cache, s, table, lens, offs.astype(np.int64), max(N, 1))
+    _check_scalar_rows(got, ref, f"scalar random tables seed {seed} s={s}")
+
+
+def test_scalar_full_size_equals_the_slot_list_read():
+    # all 2048 pages in a random order: every row equals, bit for bit, the
+    # GPU slot-list read of the slots the tables name (same arithmetic)
+    pages, S, L = 2048, 32, 4096
+    cache, _ = _random_cache(pages, 714)
+    perm = np.random.default_rng(715).permutation(pages).astype(np.int32)
+    table = perm.reshape(S, pages // S)
+    sc = torch.tensor([0.0173], dtype=torch.float32, device=DEV)
+    dc = torch.from_numpy(cache).to(DEV)
+    out = torch.empty((S * L, 512), dtype=torch.bfloat16, device=DEV)
+    K.kv_cache_gather_dequant_paged_scalar_scale(
+        dc, sc, torch.from_numpy(table).to(DEV),
+        torch.full((S,), L, dtype=torch.int32, device=DEV),
+        torch.arange(S, dtype=torch.int64, device=DEV) * L, out)
+    slots = (table.astype(np.int64)[:, :, None] * 64 + np.arange(64)).reshape(-1)
+    flat = K.kv_cache_gather_dequant_scalar_scale(dc, sc, torch.from_numpy(slots).to(DEV))
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), flat.view(torch.int16))
+    # and a sample of rows against the oracle
+    rows = np.random.default_rng(716).choice(S * L, 512, replace=False)
+    ref = O.kv_cache_gather_dequant_scalar(cache, 0.0173, slots[rows])
+    got = I.bits(out)[rows]
+    np.testing.assert_array_equal(got[:, 448:], ref[:, 448:])
+    P.check_bf16(got[:, :448], ref[:, :448], "scalar full size sample")
+
+
+def test_scalar_zero_pages():
+    empty_c = torch.empty((0, 64, 576), dtype=torch.uint8, device=DEV)
+    sc = torch.tensor([0.5], dtype=torch.float32, device=DEV)
+    out = torch.full((80, 512), CANARY, dtype=torch.int16, device=DEV).view(torch.bfloat16)
+    K.kv_cache_gather_dequant_paged_scalar_scale(
+        empty_c, sc, torch.tensor([[0, 1]], dtype=torch.int32, device=DEV),
+        torch.tensor([70], dtype=torch.int32, device=DEV),
+        torch.tensor([5], dtype=torch.int64, device=DEV), out)
+    torch.cuda.synchronize()
+    b = I.bits(out)
+    assert np.all(b[5:75] == 0) and np.all(b[:5] == CANARY) and np.all(b[75:] == CANARY)

@@ -163,6 +163,16 @@ def test_read_side_and_stages():
     torch.cuda.synchronize()
     assert torch.equal(_guards(b), before)
     assert torch.equal(pout, pref)
+    # the scalar-scale block-table read side, the same way
+    sc = torch.tensor([0.0173], dtype=torch.float32, device=DEV)
+    sref = torch.zeros((470, 512), dtype=torch.bfloat16, device=DEV)
+    K.kv_cache_gather_dequant_paged_scalar_scale(cache, sc, table, lens, offs, sref)
+    b, sout = _guarded(torch.zeros_like(sref))
+    before = _guards(b)
+    K.kv_cache_gather_dequant_paged_scalar_scale(cache, sc, table, lens, offs, sout)
+    torch.cuda.synchronize()
+    assert torch.equal(_guards(b), before)
+    assert torch.equal(sout.view(torch.int16), sref.view(torch.int16))
     # a separate RMSNorm stage into a guarded output
     nref = K.rms_norm_rows(x["kv"], x["kv_weight"], x["eps"])
     b, nout = _guarded(torch.zeros_like(nref))
