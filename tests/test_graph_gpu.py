@@ -68,6 +68,9 @@ def test_packed_and_read_side():
     lens = torch.tensor([100, 0, 64, 3000], dtype=torch.int32, device=DEV)
     offs = torch.tensor([0, 100, 100, 164], dtype=torch.int64, device=DEV)
     pout = torch.empty((2000, 512), dtype=torch.bfloat16, device=DEV)
+    sc = torch.tensor([0.0173], dtype=torch.float32, device=DEV)
+    sout = torch.empty_like(out)
+    spout = torch.empty_like(pout)
 
     def run():
         K.qk_norm_rope_packed(qkv, pw.num_heads_q, pw.num_heads_k, pw.num_heads_v,
@@ -75,17 +78,26 @@ def test_packed_and_read_side():
                               px["cos_sin_cache"], True, px["position_ids"])
         K.kv_cache_gather_dequant(cache, scale, x["slot_mapping"], out=out)
         K.kv_cache_gather_dequant_paged(cache, scale, table, lens, offs, pout)
+        K.kv_cache_gather_dequant_scalar_scale(cache, sc, x["slot_mapping"], out=sout)
+        K.kv_cache_gather_dequant_paged_scalar_scale(cache, sc, table, lens, offs,
+                                                     spout)
     pout.zero_()
+    spout.zero_()
     run()
     ref_qkv, ref_out, ref_pout = qkv.clone(), out.clone(), pout.clone()
+    ref_sout, ref_spout = sout.clone(), spout.clone()
     g = _capture(run)
     for _ in range(REPLAYS):
         qkv.copy_(px["qkv"])
         out.zero_()
         pout.zero_()
+        sout.zero_()
+        spout.zero_()
         torch.cuda.synchronize()
         g.replay()
         torch.cuda.synchronize()
         assert torch.equal(qkv, ref_qkv)
         assert torch.equal(out, ref_out)
         assert torch.equal(pout, ref_pout)
+        assert torch.equal(sout.view(torch.int16), ref_sout.view(torch.int16))
+        assert torch.equal(spout.view(torch.int16), ref_spout.view(torch.int16))
