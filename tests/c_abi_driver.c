@@ -10,7 +10,9 @@
  *      kv_weight bf16[512], cos_sin fp32[max_position*64], positions
  *      int64[T], slot_mapping int64[T], kv_cache u8[pages*64*576],
  *      kv_scale u8[pages*64*8]
- * OUT: q, kv_cache, kv_scale after the call, in that order.
+ * OUT: q, kv_cache, kv_scale after the call, in that order; then, when the
+ *      cache has pages, the cache read back through a block table (one
+ *      sequence covering every page in order): bf16[pages*64*512].
  *
  * Before the real call it makes one call with a NULL kv pointer and checks
  * that the library refuses it (FP8KV_ERR_NULL) with a status string.  Exit
@@ -113,6 +115,39 @@ int main(int argc, char** argv) {
     fprintf(stderr, "call failed: %s\n", fp8kv_status_string(st));
     return 6;
   }
+  /* read the cache back through a block table on the same stream */
+  const size_t nrows = (size_t)(pages * 64), nread = nrows * 512 * 2;
+  void* hread = malloc(nread ? nread : 1);
+  void* dread = NULL;
+  if (pages > 0) {
+    int32_t* htable = (int32_t*)malloc((size_t)pages * sizeof(int32_t));
+    if (!hread || !htable) {
+      fprintf(stderr, "out of host memory\n");
+      return 8;
+    }
+    for (int64_t i = 0; i < pages; ++i) htable[i] = (int32_t)i;
+    const int32_t hlen = (int32_t)nrows;
+    const int64_t hoff = 0;
+    void* dtable = to_device(htable, (size_t)pages * sizeof(int32_t));
+    void* dlen = to_device(&hlen, sizeof hlen);
+    void* doff = to_device(&hoff, sizeof hoff);
+    CHECK_HIP(hipMalloc(&dread, nread));
+    st = kv_cache_gather_dequant_paged(
+        (const uint8_t*)cache, (const uint8_t*)scale, pages, 64,
+        (const int32_t*)dtable, 1, (int32_t)pages, (const int32_t*)dlen,
+        (const int64_t*)doff, (int64_t)nrows, dread, (void*)stream);
+    if (st != FP8KV_OK) {
+      fprintf(stderr, "read-back failed: %s\n", fp8kv_status_string(st));
+      return 9;
+    }
+    CHECK_HIP(hipStreamSynchronize(stream));
+    CHECK_HIP(hipMemcpy(hread, dread, nread, hipMemcpyDeviceToHost));
+    CHECK_HIP(hipFree(dtable));
+    CHECK_HIP(hipFree(dlen));
+    CHECK_HIP(hipFree(doff));
+    CHECK_HIP(hipFree(dread));
+    free(htable);
+  }
   CHECK_HIP(hipStreamSynchronize(stream));
   CHECK_HIP(hipMemcpy(hq, q, nq, hipMemcpyDeviceToHost));
   CHECK_HIP(hipMemcpy(hcache, cache, ncache, hipMemcpyDeviceToHost));
@@ -120,11 +155,13 @@ int main(int argc, char** argv) {
 
   FILE* out = fopen(argv[2], "wb");
   if (!out || fwrite(hq, 1, nq, out) != nq || fwrite(hcache, 1, ncache, out) != ncache ||
-      fwrite(hscale, 1, nscale, out) != nscale) {
+      fwrite(hscale, 1, nscale, out) != nscale ||
+      (pages > 0 && fwrite(hread, 1, nread, out) != nread)) {
     fprintf(stderr, "cannot write %s\n", argv[2]);
     return 7;
   }
   fclose(out);
+  free(hread);
   CHECK_HIP(hipStreamDestroy(stream));
   void* dev[] = {q, kv, qw, kw, cs, pos, slot, cache, scale};
   for (size_t i = 0; i < sizeof dev / sizeof dev[0]; ++i) CHECK_HIP(hipFree(dev[i]));

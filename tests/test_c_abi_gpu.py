@@ -39,9 +39,11 @@ def test_c_caller_matches_oracle(tmp_path, T, H, seed):
     raw = np.fromfile(dst, np.uint8)
     nq = T * H * 512 * 2
     nc = pages * 64 * 576
+    ns = pages * 64 * 8
     q = raw[:nq].view(np.uint16).reshape(T, H, 512)
     cache = raw[nq:nq + nc].reshape(pages, 64, 576)
-    scale = raw[nq + nc:].reshape(pages, 64, 8)
+    scale = raw[nq + nc:nq + nc + ns].reshape(pages, 64, 8)
+    readback = raw[nq + nc + ns:].view(np.uint16).reshape(pages * 64, 512)
 
     ref = {k: (v.copy() if isinstance(v, np.ndarray) else v) for k, v in x.items()}
     O.qnorm_rope_kv_quant_insert(ref["q"], ref["kv"], ref["q_weight"],
@@ -57,3 +59,11 @@ def test_c_caller_matches_oracle(tmp_path, T, H, seed):
                   "C caller cache")
     P.check_untouched(cache, scale, x["slot_mapping"][v], I.CACHE_CANARY,
                       I.SCALE_CANARY, "C caller")
+    # the C caller's block-table read-back of the cache it wrote equals the
+    # oracle's read of those same bytes, bit for bit
+    want = np.zeros((pages * 64, 512), np.uint16)
+    O.kv_cache_gather_dequant_paged(cache.copy(), scale.copy(),
+                                    np.arange(pages, dtype=np.int32)[None, :],
+                                    np.array([pages * 64], np.int32),
+                                    np.array([0], np.int64), want)
+    np.testing.assert_array_equal(readback, want)
