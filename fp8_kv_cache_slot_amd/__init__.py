@@ -29,7 +29,7 @@ PACKED_HEAD_DIM = 128
 
 STATUS = {0: "FP8KV_OK", 1: "FP8KV_ERR_NULL", 2: "FP8KV_ERR_SHAPE",
           3: "FP8KV_ERR_UNSUPPORTED", 4: "FP8KV_ERR_ALIGN",
-          5: "FP8KV_ERR_DEVICE", 6: "FP8KV_ERR_LAUNCH"}
+          5: "FP8KV_ERR_DEVICE", 6: "FP8KV_ERR_LAUNCH", 7: "FP8KV_ERR_VALUE"}
 
 EXPORTED = ["qnorm_rope_kv_quant_insert", "qk_norm_rope_packed",
             "kv_cache_gather_dequant", "rms_norm_rows", "rope_rows",

@@ -81,6 +81,7 @@ int prologue(void* q, const void* kv, const void* q_weight, const void* kv_weigh
              int64_t num_pages, int32_t page_size, float eps, void* stream) {
   // For the scalar-scale convention the scale pointer takes the exponent
   // tensor's place in the NULL check (required when the cache has pages).
+  if (!valid_eps(eps)) return FP8KV_ERR_VALUE;
   const uint8_t* scale_ptr =
       scalar ? reinterpret_cast<const uint8_t*>(scalar_scale) : kv_scale;
   int st = validate_prologue(q, kv, q_weight, kv_weight, cos_sin_cache,
@@ -156,6 +157,7 @@ FP8KV_API int qk_norm_rope_packed(
     const int64_t* position_ids, int32_t forced_token_heads_per_warp,
     int64_t max_position, void* stream) {
   using namespace fp8kv;
+  if (!valid_eps(eps)) return FP8KV_ERR_VALUE;
   int st = validate_packed(qkv, num_tokens, num_heads_q, num_heads_k,
                            num_heads_v, head_dim, q_weight, k_weight,
                            cos_sin_cache, is_neox, position_ids,
@@ -185,6 +187,7 @@ FP8KV_API int qk_norm_rope_packed_ex(
     const int64_t* position_ids, int32_t rotary_dim, int32_t dtype,
     int64_t max_position, void* stream) {
   using namespace fp8kv;
+  if (!valid_eps(eps)) return FP8KV_ERR_VALUE;
   int st = validate_packed_ex(qkv, num_tokens, num_heads_q, num_heads_k,
                               num_heads_v, head_dim, q_weight, k_weight,
                               cos_sin_cache, is_neox, position_ids, rotary_dim,
@@ -314,6 +317,7 @@ FP8KV_API int rms_norm_rows(const void* x, void* out, const void* weight,
                             int64_t num_rows, int32_t row_dim, float eps,
                             void* stream) {
   using namespace fp8kv;
+  if (!valid_eps(eps)) return FP8KV_ERR_VALUE;
   int st = validate_rms_norm_rows(x, out, weight, num_rows, row_dim);
   if (st != FP8KV_OK || num_rows == 0) return st;
   st = check_device();
@@ -388,6 +392,7 @@ FP8KV_API const char* fp8kv_status_string(int status) {
     case FP8KV_ERR_ALIGN: return "pointer not aligned as required";
     case FP8KV_ERR_DEVICE: return "no current HIP device or device is not gfx950";
     case FP8KV_ERR_LAUNCH: return "kernel launch failed";
+    case FP8KV_ERR_VALUE: return "eps is negative, infinite or NaN";
     default: return "unknown status";
   }
 }

@@ -19,6 +19,11 @@ inline bool aligned(const void* p, uintptr_t a) {
   return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0;
 }
 
+// eps must be finite and non-negative (a NaN fails both comparisons).
+inline bool valid_eps(float eps) {
+  return eps >= 0.0f && eps <= 3.4028234663852886e38f;
+}
+
 inline int validate_prologue(const void* q, const void* kv,
                              const void* q_weight, const void* kv_weight,
                              const float* cos_sin_cache,

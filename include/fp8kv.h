@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define FP8KV_ABI_VERSION 1
+#define FP8KV_ABI_VERSION 2
 
 enum fp8kv_status {
   FP8KV_OK = 0,
@@ -53,7 +53,8 @@ enum fp8kv_status {
   FP8KV_ERR_UNSUPPORTED = 3, /* a layout parameter other than the supported one */
   FP8KV_ERR_ALIGN = 4,       /* a pointer is not aligned as documented          */
   FP8KV_ERR_DEVICE = 5,      /* no current HIP device, or it is not gfx950      */
-  FP8KV_ERR_LAUNCH = 6       /* the kernel launch itself failed                 */
+  FP8KV_ERR_LAUNCH = 6,      /* the kernel launch itself failed                 */
+  FP8KV_ERR_VALUE = 7        /* eps is negative, infinite or NaN                */
 };
 
 /*
@@ -92,7 +93,9 @@ enum fp8kv_status {
  *                  (amax 0 gives -127).  Byte 7 is never written.  One
  *                  exponent for each of a token's seven blocks: FlagGems
  *                  PR #5449, "Performance".
- *   eps            added to the mean square inside the square root.
+ *   eps            added to the mean square inside the square root; finite
+ *                  and >= 0 (FP8KV_ERR_VALUE otherwise).  With eps = 0 an
+ *                  all-zero head is 0/0 and its outputs are NaN.
  *
  * Per token t, for each Q head and then for the KV head x (with its weight w):
  *   y_d = x_d / sqrt(mean_d(x_d^2) + eps) * w_d            (fp32)
@@ -145,7 +148,8 @@ int qnorm_rope_kv_quant_insert_scalar_scale(
  *   num_heads_q/k/v  Hq >= 0, Hk >= 0, Hv >= 0, Hq + Hk >= 1.
  *   head_dim      D = 128 (the page's guarded fast path; others ->
  *                 FP8KV_ERR_UNSUPPORTED).
- *   eps           added inside the square root.
+ *   eps           added inside the square root; finite and >= 0
+ *                 (FP8KV_ERR_VALUE otherwise).
  *   q_weight      bf16 [D] for Q heads; k_weight bf16 [D] for K heads;
  *                 separate one-dimensional tensors as on the page.  16-B
  *                 aligned.

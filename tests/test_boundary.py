@@ -33,7 +33,7 @@ def test_header_declarations_are_exported():
     for n in names:
         assert hasattr(lib, n), n
     assert sorted(names) == sorted(K.EXPORTED)
-    assert K.abi_version() == 1
+    assert K.abi_version() == 2
 
 
 def test_exports_nothing_else():
@@ -45,7 +45,7 @@ def test_exports_nothing_else():
 
 
 def test_status_strings():
-    for s in range(7):
+    for s in range(8):
         assert K.lib().fp8kv_status_string(s).decode()
     assert K.lib().fp8kv_status_string(99) == b"unknown status"
 
@@ -94,6 +94,15 @@ def test_prologue_argument_errors(over, want):
 ])
 def test_packed_argument_errors(over, want):
     assert _packed(**over) == want
+
+
+@pytest.mark.parametrize("eps", [-1e-6, float("nan"), float("inf"), -float("inf")])
+def test_eps_must_be_finite_and_non_negative(eps):
+    # every entry point that takes eps refuses these before anything else
+    assert _prologue(eps=eps) == 7 and _prologue(eps=eps, T=0) == 7
+    assert _prologue_scalar(eps=eps) == 7
+    assert _packed(eps=eps) == 7 and _packed_ex(eps=eps) == 7
+    assert _norm(eps=eps) == 7
 
 
 def _prologue_scalar(**over):
