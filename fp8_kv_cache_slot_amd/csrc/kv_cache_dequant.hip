@@ -25,80 +25,80 @@ namespace {
 
 constexpr int kRopeLane0 = 56;
 
-// One group of RS rows as loaded.  Every lane issues the same three loads per
-// row, with no branch around them (so they stay in flight while other work
-// runs): 8 code bytes at dims 8 min(l, 55).., the rotary vector of lane
-// 56 + (l & 7), and the exponent byte of block l >> 3 (lanes 56..63 read the
-// unused byte 7 of the 8-byte exponent row).  Each lane keeps what it needs.
-// A row whose slot is invalid reads slot 0 (the cache has pages here) and is
-// stored as zeros.
+// One group of RS rows as loaded.  Each lane issues one 16-byte load per
+// row: lane l < 56 reads bytes 8l..8l+15 of the row and keeps the low 8 (its
+// codes; lane 55 ends at byte 455, inside the 576-byte row), lanes 56..63
+// read the rotary vector 448 + 16 (l - 56).  The row's 8 exponent bytes are
+// one wave-uniform (scalar) load.  A row whose slot is invalid reads slot 0
+// (the cache has pages here) and is stored as zeros.
+//
+// All of a group's loads are issued before anything waits on them or
+// branches: the empty asm statements below take the loaded registers as
+// operands, so hipcc cannot sink a row's loads below the per-row store
+// conditions (it did, and then each row waited for its own round trip).
 template <int RS>
 struct Rows {
-  u32x2_t codes[RS];
-  u32x4_t rope[RS];
-  uint32_t ebyte[RS];
+  u32x4_t v[RS];
+  uint64_t ev[RS];
 };
 
 __device__ __forceinline__ bool slot_valid(int64_t s, int64_t num_cache_slots) {
   return s >= 0 && s < num_cache_slots;
 }
 
+__device__ __forceinline__ int row_offset(int lane) {
+  return lane < kRopeLane0 ? lane * 8 : 448 + (lane - kRopeLane0) * 16;
+}
+
+// Rows at slots s[0..RS), each already in [0, num_cache_slots).
 template <int RS, bool SCALAR>
 __device__ __forceinline__ void load_rows(const uint8_t* __restrict__ kv_cache,
                                           const uint8_t* __restrict__ kv_scale,
-                                          const int64_t* s, int64_t num_cache_slots,
-                                          int lane, Rows<RS>& d) {
-  const int cl = lane < kRopeLane0 ? lane : kRopeLane0 - 1;
+                                          const int64_t* slot, int lane,
+                                          Rows<RS>& d) {
+  const int off = row_offset(lane);
 #pragma unroll
   for (int r = 0; r < RS; ++r) {
-    const int64_t slot = slot_valid(s[r], num_cache_slots) ? s[r] : 0;
-    const uint8_t* row = kv_cache + slot * 576;
-    d.codes[r] = *reinterpret_cast<const u32x2_t*>(row + cl * 8);
-    d.rope[r] = *reinterpret_cast<const u32x4_t*>(row + 448 + (lane & 7) * 16);
+    d.v[r] = *reinterpret_cast<const u32x4_t*>(kv_cache + slot[r] * 576 + off);
+    d.ev[r] = SCALAR ? 0u : *reinterpret_cast<const uint64_t*>(kv_scale + slot[r] * 8);
+  }
+#pragma unroll
+  for (int r = 0; r < RS; ++r) {
     if constexpr (SCALAR)
-      d.ebyte[r] = 0u;
+      __asm__ volatile("" : "+v"(d.v[r]));
     else
-      d.ebyte[r] = kv_scale[slot * 8 + (lane >> 3)];
+      __asm__ volatile("" : "+v"(d.v[r]), "+s"(d.ev[r]));
   }
 }
 
-// Dequantise and store the RS rows of group grp (rows grp*RS ..); fs is the
-// scalar scale (SCALAR) or unused.
-template <int RS, bool SCALAR>
-__device__ __forceinline__ void store_rows(const Rows<RS>& d, const int64_t* s,
-                                           float fs, uint16_t* __restrict__ out,
-                                           int32_t grp, int32_t num_rows,
-                                           int64_t num_cache_slots, int lane) {
+// Output vector of row r for this lane: decoded codes (lanes < 56) or the
+// stored rotary vector; fs is the scalar scale (SCALAR) or unused.
+template <bool SCALAR>
+__device__ __forceinline__ u32x4_t dequant_vector(u32x4_t v, uint64_t ev, float fs,
+                                                  int lane) {
+  const int sh = (lane >> 3) * 8;  // exponent byte of block l >> 3
+  const uint32_t w = sh < 32 ? static_cast<uint32_t>(ev) : static_cast<uint32_t>(ev >> 32);
+  const int e = static_cast<int>((w >> (sh & 31)) & 0xFFu) - 127;
+  const int lo = static_cast<int>(v[0]);
+  const int hi = static_cast<int>(v[1]);
+  const float2_t p[4] = {__builtin_amdgcn_cvt_pk_f32_fp8(lo, false),
+                         __builtin_amdgcn_cvt_pk_f32_fp8(lo, true),
+                         __builtin_amdgcn_cvt_pk_f32_fp8(hi, false),
+                         __builtin_amdgcn_cvt_pk_f32_fp8(hi, true)};
+  float f[8];
 #pragma unroll
-  for (int r = 0; r < RS; ++r) {
-    const int32_t i = grp * RS + r;
-    if (i >= num_rows) break;
-    const int e = static_cast<int>(d.ebyte[r]) - 127;
-    const int lo = static_cast<int>(d.codes[r][0]);
-    const int hi = static_cast<int>(d.codes[r][1]);
-    const float2_t p[4] = {__builtin_amdgcn_cvt_pk_f32_fp8(lo, false),
-                           __builtin_amdgcn_cvt_pk_f32_fp8(lo, true),
-                           __builtin_amdgcn_cvt_pk_f32_fp8(hi, false),
-                           __builtin_amdgcn_cvt_pk_f32_fp8(hi, true)};
-    float v[8];
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      if constexpr (SCALAR) {
-        v[2 * k] = p[k][0] * fs;
-        v[2 * k + 1] = p[k][1] * fs;
-      } else {
-        v[2 * k] = __builtin_ldexpf(p[k][0], e);
-        v[2 * k + 1] = __builtin_ldexpf(p[k][1], e);
-      }
+  for (int k = 0; k < 4; ++k) {
+    if constexpr (SCALAR) {
+      f[2 * k] = p[k][0] * fs;
+      f[2 * k + 1] = p[k][1] * fs;
+    } else {
+      f[2 * k] = __builtin_ldexpf(p[k][0], e);
+      f[2 * k + 1] = __builtin_ldexpf(p[k][1], e);
     }
-    const u32x4_t q = {pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3]),
-                       pack_bf16(v[4], v[5]), pack_bf16(v[6], v[7])};
-    const u32x4_t z = {0u, 0u, 0u, 0u};
-    const u32x4_t o = slot_valid(s[r], num_cache_slots)
-                          ? (lane < kRopeLane0 ? q : d.rope[r])
-                          : z;
-    store16<true>(out + static_cast<int64_t>(i) * 512 + lane * 8, o);
   }
+  const u32x4_t q = {pack_bf16(f[0], f[1]), pack_bf16(f[2], f[3]),
+                     pack_bf16(f[4], f[5]), pack_bf16(f[6], f[7])};
+  return lane < kRopeLane0 ? q : v;
 }
 
 // SCALAR: the scalar-scale convention, out = E4M3(code) * scalar_scale[0]
@@ -106,15 +106,16 @@ __device__ __forceinline__ void store_rows(const Rows<RS>& d, const int64_t* s,
 //
 // The gather is a chain of two dependent loads: the slots, then the rows.
 // Each one-wave block takes one group of RS consecutive rows: the RS slot
-// indices are wave-uniform (one scalar load), then every lane issues the
-// group's row loads with no branch in front of them, and the rows are
-// dequantised and stored.  Many small one-shot blocks keep enough groups in
-// flight to hide the two round trips.  Measured on MI355X over all 131072
-// slots of a 2048-page cache in random order, caches cold and clean: 41.9 us
-// with 4 rows per one-wave block, against 43.6 us with 2 rows, 42.8 with 8,
-// 52.2 with 1, 42.3 with two waves of 4 rows and 44.1 with four waves of 2;
-// and against 43.9 us for a persistent form in which each wave looped over
-// its share of the groups with the next group's loads in flight.
+// indices are wave-uniform (scalar loads), then every lane issues the group's
+// row loads, and the rows are dequantised and stored.  Many small one-shot
+// blocks keep enough groups in flight to hide the two round trips.  Measured
+// on MI355X over all 131072 slots of a 2048-page cache in random order,
+// caches cold and clean: 40.0 us with 2 rows per one-wave block, against
+// 41.0 with 4 and 41.7 with 8; a plain streaming kernel with the same bytes
+// per row (576 read, 1024 written, contiguous rows, no arithmetic) takes
+// 40.1 us.  The form before (three loads per row: codes, rotary vector and
+// exponent byte, some sunk below the store conditions) took 42.0 us, and a
+// persistent form with the next group's loads in flight 43.9 us.
 template <int RS, bool SCALAR>
 __global__ void __launch_bounds__(64) kv_cache_gather_dequant_kernel(
     const uint8_t* __restrict__ kv_cache, const uint8_t* __restrict__ kv_scale,
@@ -123,8 +124,8 @@ __global__ void __launch_bounds__(64) kv_cache_gather_dequant_kernel(
   const int lane = lane_id();
   const int32_t grp = static_cast<int32_t>(blockIdx.x);
   if (grp * RS >= num_rows) return;
+  const u32x4_t z = {0u, 0u, 0u, 0u};
   if (num_cache_slots <= 0) {  // a cache without pages: every row is zero
-    const u32x4_t z = {0u, 0u, 0u, 0u};
 #pragma unroll
     for (int r = 0; r < RS; ++r) {
       const int32_t i = grp * RS + r;
@@ -134,22 +135,35 @@ __global__ void __launch_bounds__(64) kv_cache_gather_dequant_kernel(
   }
   // Rows past the last one re-read the last slot (in bounds) and are not
   // stored.
-  int64_t s[RS];
+  int64_t s[RS], slot[RS];
 #pragma unroll
   for (int r = 0; r < RS; ++r) {
     int32_t i = grp * RS + r;
     if (i > num_rows - 1) i = num_rows - 1;
     s[r] = slots[i];
   }
+  // all slot loads in flight together
+#pragma unroll
+  for (int r = 0; r < RS; ++r) __asm__ volatile("" : "+s"(s[r]));
+#pragma unroll
+  for (int r = 0; r < RS; ++r) slot[r] = slot_valid(s[r], num_cache_slots) ? s[r] : 0;
   // with pages, the scalar scale pointer is a checked device pointer
   float fs = 1.0f;
   if constexpr (SCALAR) fs = *scalar_scale;
   Rows<RS> d;
-  load_rows<RS, SCALAR>(kv_cache, kv_scale, s, num_cache_slots, lane, d);
-  store_rows<RS, SCALAR>(d, s, fs, out, grp, num_rows, num_cache_slots, lane);
+  load_rows<RS, SCALAR>(kv_cache, kv_scale, slot, lane, d);
+#pragma unroll
+  for (int r = 0; r < RS; ++r) {
+    const int32_t i = grp * RS + r;
+    if (i >= num_rows) break;
+    const u32x4_t o = slot_valid(s[r], num_cache_slots)
+                          ? dequant_vector<SCALAR>(d.v[r], d.ev[r], fs, lane)
+                          : z;
+    store16<true>(out + static_cast<int64_t>(i) * 512 + lane * 8, o);
+  }
 }
 
-constexpr int kDequantRows = 4;
+constexpr int kDequantRows = 2;
 
 // The read side through block tables, as an attention consumer indexes the
 // cache: token j of sequence s sits in slot
@@ -157,10 +171,11 @@ constexpr int kDequantRows = 4;
 // out[out_offsets[s] + j].  Grid: x = groups of PRS consecutive tokens of a
 // sequence (covering max_blocks_per_seq pages), y = sequence.  PRS divides 64,
 // so a wave's rows are consecutive slots of one page (PRS * 576 contiguous
-// bytes).  The page id, length and output offset are three independent
-// loads; every lane then issues its row loads with no branch in front of
-// them (an invalid page reads slot 0 and stores zero rows, as in the slot-list
-// kernel), and only the stores depend on the length and the output bounds.
+// bytes, and PRS * 8 contiguous exponent bytes).  The page id, length and
+// output offset are three independent scalar loads, all issued before the
+// wave branches on the length; the row loads follow (an invalid page reads
+// slots 0.. and stores zero rows, as in the slot-list kernel), and only the
+// stores depend on the length and the output bounds.
 //
 // SCALAR: the scalar-scale convention, as in the slot-list kernel (no exponent
 // bytes read; codes times scalar_scale[0], rounded to fp32, then to bf16).
@@ -176,10 +191,13 @@ __global__ void __launch_bounds__(WAVES * 64) kv_cache_gather_dequant_paged_kern
   const int32_t seq = static_cast<int32_t>(blockIdx.y);
   // j0 < max_blocks_per_seq * 64: the grid covers exactly that many tokens
   const int32_t j0 = (static_cast<int32_t>(blockIdx.x) * WAVES + wave_id()) * PRS;
-  const int64_t page =
-      block_table[static_cast<int64_t>(seq) * max_blocks_per_seq + j0 / 64];
-  const int32_t len = seq_lens[seq];
-  const int64_t first = out_offsets[seq] + j0;
+  int32_t page = block_table[static_cast<int64_t>(seq) * max_blocks_per_seq + j0 / 64];
+  int32_t len = seq_lens[seq];
+  int64_t first = out_offsets[seq];
+  // all three loads in flight together (hipcc otherwise waits for the length
+  // and branches before it asks for the other two)
+  __asm__ volatile("" : "+s"(page), "+s"(len), "+s"(first));
+  first += j0;
   if (j0 >= len) return;
 
   const u32x4_t z = {0u, 0u, 0u, 0u};
@@ -193,51 +211,32 @@ __global__ void __launch_bounds__(WAVES * 64) kv_cache_gather_dequant_paged_kern
     return;
   }
   const bool page_ok = page >= 0 && page < num_pages;
-  const int64_t slot0 = (page_ok ? page : 0) * 64 + j0 % 64;
-  int64_t sl[PRS];
+  const int64_t slot0 = page_ok ? static_cast<int64_t>(page) * 64 + j0 % 64 : 0;
+  int64_t slot[PRS];
 #pragma unroll
-  for (int r = 0; r < PRS; ++r) sl[r] = page_ok ? slot0 + r : -1;
+  for (int r = 0; r < PRS; ++r) slot[r] = slot0 + r;
   // with pages, the scalar scale pointer is a checked device pointer
   float fs = 1.0f;
   if constexpr (SCALAR) fs = *scalar_scale;
   Rows<PRS> d;
-  load_rows<PRS, SCALAR>(kv_cache, kv_scale, sl, num_pages * 64, lane, d);
+  load_rows<PRS, SCALAR>(kv_cache, kv_scale, slot, lane, d);
 #pragma unroll
   for (int r = 0; r < PRS; ++r) {
     const int64_t i = first + r;
     if (j0 + r >= len || i < 0 || i >= num_rows) continue;
-    const int e = static_cast<int>(d.ebyte[r]) - 127;
-    const int lo = static_cast<int>(d.codes[r][0]);
-    const int hi = static_cast<int>(d.codes[r][1]);
-    const float2_t p[4] = {__builtin_amdgcn_cvt_pk_f32_fp8(lo, false),
-                           __builtin_amdgcn_cvt_pk_f32_fp8(lo, true),
-                           __builtin_amdgcn_cvt_pk_f32_fp8(hi, false),
-                           __builtin_amdgcn_cvt_pk_f32_fp8(hi, true)};
-    float v[8];
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      if constexpr (SCALAR) {
-        v[2 * k] = p[k][0] * fs;
-        v[2 * k + 1] = p[k][1] * fs;
-      } else {
-        v[2 * k] = __builtin_ldexpf(p[k][0], e);
-        v[2 * k + 1] = __builtin_ldexpf(p[k][1], e);
-      }
-    }
-    const u32x4_t q = {pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3]),
-                       pack_bf16(v[4], v[5]), pack_bf16(v[6], v[7])};
-    const u32x4_t o = page_ok ? (lane < kRopeLane0 ? q : d.rope[r]) : z;
+    const u32x4_t o = page_ok ? dequant_vector<SCALAR>(d.v[r], d.ev[r], fs, lane) : z;
     store16<true>(out + i * 512 + lane * 8, o);
   }
 }
 
-// 2 waves of 8 rows (4.6 KiB of contiguous cache rows per wave).  Measured
-// on MI355X over all 2048 pages of a cache in a random page order, caches
-// cold and clean: 42.5 us for 32 x 4096 and for 256 x 512 tokens, against
-// 43.5-44.7 us for 4 x 4, 43.5-43.9 for 4 x 8, 44.5-45.5 for 8 x 4 and
-// 46-49 us for 4 x 2 and 4 x 16 (waves x rows per wave).
-constexpr int kPagedWaves = 2;
-constexpr int kPagedRows = 8;
+// One wave of 2 rows per block.  Measured on MI355X over all 2048 pages of a
+// cache in a random page order, caches cold and clean: 40.3 us for 32 x 4096
+// and 39.9 us for 256 x 512 tokens, against 40.6 for 1 x 4 and 2 x 4, 40.5-
+// 40.7 for 4 x 4, 41.0-41.2 for 1 x 8 and 2 x 8 (waves x rows per wave); the
+// form before (three loads per row, the length waited for before the page id
+// was asked for) took 42.4 and 42.9 us.
+constexpr int kPagedWaves = 1;
+constexpr int kPagedRows = 2;
 
 }  // namespace
 
