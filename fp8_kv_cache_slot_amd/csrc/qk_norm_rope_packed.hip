@@ -42,6 +42,15 @@ __attribute__((amdgpu_waves_per_eu(8, 8))) qk_norm_rope_packed_kernel(
   const int l16 = lane & 15;
   const int32_t nh = num_heads_q + num_heads_k;
 
+  // Load order: the U head loads, then both weight vectors, then the
+  // position and (depending on it) the cos/sin row, with nothing between them
+  // that waits.  A weight of a group without heads may be null, so that group
+  // borrows the other pointer (Hq + Hk >= 1, so one is non-null).  Loading a
+  // weight only when its group has heads put a branch and a wait for every
+  // outstanding load between the head loads and the position load; and a
+  // branch on whether a wave's first access holds a head (it always does) let
+  // hipcc sink the head loads below the position's round trip.  Heads past
+  // the last one re-read head 0 (in bounds) and are not stored.
   uint16_t* base = qkv + static_cast<int64_t>(t) * row_elems + l16 * 8;
   u32x4_t x[U];
 #pragma unroll
@@ -50,11 +59,9 @@ __attribute__((amdgpu_waves_per_eu(8, 8))) qk_norm_rope_packed_kernel(
     x[u] = load16<true>(base + (h < nh ? h : 0) * 128);  // in bounds
   }
 
-  float wq[8], wk[8];
-#pragma unroll
-  for (int j = 0; j < 8; ++j) wq[j] = wk[j] = 0.0f;
-  if (num_heads_q > 0) unpack8(load16<false>(q_weight + l16 * 8), wq);
-  if (num_heads_k > 0) unpack8(load16<false>(k_weight + l16 * 8), wk);
+  const u32x4_t wqr = load16<false>((num_heads_q > 0 ? q_weight : k_weight) + l16 * 8);
+  const u32x4_t wkr = load16<false>((num_heads_k > 0 ? k_weight : q_weight) + l16 * 8);
+  __builtin_amdgcn_sched_barrier(0);  // keep the position load after these
   // A position out of range makes the stores, not an early return,
   // conditional: no branch on the position sits in front of the head loads.
   // Its cos/sin reads use row 0.
@@ -77,15 +84,16 @@ __attribute__((amdgpu_waves_per_eu(8, 8))) qk_norm_rope_packed_kernel(
 
 #pragma unroll
   for (int u = 0; u < U; ++u) {
-    if (h0 + 4 * u >= nh) break;  // no head of this access exists
     const int32_t h = h0 + 4 * u + g;
     float f[8], n[8];
     unpack8(x[u], f);
     const float ss = row16_sum(sum_sq8(f));
     const float r = __builtin_amdgcn_rsqf(fmaf(ss, 1.0f / 128.0f, eps));
     const bool is_q = h < num_heads_q;
+    float w[8];
+    unpack8(is_q ? wqr : wkr, w);
 #pragma unroll
-    for (int j = 0; j < 8; ++j) n[j] = f[j] * r * (is_q ? wq[j] : wk[j]);
+    for (int j = 0; j < 8; ++j) n[j] = f[j] * r * w[j];
     float o[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
@@ -108,6 +116,7 @@ __attribute__((amdgpu_waves_per_eu(8, 8))) qk_norm_rope_packed_kernel(
 // 24 heads in one wave 34.7 us (register-limited).  At 17 tokens 6.7 us
 // against 7.0 us with four waves per block.  With four waves per block the
 // position read before the head loads cost 1.5 us at 8192 tokens (27.5 us).
+// The load order above took the kernel from 23.6 to 23.1 us at 8192 tokens.
 constexpr int kPackedWaves = 1;
 constexpr int kPackedUnroll = 3;
 

@@ -89,65 +89,70 @@ __global__ void __launch_bounds__(WAVES * 64) qk_norm_rope_packed_ex_kernel(
   const int32_t nh = num_heads_q + num_heads_k;
   uint16_t* base = qkv + static_cast<int64_t>(t) * row_elems + lh * 8;
 
-  // The head loads go out before the position load, so the position and
-  // cos/sin loads overlap them.  A position out of range makes the token's
-  // stores, not an early return, conditional, so that no branch on the
-  // position sits in front of the loads; its cos/sin reads use row 0.  Heads
-  // past the last one re-read head 0 (in bounds) and are not stored.
+  // Load order: the U head loads, both weight vectors, then the position and
+  // (depending on it) the cos/sin row, with nothing between them that waits.
+  // A weight of a group without heads may be null, so that group borrows the
+  // other pointer (Hq + Hk >= 1).  Every lane loads cos/sin, at offset 0
+  // outside the rotary dims, behind a test of rotary_dim > 0 only (uniform),
+  // and selects afterwards.  (Branches around the weight loads and around
+  // the cos/sin loads of the rotary lanes each added a wait for every
+  // outstanding load; a branch on the wave's first access holding a head,
+  // which it always does, let hipcc sink the head loads below the position's
+  // round trip.)  A position out of range makes the token's stores, not an
+  // early return, conditional; its cos/sin reads use row 0.  Heads past the
+  // last one re-read head 0 (in bounds) and are not stored.
   u32x4_t x[U];
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     const int32_t h = h0 + u * HPW + g;
     x[u] = load16<true>(base + static_cast<int64_t>(h < nh ? h : 0) * D);
   }
+  const u32x4_t wqr = load16<false>((num_heads_q > 0 ? q_weight : k_weight) + lh * 8);
+  const u32x4_t wkr = load16<false>((num_heads_k > 0 ? k_weight : q_weight) + lh * 8);
+  __builtin_amdgcn_sched_barrier(0);  // keep the position load after these
   const int64_t pos_in = position_ids[t];
   const bool valid = pos_in >= 0 && pos_in < max_position;
   const int64_t pos = valid ? pos_in : 0;
-
-  float wq[8], wk[8];
-#pragma unroll
-  for (int j = 0; j < 8; ++j) wq[j] = wk[j] = 0.0f;
-  if (num_heads_q > 0) unpack8_any<FP16>(load16<false>(q_weight + lh * 8), wq);
-  if (num_heads_k > 0) unpack8_any<FP16>(load16<false>(k_weight + lh * 8), wk);
 
   // Rotation coefficients of this lane: identity outside the rotary dims.
   const int rot_lanes = rotary_dim / 8;
   const bool rotary = lh < rot_lanes;
   float c[8], s[8];
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    c[j] = 1.0f;
-    s[j] = 0.0f;
-  }
   int partner = lane;
-  if (rotary) {
-    const float* row = cos_sin + pos * rotary_dim;
-    const int half = rotary_dim / 2;
-    if constexpr (NEOX) {
-      // dims 8lh.. pair with dims 8lh +- R/2, R/16 lanes away; the first half
-      // takes n c - n' s, the second half n c + n' s
-      const bool first = lh < rot_lanes / 2;
-      const int i0 = first ? 8 * lh : 8 * lh - half;
-      const f32x4_t c0 = load16f(row + i0), c1 = load16f(row + i0 + 4);
-      const f32x4_t s0 = load16f(row + half + i0), s1 = load16f(row + half + i0 + 4);
-      const float sg = first ? -1.0f : 1.0f;
+  const int half = rotary_dim / 2;
+  const float* row = cos_sin + pos * rotary_dim;
+  if constexpr (NEOX) {
+    // dims 8lh.. pair with dims 8lh +- R/2, R/16 lanes away; the first half
+    // takes n c - n' s, the second half n c + n' s.  i0 <= R/2 - 8, so every
+    // read stays inside the row (R >= 16 whenever R > 0).
+    const bool first = lh < rot_lanes / 2;
+    const int i0 = !rotary ? 0 : (first ? 8 * lh : 8 * lh - half);
+    f32x4_t c0 = {1.f, 1.f, 1.f, 1.f}, c1 = c0, s0 = {0.f, 0.f, 0.f, 0.f}, s1 = s0;
+    if (rotary_dim > 0) {
+      c0 = load16f(row + i0); c1 = load16f(row + i0 + 4);
+      s0 = load16f(row + half + i0); s1 = load16f(row + half + i0 + 4);
+    }
+    const float sg = first ? -1.0f : 1.0f;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        c[j] = c0[j];
-        c[4 + j] = c1[j];
-        s[j] = sg * s0[j];
-        s[4 + j] = sg * s1[j];
-      }
-      partner = first ? lane + rot_lanes / 2 : lane - rot_lanes / 2;
-    } else {
-      // pairs 4lh .. 4lh+3 inside the lane
-      const f32x4_t cc = load16f(row + 4 * lh), ss = load16f(row + half + 4 * lh);
+    for (int j = 0; j < 4; ++j) {
+      c[j] = rotary ? c0[j] : 1.0f;
+      c[4 + j] = rotary ? c1[j] : 1.0f;
+      s[j] = rotary ? sg * s0[j] : 0.0f;
+      s[4 + j] = rotary ? sg * s1[j] : 0.0f;
+    }
+    if (rotary) partner = first ? lane + rot_lanes / 2 : lane - rot_lanes / 2;
+  } else {
+    // pairs 4lh .. 4lh+3 inside the lane
+    const int i0 = rotary ? 4 * lh : 0;
+    f32x4_t cc = {1.f, 1.f, 1.f, 1.f}, ss = {0.f, 0.f, 0.f, 0.f};
+    if (rotary_dim > 0) {
+      cc = load16f(row + i0); ss = load16f(row + half + i0);
+    }
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        c[2 * k] = c[2 * k + 1] = cc[k];
-        s[2 * k] = -ss[k];      // a' = a c - b s
-        s[2 * k + 1] = ss[k];   // b' = b c + a s
-      }
+    for (int k = 0; k < 4; ++k) {
+      c[2 * k] = c[2 * k + 1] = rotary ? cc[k] : 1.0f;
+      s[2 * k] = rotary ? -ss[k] : 0.0f;
+      s[2 * k + 1] = rotary ? ss[k] : 0.0f;
     }
   }
   const int partner_addr = partner * 4;  // ds_bpermute byte address
@@ -155,14 +160,15 @@ __global__ void __launch_bounds__(WAVES * 64) qk_norm_rope_packed_ex_kernel(
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     const int32_t h = h0 + u * HPW + g;
-    if (h0 + u * HPW >= nh) break;  // no head of this access exists
     float f[8], n[8], o[8];
     unpack8_any<FP16>(x[u], f);
     const float ss = head_sum<LPH>(sum_sq8(f));
     const float r = __builtin_amdgcn_rsqf(fmaf(ss, 1.0f / D, eps));
     const bool is_q = h < num_heads_q;
+    float w[8];
+    unpack8_any<FP16>(is_q ? wqr : wkr, w);
 #pragma unroll
-    for (int j = 0; j < 8; ++j) n[j] = f[j] * r * (is_q ? wq[j] : wk[j]);
+    for (int j = 0; j < 8; ++j) n[j] = f[j] * r * w[j];
     if constexpr (NEOX) {
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
@@ -192,7 +198,9 @@ __global__ void __launch_bounds__(WAVES * 64) qk_norm_rope_packed_ex_kernel(
 // interleaved bf16 23.3 us, against 15.7 / 44.1 / 26.1 us for one wave per
 // token walking its heads in batches of four accesses (four waves per
 // block).  Two accesses per wave: 17.5 / 43.2 / 25.8 us; four: 14.0 / 41.4 /
-// 24.9 us; four waves per block: 14.4 / 41.2 / 24.2 us.
+// 24.9 us; four waves per block: 14.4 / 41.2 / 24.2 us.  Those figures
+// predate the load order above, which took the three forms from 14.2 / 41.8
+// / 23.1 us to 13.6 / 37.7 / 22.2 us.
 constexpr int kExWaves = 1;
 constexpr int kExUnroll = 3;
 
