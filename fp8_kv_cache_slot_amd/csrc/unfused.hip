@@ -29,8 +29,11 @@ namespace {
 // pipeline took 800 us at 32768 x 64 with this shape on MI355X (caches cold),
 // against 816 us with four waves of two rows, 824 us with one row per
 // one-wave block and 834 us with two waves of one row; within 1 us of each
-// other at 1024 x 64 (38.3-39.5 us).  The baseline is tuned like the fused
-// kernel it is compared with.
+// other at 1024 x 64 (38.3-39.5 us).  Issuing the RoPE stage's row load
+// before its position wait and the quantiser's row load with its slot load
+// (below) then took the pipeline from 802.6 to 797.4 us (38.9 to 38.1 us at
+// 1024 x 64).  The baseline is tuned like the fused kernel it is compared
+// with.
 constexpr int kWaves = 1;
 constexpr int kRowsPerWave = 2;
 
@@ -85,6 +88,8 @@ __global__ void __launch_bounds__(kWaves * 64) rope_rows_kernel(
   // An out-of-range position turns off the store (row 0's angles are read
   // instead), so no branch on the loaded position sits behind the row load.
   const int64_t pos_in = positions[t];
+  // keep the row load in front of the wait for the position
+  __builtin_amdgcn_sched_barrier(0);
   const bool ok = pos_in >= 0 && pos_in < max_position;
   const int64_t pos = ok ? pos_in : 0;
   const f32x4_t c = load16f(cos_sin + pos * 64 + j * 4);
@@ -111,10 +116,14 @@ __global__ void __launch_bounds__(kWaves * 64) kv_quant_insert_kernel(
   const int32_t t = static_cast<int32_t>(blockIdx.x) * kWaves + wave_id();
   if (t >= num_tokens) return;
   // The row load goes out with the slot load; a skipped slot turns off the
-  // stores rather than returning in front of the row load.
+  // stores rather than returning in front of the row load.  The empty asm
+  // statement takes both loaded values, so hipcc cannot sink the row load
+  // below the test of the slot (it did, and the row then waited for it).
+  u32x4_t raw = load16<true>(kv + static_cast<int64_t>(t) * 512 + lane * 8);
+  int64_t slot = slot_mapping[t];
+  __asm__ volatile("" : "+v"(raw), "+s"(slot));
   float y[8];
-  unpack8(load16<true>(kv + static_cast<int64_t>(t) * 512 + lane * 8), y);
-  const int64_t slot = slot_mapping[t];
+  unpack8(raw, y);
   if (slot >= 0 && slot < num_cache_slots)
     quantise_store_row(y, lane, kv_cache + slot * 576, kv_scale + slot * 8);
 }
