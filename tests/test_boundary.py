@@ -390,3 +390,17 @@ def test_generators_shapes_and_slot_maps():
     p = I.make_packed(I.PACKED_WORKLOADS["packed_t17"], "cpu")
     assert p["qkv"].shape == (17, 32 * 128)
     assert p["cos_sin_cache"].shape == (8192, 128)
+
+
+@pytest.mark.parametrize("gpus", ["2", "8"])
+def test_bench_refuses_more_than_one_gpu(gpus):
+    """bench.py measures one GPU: any other --gpus exits with status 2 and a
+    message, before touching a device."""
+    import subprocess
+    import sys
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"),
+                        "--gpus", gpus], capture_output=True, text=True,
+                       timeout=120)
+    assert r.returncode == 2
+    assert "one GPU only" in r.stderr
+    assert r.stdout == ""
