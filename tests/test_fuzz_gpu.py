@@ -4,7 +4,10 @@ eps, the built tiling and the dispatch side for the fused prologue; head
 width, rotary width, pairing, dtype and head mix for the packed forms), so
 combinations no hand-written case names get checked too.  Every case is
 deterministic in its seed and small enough for the oracle to finish in well
-under a second.  Needs an MI355X."""
+under a second.  Needs an MI355X.  FP8KV_FUZZ_CASES sets the number of
+cases of each kind (default 128)."""
+
+import os
 
 import numpy as np
 import pytest
@@ -17,6 +20,7 @@ from tests import parity as P
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
+CASES = int(os.environ.get("FP8KV_FUZZ_CASES", "128"))
 SHAPES = [(1, 1), (1, 2), (2, 1), (2, 2), (4, 1), (4, 2), (4, 4), (8, 1),
           (8, 2), (8, 4), (16, 1), (16, 2)]
 
@@ -32,7 +36,7 @@ def _say(msg):
     print(msg, flush=True)
 
 
-@pytest.mark.parametrize("case", range(32))
+@pytest.mark.parametrize("case", range(CASES))
 def test_prologue_random_case(case):
     rng = np.random.default_rng(7000 + case)
     T = int(rng.integers(1, 300))
@@ -88,7 +92,7 @@ def _bits16(t):
     return t.detach().contiguous().cpu().view(torch.int16).numpy().view(np.uint16)
 
 
-@pytest.mark.parametrize("case", range(32))
+@pytest.mark.parametrize("case", range(CASES))
 def test_packed_random_case(case):
     rng = np.random.default_rng(8000 + case)
     D = int(rng.choice([64, 128, 256]))
