@@ -3,7 +3,6 @@ hand-derived worked example, numpy complex multiplication, invariants of
 RMSNorm and of the quantiser, and brute force on small inputs."""
 
 import numpy as np
-import pytest
 import torch
 
 import oracle as O

@@ -6,7 +6,6 @@ round-to-nearest."""
 import math
 
 import numpy as np
-import pytest
 import torch
 
 import oracle as O

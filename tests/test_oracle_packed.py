@@ -2,7 +2,6 @@
 forms, numpy complex multiplication and invariants."""
 
 import numpy as np
-import torch
 
 import oracle as O
 from fp8_kv_cache_slot_amd import inputs as I
