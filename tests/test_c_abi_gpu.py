@@ -15,12 +15,15 @@ from fp8_kv_cache_slot_amd import inputs as I
 from tests import parity as P
 
 pytestmark = pytest.mark.gpu
-DRIVER = os.path.join(os.path.dirname(os.path.abspath(__file__)), "c_abi_driver")
+# FP8KV_C_DRIVER names another build of the driver (e.g. the CMake one).
+DRIVER = os.environ.get(
+    "FP8KV_C_DRIVER",
+    os.path.join(os.path.dirname(os.path.abspath(__file__)), "c_abi_driver"))
 
 
 @pytest.mark.parametrize("T,H,seed", [(16, 16, 6000), (40, 64, 6001), (9, 7, 6002)])
 def test_c_caller_matches_oracle(tmp_path, T, H, seed):
-    assert os.path.exists(DRIVER), "tests/c_abi_driver is not built (run build())"
+    assert os.path.exists(DRIVER), f"{DRIVER} is not built (run build())"
     w = I.custom_dsv4(T, H, seed=seed, max_position=512)
     x = {k: (I.bits(v).copy() if isinstance(v, torch.Tensor) else v)
          for k, v in I.make_dsv4(w, "cpu").items()}
