@@ -3,7 +3,9 @@
 //
 // Everything is computed in double; the only roundings are the ones that
 // produce a stored output (bf16 for q and for the rotary part of the cache,
-// E4M3 for the cache codes, an exact integer for the block exponent).
+// E4M3 for the cache codes, an exact integer for the block exponent), and the
+// rounding of each quantised element to fp32 on which the quantiser's two
+// integer decisions (block exponent and code) are taken.
 // No blocking, fusion or reordering: each token, then each head, then each
 // element, in the order the operator is described.
 
@@ -43,6 +45,12 @@ struct NearestEven {
   NearestEven() : saved(std::fegetround()) { std::fesetround(FE_TONEAREST); }
   ~NearestEven() { std::fesetround(saved); }
 };
+
+// Nearest fp32 value of v, ties to even.
+double to_fp32(double v) {
+  NearestEven mode;
+  return static_cast<double>(static_cast<float>(v));
+}
 
 // RMSNorm of one row of n bf16 values with a bf16 weight, all in double:
 //   y_d = x_d / sqrt(mean(x^2) + eps) * w_d
@@ -86,16 +94,23 @@ void kv_head(const uint16_t* x, const uint16_t* w, const float* cosv,
 // "Performance": a single scalar scale could not hold one exponent per
 // block), each the smallest power of two that brings the block's largest
 // magnitude within the E4M3 range; the rotary dims are kept
-// as bf16 after the codes (reading).
+// as bf16 after the codes (reading).  The exponent and the codes are integers
+// that floating-point values decide; both are decided on each element's
+// nearest fp32 value, the precision the operator computes in ([P2] "The four
+// test and benchmark fixes": the reference takes q to fp32), so that a block
+// maximum a hair above a power-of-two boundary in double, but on it in fp32,
+// gets the fp32 answer.
 void quantise_insert(const double* y, uint8_t* dst, uint8_t* scale) {
+  double yf[kRopeStart];
+  for (int d = 0; d < kRopeStart; ++d) yf[d] = to_fp32(y[d]);
   for (int b = 0; b < kNumBlocks; ++b) {
     double amax = 0.0;
     for (int d = b * kQuantBlock; d < (b + 1) * kQuantBlock; ++d)
-      amax = std::fmax(amax, std::fabs(y[d]));
+      amax = std::fmax(amax, std::fabs(yf[d]));
     int32_t e = oracle_ue8m0_exponent(amax);
     scale[b] = static_cast<uint8_t>(e + 127);
     for (int d = b * kQuantBlock; d < (b + 1) * kQuantBlock; ++d)
-      dst[d] = oracle_e4m3_encode(std::ldexp(y[d], -e));  // exact scaling
+      dst[d] = oracle_e4m3_encode(std::ldexp(yf[d], -e));  // exact scaling
   }
   for (int j = 0; j < kRopeDim; ++j) {
     uint16_t bits = oracle_bf16_rne(y[kRopeStart + j]);
@@ -317,9 +332,13 @@ void oracle_qnorm_rope_kv_quant_insert_scalar(
     if (slot < 0 || slot >= num_slots) continue;
     kv_head(kv + t * kHeadDim, kv_weight, cosv, sinv, eps, y);
     uint8_t* dst = kv_cache + slot * kRowBytes;
-    // one scale for everything: codes of y / s, saturating at the E4M3 range
+    // one scale for everything: codes of y / s, saturating at the E4M3 range.
+    // The code is decided in fp32 like the blockwise one: the element's fp32
+    // value divided by the fp32 scale, the quotient rounded to fp32 (a double
+    // quotient of two fp32 values rounds to the correctly rounded fp32 one).
     for (int d = 0; d < kRopeStart; ++d)
-      dst[d] = oracle_e4m3_encode(y[d] / static_cast<double>(kv_cache_scale));
+      dst[d] = oracle_e4m3_encode(
+          to_fp32(to_fp32(y[d]) / static_cast<double>(kv_cache_scale)));
     for (int j = 0; j < kRopeDim; ++j) {
       uint16_t bits = oracle_bf16_rne(y[kRopeStart + j]);
       dst[kRopeStart + 2 * j] = static_cast<uint8_t>(bits & 0xFF);

@@ -3,7 +3,9 @@
  *
  * TEST INFRASTRUCTURE ONLY.  This library is a plain, slow, single-threaded
  * statement of what the two operators compute, evaluated in double precision
- * with exactly one rounding at every stored output.  Only the test suite, the
+ * with exactly one rounding at every stored output, except that the FP8
+ * quantiser takes its integer decisions (block exponent, code) on each
+ * element's fp32 value, the precision the operator computes in.  Only the test suite, the
  * smoke check and the CPU-baseline leg of the benchmark may load it.  It shares
  * no code, header, table or helper with the GPU library and never calls it.
  *
@@ -81,6 +83,8 @@ int32_t oracle_ue8m0_exponent(double amax);
  *   kv_scale      uint8 [num_pages, 64, 8]: bytes 0..6 = e_b + 127 for the
  *                 seven 64-dim quantisation blocks; byte 7 is never written
  *   eps           added to the mean square inside the square root
+ * e_b and the codes E4M3(y_d 2^-e_b) are decided on fp32(y_d), each element
+ * of the normalised, rotated KV row rounded to the nearest fp32 value.
  */
 void oracle_qnorm_rope_kv_quant_insert(
     uint16_t* q, const uint16_t* kv, const uint16_t* q_weight,
@@ -94,7 +98,8 @@ void oracle_qnorm_rope_kv_quant_insert(
  * against the blockwise one ([P1] "Performance": a single kv_cache_scale
  * float for the whole cache, with no room for an exponent per block).  q is
  * processed exactly as above; the KV row's dims 0..447 become
- * E4M3(y_d / kv_cache_scale) (nearest even, saturating at +-448) and dims
+ * E4M3(fp32(fp32(y_d) / kv_cache_scale)) (nearest even, saturating at
+ * +-448; the code decided in fp32 as in entry 1) and dims
  * 448..511 are stored as bf16 as before; no exponent bytes exist.
  * kv_cache_scale must be positive and finite.
  */

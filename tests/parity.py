@@ -13,7 +13,9 @@ bit-exact):
     lies within 2^-18 of an exponent boundary (A / (448 2^e) > 1 - 2^-18 or
     < (1 + 2^-18) / 2): there the two exponents may differ by one and the
     block's codes are checked by dequantised value against the oracle's
-    unrounded values instead.
+    unrounded values instead.  Both sides decide exponents and codes on fp32
+    values; the allowance covers the kernel's own fp32 rounding error, which
+    can move a maximum that sits within a few fp32 steps of a boundary.
   * Everything the operator must not write: bit-exact (canary bytes, byte 7
     of every scale row, the V section of packed qkv).
 """

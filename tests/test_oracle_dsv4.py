@@ -263,9 +263,9 @@ def test_cos_sin_generator_row_zero():
 def test_kv_normalised_is_the_unrounded_kv_row():
     # The unrounded KV values the bound checks compare against: rounding them
     # as the operator does must give the fused oracle's stored bytes exactly
-    # (bf16 rotary dims; the exponent of each block's maximum; E4M3 codes of
-    # y 2^-e), and with a constant row and eps = 0 the non-rotary dims are
-    # exactly kv_weight.
+    # (bf16 rotary dims; the exponent of each block's maximum and the E4M3
+    # codes of y 2^-e, both taken on the fp32 values of y), and with a
+    # constant row and eps = 0 the non-rotary dims are exactly kv_weight.
     x = _host(I.custom_dsv4(12, 3, seed=77))
     y = O.kv_normalised(x["kv"].copy(), x["kv_weight"], x["cos_sin_cache"],
                         x["positions"], x["eps"])
@@ -278,7 +278,7 @@ def test_kv_normalised_is_the_unrounded_kv_row():
         rot = _bf16(y[t, 448:])
         np.testing.assert_array_equal(rows[s, 448:].view(np.uint16), rot)
         for b in range(7):
-            blk = y[t, 64 * b:64 * b + 64]
+            blk = y[t, 64 * b:64 * b + 64].astype(np.float32).astype(np.float64)
             e = O.ue8m0_exponent(float(np.abs(blk).max()))
             assert scales[s, b] == e + 127
             codes = [O.e4m3_encode(float(v) * 2.0 ** -e) for v in blk]

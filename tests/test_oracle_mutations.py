@@ -96,13 +96,14 @@ MUTATIONS = [
     # quantise + insert
     ("quant_half_block_amax",
      "    for (int d = b * kQuantBlock; d < (b + 1) * kQuantBlock; ++d)\n"
-     "      amax = std::fmax(amax, std::fabs(y[d]));",
+     "      amax = std::fmax(amax, std::fabs(yf[d]));",
      "    for (int d = b * kQuantBlock; d < b * kQuantBlock + kQuantBlock / 2; ++d)\n"
-     "      amax = std::fmax(amax, std::fabs(y[d]));"),
+     "      amax = std::fmax(amax, std::fabs(yf[d]));"),
     ("quant_byte_bias", "scale[b] = static_cast<uint8_t>(e + 127);",
      "scale[b] = static_cast<uint8_t>(e + 128);"),
-    ("quant_scale_direction", "dst[d] = oracle_e4m3_encode(std::ldexp(y[d], -e));",
-     "dst[d] = oracle_e4m3_encode(std::ldexp(y[d], e));"),
+    ("quant_scale_direction", "dst[d] = oracle_e4m3_encode(std::ldexp(yf[d], -e));",
+     "dst[d] = oracle_e4m3_encode(std::ldexp(yf[d], e));"),
+    ("quant_decides_in_double", "yf[d] = to_fp32(y[d]);", "yf[d] = y[d];"),
     ("rope_bytes_big_endian",
      "    uint16_t bits = oracle_bf16_rne(y[kRopeStart + j]);\n"
      "    dst[kRopeStart + 2 * j] = static_cast<uint8_t>(bits & 0xFF);\n"
@@ -116,8 +117,11 @@ MUTATIONS = [
      "if (slot < 0 || slot >= num_slots) continue;  // skipped token",
      "if (slot < 0 || slot >= num_slots - 1) continue;  // skipped token"),
     ("scalar_scale_multiplies",
-     "oracle_e4m3_encode(y[d] / static_cast<double>(kv_cache_scale));",
-     "oracle_e4m3_encode(y[d] * static_cast<double>(kv_cache_scale));"),
+     "to_fp32(to_fp32(y[d]) / static_cast<double>(kv_cache_scale))",
+     "to_fp32(to_fp32(y[d]) * static_cast<double>(kv_cache_scale))"),
+    ("scalar_decides_in_double",
+     "to_fp32(to_fp32(y[d]) / static_cast<double>(kv_cache_scale))",
+     "y[d] / static_cast<double>(kv_cache_scale)"),
     # separate stages
     ("rms_rows_wrong_row", "rms_norm(x + r * kHeadDim, weight, kHeadDim, eps, y);",
      "rms_norm(x, weight, kHeadDim, eps, y);"),
@@ -192,8 +196,8 @@ MUTATIONS = [
      "      for (int d = 0; d < kHeadDim; ++d) qh[d] = oracle_bf16_rne(y[d]);\n"
      "    }\n    const int64_t slot"),
     ("scalar_drops_sign",
-     "dst[d] = oracle_e4m3_encode(y[d] / static_cast<double>(kv_cache_scale));",
-     "dst[d] = oracle_e4m3_encode(std::fabs(y[d]) / static_cast<double>(kv_cache_scale));"),
+     "to_fp32(to_fp32(y[d]) / static_cast<double>(kv_cache_scale))",
+     "to_fp32(to_fp32(std::fabs(y[d])) / static_cast<double>(kv_cache_scale))"),
     # read side through block tables, unrounded KV, separate quantiser
     ("paged_page_zero_invalid",
      "const int64_t slot = page < 0 || page >= num_pages ? -1 : page * kPageSize + j % kPageSize;",

@@ -8,6 +8,7 @@ import torch
 import fp8_kv_cache_slot_amd as K
 import oracle as O
 from fp8_kv_cache_slot_amd import inputs as I
+from tests import fp32_decision_case
 from tests import golden_case
 from tests import parity as P
 
@@ -84,6 +85,35 @@ def test_golden_worked_example(threshold):
     np.testing.assert_array_equal(I.bits(q), exp["q"])
     np.testing.assert_array_equal(I.bits(scale), exp["kv_scale"])
     np.testing.assert_array_equal(I.bits(cache), exp["kv_cache"])
+
+
+@pytest.mark.parametrize("threshold", [SMALL, TILED], ids=["small", "tiled"])
+def test_quantiser_decides_in_fp32(threshold):
+    # A KV row whose block maxima sit a hair (2^-28 relative) above the
+    # exponent boundary 1.75 = 448 * 2^-8 and the E4M3 midpoint 232 in
+    # double, and exactly on them in fp32: the kernel and the oracle both
+    # decide in fp32, so exponents and codes match the hand-derived bytes
+    # bit for bit (no boundary-band allowance), for both cache conventions.
+    h = fp32_decision_case.inputs()
+    x = {k: (I.from_bits(v, DEV) if isinstance(v, np.ndarray) else v)
+         for k, v in h.items()}
+    q, cache, scale = _run(x, threshold)
+    row, sc = I.bits(cache).reshape(-1, 576)[5], I.bits(scale).reshape(-1, 8)[5]
+    assert list(sc[:7]) == fp32_decision_case.SCALE_BYTES and sc[7] == 0x5A
+    assert list(row[:448]) == fp32_decision_case.CODES
+    assert np.all(row[448:].view(np.uint16) == fp32_decision_case.ROPE_BF16)
+    ref = _oracle(h)
+    np.testing.assert_array_equal(I.bits(q), ref["q"])
+    np.testing.assert_array_equal(I.bits(cache), ref["kv_cache"])
+    np.testing.assert_array_equal(I.bits(scale), ref["kv_scale"])
+    # the scalar-scale convention with kv_cache_scale = 1
+    c2 = x["kv_cache"].clone()
+    K.qnorm_rope_kv_quant_insert_scalar_scale(
+        x["q"].clone(), x["kv"], x["q_weight"], x["kv_weight"],
+        x["cos_sin_cache"], x["positions"], x["slot_mapping"], c2,
+        torch.ones(1, dtype=torch.float32, device=DEV), x["eps"])
+    torch.cuda.synchronize()
+    assert list(I.bits(c2).reshape(-1, 576)[5, :448]) == fp32_decision_case.SCALAR_CODES
 
 
 @pytest.mark.parametrize("name", ["tiny", "decode"])
