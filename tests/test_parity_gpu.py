@@ -239,6 +239,32 @@ def _check_full_size(w):
     P.check_cache(I.bits(cache), I.bits(scale), ref["kv_cache"], ref["kv_scale"],
                   slots, y, I.CACHE_CANARY, I.SCALE_CANARY, name)
 
+    # Every KV row at full size against the oracle's KV path (the oracle with
+    # no Q heads), in token chunks: exponents bit-exact outside the boundary
+    # band, codes within one step, rotary dims by the bf16 rule.
+    got_c, got_s = I.bits(cache), I.bits(scale)
+    kv_all, pos_all, sm_all = I.bits(x["kv"]), I.bits(x["positions"]), I.bits(sm)
+    ref_c = np.full((w.num_pages, 64, 576), I.CACHE_CANARY, np.uint8)
+    ref_s = np.full((w.num_pages, 64, 8), I.SCALE_CANARY, np.uint8)
+    band = diff = rows = 0
+    chunk = 32768
+    for a in range(0, w.num_tokens, chunk):
+        b = min(a + chunk, w.num_tokens)
+        O.qnorm_rope_kv_quant_insert(
+            np.zeros((b - a, 0, 512), np.uint16), kv_all[a:b].copy(),
+            h["q_weight"], h["kv_weight"], h["cos_sin_cache"],
+            pos_all[a:b].copy(), sm_all[a:b].copy(), ref_c, ref_s, h["eps"])
+        v = P.valid_slots(sm_all[a:b], num_slots)
+        yc = O.kv_normalised(kv_all[a:b][v].copy(), h["kv_weight"],
+                             h["cos_sin_cache"], pos_all[a:b][v].copy(), h["eps"])
+        st = P.check_cache(got_c, got_s, ref_c, ref_s, sm_all[a:b][v], yc,
+                           I.CACHE_CANARY, I.SCALE_CANARY, f"{name} tokens {a}..{b}")
+        band += st["band_blocks"]
+        diff += st["code_diff"]
+        rows += st["rows"]
+    _say(f"{name}: all {rows} KV rows checked; {band} exponent(s) in the boundary "
+         f"band, {diff} of {rows * 448} codes one step apart")
+
 
 def test_rows_of_distinct_magnitude():
     # Regression for the cross-row reduction: the four 16-lane rows of a head
