@@ -103,6 +103,26 @@ def test_no_rotation_and_large_token_count():
            "T=8192 D=64")
 
 
+def test_past_4_gib():
+    # 262144 tokens of 16/8/8 fp16 heads of 256 with interleaved rotation on
+    # 128 dims: qkv is 4 GiB, so row offsets run past 2^32 bytes.  Sampled
+    # rows against the oracle; the whole V section unchanged.
+    T, D, R = 262144, 256, 128
+    qkv, qw, kw, cs, pos = _make(T, 16, 8, 8, D, R, torch.float16, seed=93)
+    out = qkv.clone()
+    K.qk_norm_rope_packed_ex(out, 16, 8, 8, D, 1e-6, qw, kw, cs, False, pos,
+                             rotary_dim=R)
+    torch.cuda.synchronize()
+    n = 24 * D
+    assert torch.equal(out[:, n:], qkv[:, n:])
+    rng = np.random.default_rng(93)
+    toks = np.unique(np.concatenate([np.arange(64), np.arange(T - 64, T),
+                                     rng.choice(T, 128, replace=False)]))
+    ti = torch.from_numpy(toks).to(DEV)
+    _check(qkv[ti].contiguous(), out[ti].contiguous(), 16, 8, 8, D, R, False,
+           torch.float16, qw, kw, cs, pos[ti], "T=262144 D=256")
+
+
 def test_guarded_case_goes_to_the_tuned_kernel_with_identical_results():
     x = I.make_packed(I.PACKED_WORKLOADS["packed_t17"], DEV)
     a, b = x["qkv"].clone(), x["qkv"].clone()

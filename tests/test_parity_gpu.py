@@ -409,6 +409,23 @@ def test_packed_workloads(name):
     assert torch.equal(got, _run_packed(x, explicit=False))
 
 
+def test_packed_past_2_gib():
+    # 262144 tokens of 16/8/8 heads of 128: qkv is 2 GiB, so row offsets run
+    # past 2^31 bytes.  Sampled rows (first, last and random) against the
+    # oracle; the whole V section unchanged.
+    w = I.PackedWorkload("packed_2gib", 262144, seed=1034)
+    _say(f"workload {w.name} T={w.num_tokens}")
+    x = I.make_packed(w, DEV)
+    got = _run_packed(x)
+    nqk = (w.num_heads_q + w.num_heads_k) * w.head_dim
+    assert torch.equal(got[:, nqk:], x["qkv"][:, nqk:])
+    toks = _sampled_tokens(w.num_tokens, np.random.default_rng(w.seed))
+    ti = torch.from_numpy(toks).to(DEV)
+    xs = dict(x, qkv=x["qkv"][ti].contiguous(), position_ids=x["position_ids"][ti])
+    ref = _oracle_packed(xs)
+    P.check_bf16(I.bits(got[ti])[:, :nqk], ref[:, :nqk], w.name)
+
+
 @pytest.mark.parametrize("heads", [(16, 0, 8), (0, 8, 8), (5, 3, 1), (1, 1, 0),
                                    (32, 8, 8), (40, 4, 4), (7, 6, 2), (20, 5, 0),
                                    (12, 0, 3)])
