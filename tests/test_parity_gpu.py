@@ -266,6 +266,64 @@ def _check_full_size(w):
          f"band, {diff} of {rows * 448} codes one step apart")
 
 
+def test_cache_past_2_gib():
+    # 65536 pages: 2.4 GB of cache rows, so the rows of slots in the last
+    # pages start past 2^31 bytes.  Half the tokens go to the last slots of
+    # the cache, half to random ones.  The written rows are compared with the
+    # oracle (run on a compact cache of one row per token), every other byte
+    # keeps its canary, and both read sides return the oracle's dequantised
+    # rows.
+    pages, T, H = 65536, 64, 2
+    num_slots = pages * 64
+    w = I.custom_dsv4(T, H, seed=2400, num_pages=pages, max_position=4096,
+                      skipped=0)
+    _say(f"cache of {pages} pages, T={T} H={H}")
+    x = I.make_dsv4(w, DEV)
+    rng = np.random.default_rng(2400)
+    top = num_slots - 1 - np.arange(T // 2)
+    low = rng.choice(num_slots - T, size=T - T // 2, replace=False)
+    slots = np.concatenate([top, low]).astype(np.int64)
+    assert (slots[: T // 2] * 576 >= 2 ** 31).all()
+    x["slot_mapping"] = torch.from_numpy(slots).to(DEV)
+    small = {k: v for k, v in x.items() if k not in ("kv_cache", "kv_scale")}
+    compact = dict(_host(small), slot_mapping=np.arange(T, dtype=np.int64),
+                   kv_cache=np.full((1, 64, 576), I.CACHE_CANARY, np.uint8),
+                   kv_scale=np.full((1, 64, 8), I.SCALE_CANARY, np.uint8))
+    ref = _oracle(compact)
+    y = O.kv_normalised(compact["kv"], compact["kv_weight"],
+                        compact["cos_sin_cache"], compact["positions"],
+                        compact["eps"])
+    for label, thr in [("small", SMALL), ("tiled", TILED)]:
+        q, cache, scale = _run(x, thr)
+        P.check_bf16(I.bits(q), ref["q"], f"{label} q")
+        si = torch.from_numpy(slots).to(DEV)
+        c2, s2 = cache.view(-1, 576), scale.view(-1, 8)
+        got_c = I.bits(c2[si]).reshape(1, 64, 576)
+        got_s = I.bits(s2[si]).reshape(1, 64, 8)
+        P.check_cache(got_c, got_s, ref["kv_cache"], ref["kv_scale"],
+                      np.arange(T), y, I.CACHE_CANARY, I.SCALE_CANARY, label)
+        # every other byte of the 2.4 GB cache is untouched
+        c2[si] = I.CACHE_CANARY
+        s2[si, :7] = I.SCALE_CANARY
+        assert bool((c2 == I.CACHE_CANARY).all()) and bool((s2 == I.SCALE_CANARY).all())
+        c2[si] = torch.from_numpy(got_c.reshape(T, 576)).to(DEV)
+        s2[si] = torch.from_numpy(got_s.reshape(T, 8)).to(DEV)
+        # read side by slot list and through a block table of the last page
+        want = O.kv_cache_gather_dequant(got_c, got_s, np.arange(T, dtype=np.int64))
+        out = K.kv_cache_gather_dequant(cache, scale, si)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(I.bits(out), want)
+        last = torch.full((1, 1), pages - 1, dtype=torch.int32, device=DEV)
+        out2 = torch.zeros((64, 512), dtype=torch.bfloat16, device=DEV)
+        K.kv_cache_gather_dequant_paged(
+            cache, scale, last, torch.tensor([64], dtype=torch.int32, device=DEV),
+            torch.zeros(1, dtype=torch.int64, device=DEV), out2)
+        ref_last = K.kv_cache_gather_dequant(
+            cache, scale, torch.arange(num_slots - 64, num_slots, device=DEV))
+        torch.cuda.synchronize()
+        assert torch.equal(out2, ref_last)
+
+
 def test_rows_of_distinct_magnitude():
     # Regression for the cross-row reduction: the four 16-lane rows of a head
     # (dims 0-127, 128-255, 256-383, 384-511) hold very different magnitudes,
