@@ -306,7 +306,7 @@ def qk_norm_rope_packed_ex(qkv, num_heads_q: int, num_heads_k: int,
           float(eps), q_weight.data_ptr(), k_weight.data_ptr(),
           cos_sin_cache.data_ptr() if R else None, int(bool(is_neox)),
           position_ids.data_ptr(), R, dtypes[qkv.dtype],
-          max(1, cos_sin_cache.shape[0]))
+          cos_sin_cache.shape[0])
 
 
 def kv_cache_gather_dequant(kv_cache, kv_scale, slots, out=None,

@@ -59,7 +59,8 @@ __device__ __forceinline__ void load_rows(const uint8_t* __restrict__ kv_cache,
   const int off = row_offset(lane);
 #pragma unroll
   for (int r = 0; r < RS; ++r) {
-    d.v[r] = *reinterpret_cast<const u32x4_t*>(kv_cache + slot[r] * 576 + off);
+    // lane l < 56 reads bytes 8l..8l+15 of the row: 8-byte aligned only
+    d.v[r] = *reinterpret_cast<const u32x4_a8_t*>(kv_cache + slot[r] * 576 + off);
     d.ev[r] = SCALAR ? 0u : *reinterpret_cast<const uint64_t*>(kv_scale + slot[r] * 8);
   }
 #pragma unroll

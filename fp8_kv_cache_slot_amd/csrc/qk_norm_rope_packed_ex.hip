@@ -111,8 +111,10 @@ __global__ void __launch_bounds__(WAVES * 64) qk_norm_rope_packed_ex_kernel(
   const u32x4_t wkr = load16<false>((num_heads_k > 0 ? k_weight : q_weight) + lh * 8);
   __builtin_amdgcn_sched_barrier(0);  // keep the position load after these
   const int64_t pos_in = position_ids[t];
-  const bool valid = pos_in >= 0 && pos_in < max_position;
-  const int64_t pos = valid ? pos_in : 0;
+  // Without rotary dims no table row is read, so every token is stored.
+  const bool in_range = pos_in >= 0 && pos_in < max_position;
+  const bool valid = in_range || rotary_dim == 0;
+  const int64_t pos = in_range ? pos_in : 0;
 
   // Rotation coefficients of this lane: identity outside the rotary dims.
   const int rot_lanes = rotary_dim / 8;

@@ -95,7 +95,8 @@ inline int validate_packed_ex(const void* qkv, int64_t num_tokens,
                               const int64_t* position_ids, int32_t rotary_dim,
                               int32_t dtype, int64_t max_position) {
   if (num_tokens < 0 || num_heads_q < 0 || num_heads_k < 0 ||
-      num_heads_v < 0 || num_heads_q + num_heads_k < 1 || max_position < 1)
+      num_heads_v < 0 || num_heads_q + num_heads_k < 1 ||
+      (rotary_dim > 0 && max_position < 1))  // R = 0 indexes no table
     return FP8KV_ERR_SHAPE;
   if ((head_dim != 64 && head_dim != 128 && head_dim != 256) ||
       rotary_dim < 0 || rotary_dim > head_dim || rotary_dim % 16 != 0 ||

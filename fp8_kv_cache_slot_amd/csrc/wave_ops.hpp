@@ -13,6 +13,9 @@ typedef float float2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+// Four dwords at an address that is only known to be 8-byte aligned (gfx950
+// global loads do not need the vector's natural 16-byte alignment).
+typedef uint32_t u32x4_a8_t __attribute__((ext_vector_type(4), aligned(8)));
 
 // DPP lane patterns (GCN/CDNA encoding).  All reductions below run with every
 // lane of the wave active.

@@ -184,7 +184,10 @@ enum fp8kv_dtype { FP8KV_DTYPE_BF16 = 0, FP8KV_DTYPE_FP16 = 1 };
  *   head_dim     64, 128 or 256
  *   rotary_dim   R, a multiple of 16 with 0 <= R <= head_dim: only dims
  *                [0, R) of a head rotate; dims [R, head_dim) are normalised
- *                and weighted only (partial rotary); R = 0 is RMSNorm alone
+ *                and weighted only (partial rotary); R = 0 is RMSNorm alone:
+ *                no table row is read, so position_ids are not used (every
+ *                token is written, whatever its position) and max_position
+ *                may be 0
  *   is_neox      1: pairs (i, i + R/2); 0: interleaved pairs (2i, 2i + 1);
  *                i < R/2, rotated by cos_sin_cache row positions[t] =
  *                [R/2 cosines | R/2 sines] (fp32 [max_position, R]; may be

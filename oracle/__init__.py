@@ -333,8 +333,8 @@ def qk_norm_rope_packed_ex(qkv, num_heads_q, num_heads_k, num_heads_v,
         raise ValueError("cos_sin_cache must be [max_position, rotary_dim]")
     if position_ids.shape != (T,):
         raise ValueError("position_ids must be [T]")
-    if T and (position_ids.min() < 0
-              or position_ids.max() >= cos_sin_cache.shape[0]):
+    if T and rotary_dim and (position_ids.min() < 0
+                             or position_ids.max() >= cos_sin_cache.shape[0]):
         raise ValueError("position out of range")
     _load().oracle_qk_norm_rope_packed_ex(
         _ptr(qkv, np.uint16, True), T, num_heads_q, num_heads_k, num_heads_v,

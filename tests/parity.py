@@ -37,18 +37,42 @@ def bf16_val(bits):
         np.float32).astype(np.float64)
 
 
-def check_bf16(got, ref, what=""):
+def bf16_ordered(bits):
+    """bf16 patterns on the signed integer line (sign-magnitude, +0 == -0),
+    so that the difference of two is their distance in bf16 steps."""
+    b = np.asarray(bits, np.uint16).astype(np.int32)
+    mag = b & 0x7FFF
+    return np.where(b & 0x8000, -mag, mag)
+
+
+def check_bf16(got, ref, what="", stats=None):
+    """Apply the bf16 rule; returns the fraction of values whose bits differ.
+    Only the differing values need the tolerance test: an equal pair is
+    within it unless it is a NaN, which never is.  With ``stats`` (a dict),
+    adds the values compared ("n"), the values differing ("diff") and the
+    largest distance in bf16 steps ("max_steps") to it."""
     got = np.asarray(got, np.uint16)
     ref = np.asarray(ref, np.uint16)
     assert got.shape == ref.shape, (what, got.shape, ref.shape)
-    g, r = bf16_val(got), bf16_val(ref)
+    gr, rr = got.reshape(-1), ref.reshape(-1)
+    nan = (rr & 0x7FFF) > 0x7F80
+    if nan.any():
+        i = np.flatnonzero(nan)[:5]
+        raise AssertionError(f"{what}: NaN in the reference at {i}")
+    idx = np.flatnonzero(gr != rr)
+    g, r = bf16_val(gr[idx]), bf16_val(rr[idx])
     bad = ~(np.abs(g - r) <= 2.0 ** -7 * np.abs(r) + 1e-3)
     if bad.any():
-        i = np.flatnonzero(bad.ravel())[:5]
+        i = idx[np.flatnonzero(bad)[:5]]
         raise AssertionError(
             f"{what}: {bad.sum()} bf16 values out of tolerance, e.g. at {i}: "
-            f"got {g.ravel()[i]} ref {r.ravel()[i]}")
-    frac = float(np.mean(got != ref)) if got.size else 0.0
+            f"got {bf16_val(gr[i])} ref {bf16_val(rr[i])}")
+    frac = idx.size / gr.size if gr.size else 0.0
+    if stats is not None:
+        steps = np.abs(bf16_ordered(gr[idx]) - bf16_ordered(rr[idx]))
+        stats["n"] = stats.get("n", 0) + gr.size
+        stats["diff"] = stats.get("diff", 0) + idx.size
+        stats["max_steps"] = max(stats.get("max_steps", 0), int(steps.max(initial=0)))
     assert frac <= MAX_MISMATCH, f"{what}: {frac:.2e} of bf16 values differ in bits"
     return frac
 

@@ -279,6 +279,8 @@ def test_no_device_is_reported_not_launched():
     assert _dequant(pages=0, cache=None, scale=None) == 5
     assert _norm() == 5 and _rope() == 5 and _quant() == 5
     assert _packed_ex() == 5 and _packed_ex(R=0, cs=None) == 5
+    # without rotary dims no table is indexed: an empty one is accepted
+    assert _packed_ex(R=0, cs=None, maxp=0) == 5
     assert _prologue_scalar() == 5 and _dequant_scalar() == 5
     assert _prologue_scalar(pages=0, cache=None, scale=None) == 5
     assert _copy() == 5 and _rmw() == 5

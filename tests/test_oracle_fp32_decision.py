@@ -48,3 +48,26 @@ def test_scalar_scale_code_decided_in_fp32():
     row = cache.reshape(-1, 576)[5]
     assert list(row[:448]) == C.SCALAR_CODES
     assert np.all(row[448:].view(np.uint16) == C.ROPE_BF16)
+
+
+def test_decision_reach_counts_the_hand_derived_case():
+    # The counting helper used for the full-size record: in this row the
+    # exponent of block 0 and all 64 codes of block 1 depend on the precision
+    # of the decision; nothing else does.  A row of exact fp32 values changes
+    # nothing.
+    from tests import decision_reach as R
+
+    x = C.inputs()
+    y = O.kv_normalised(x["kv"], x["kv_weight"], x["cos_sin_cache"],
+                        x["positions"], C.EPS)
+    assert R.decision_differences(y) == (1, 64)
+    assert R.decision_differences(np.float32(y).astype(np.float64)) == (0, 0)
+    # its rounding agrees with the oracle's encoder on every E4M3 midpoint and
+    # its neighbours
+    vals = np.array([O.e4m3_decode(c) for c in range(0x7F)])
+    mids = (vals[1:] + vals[:-1]) / 2
+    probe = np.concatenate([mids, np.nextafter(mids, 0), np.nextafter(mids, 1e9)])
+    want = np.array([O.e4m3_decode(O.e4m3_encode(v)) for v in probe])
+    np.testing.assert_array_equal(R._e4m3_round(probe), want)
+    amax = np.array([0.0, 2.0 ** -140, 448 * 2.0 ** -8, np.nextafter(448 * 2.0 ** -8, 1)])
+    assert R._exponent(amax).tolist() == [O.ue8m0_exponent(a) for a in amax]

@@ -50,6 +50,12 @@ MUTATIONS = [
     ("ue8m0_offset", "int e = k - 9 + (m > 0.875 ? 1 : 0);",
      "int e = k - 8 + (m > 0.875 ? 1 : 0);"),
     ("ue8m0_no_low_clamp", "if (e < -127) e = -127;", ""),
+    ("ue8m0_clamp_one_high", "if (e < -127) e = -127;",
+     "if (e < -126) e = -126;"),
+    ("fp32_decision_flushes_subnormals",
+     "  return static_cast<double>(static_cast<float>(v));",
+     "  const float f = static_cast<float>(v);\n"
+     "  return std::fpclassify(f) == FP_SUBNORMAL ? 0.0 : static_cast<double>(f);"),
     # RMSNorm
     ("rms_eps_outside_root", "double inv_rms = 1.0 / std::sqrt(mean_sq + eps);",
      "double inv_rms = 1.0 / (std::sqrt(mean_sq) + eps);"),

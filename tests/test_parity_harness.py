@@ -88,3 +88,23 @@ def test_bf16_truncation_is_caught_by_mismatch_rate():
     flip = np.random.default_rng(0).random(lo.shape) < 0.3
     with pytest.raises(AssertionError):
         P.check_bf16(np.where(flip, up, lo), ref["q"])
+
+
+def test_bf16_rule_statistics_and_nan():
+    # 1.0, 2^-10, -1.0, 0, 2.0
+    ref = np.array([0x3F80, 0x3A80, 0xBF80, 0x0000, 0x4000] * 400, np.uint16)
+    got = ref.copy()
+    got[0] = 0x3F81          # one step up at 1.0
+    got[6] = 0x3A82          # two steps up at 2^-10, inside the absolute 1e-3
+    st = {}
+    frac = P.check_bf16(got, ref, "t", stats=st)
+    assert st == {"n": 2000, "diff": 2, "max_steps": 2} and frac == 2 / 2000
+    assert P.bf16_ordered(np.array([0x8000, 0x0000, 0x8001, 0x0001])).tolist() == [0, 0, -1, 1]
+    nan_ref = ref.copy()
+    nan_ref[3] = 0x7FC0
+    with pytest.raises(AssertionError):
+        P.check_bf16(nan_ref, nan_ref, "t")   # equal NaNs are never within tolerance
+    nan_got = ref.copy()
+    nan_got[3] = 0xFFC0
+    with pytest.raises(AssertionError):
+        P.check_bf16(nan_got, ref, "t")
