@@ -49,8 +49,11 @@ def check_bf16(got, ref, what="", stats=None):
     """Apply the bf16 rule; returns the fraction of values whose bits differ.
     Only the differing values need the tolerance test: an equal pair is
     within it unless it is a NaN, which never is.  With ``stats`` (a dict),
-    adds the values compared ("n"), the values differing ("diff") and the
-    largest distance in bf16 steps ("max_steps") to it."""
+    adds to it the values compared ("n"), the values differing ("diff"), the
+    largest distance in bf16 steps where |ref| >= 2^-7, so that the relative
+    term governs ("max_steps"), and the largest absolute difference of any
+    value ("max_abs"; near zero, where the absolute term governs, a result of
+    a cancelling rotation may even differ in sign)."""
     got = np.asarray(got, np.uint16)
     ref = np.asarray(ref, np.uint16)
     assert got.shape == ref.shape, (what, got.shape, ref.shape)
@@ -69,10 +72,13 @@ def check_bf16(got, ref, what="", stats=None):
             f"got {bf16_val(gr[i])} ref {bf16_val(rr[i])}")
     frac = idx.size / gr.size if gr.size else 0.0
     if stats is not None:
-        steps = np.abs(bf16_ordered(gr[idx]) - bf16_ordered(rr[idx]))
+        big = np.abs(r) >= 2.0 ** -7
+        steps = np.abs(bf16_ordered(gr[idx][big]) - bf16_ordered(rr[idx][big]))
         stats["n"] = stats.get("n", 0) + gr.size
         stats["diff"] = stats.get("diff", 0) + idx.size
         stats["max_steps"] = max(stats.get("max_steps", 0), int(steps.max(initial=0)))
+        stats["max_abs"] = max(stats.get("max_abs", 0.0),
+                               float(np.abs(g - r).max(initial=0.0)))
     assert frac <= MAX_MISMATCH, f"{what}: {frac:.2e} of bf16 values differ in bits"
     return frac
 

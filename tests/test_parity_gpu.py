@@ -270,7 +270,8 @@ def _check_full_size(w):
             c_prec += pc
     _say(f"{name}: all {qstats['n']} q elements checked: {qstats['diff']} differ "
          f"in bits ({qstats['diff'] / qstats['n']:.2e}), at most "
-         f"{qstats['max_steps']} bf16 step(s) apart; all {rows} KV rows: {band} "
+         f"{qstats['max_steps']} bf16 step(s) apart where |ref| >= 2^-7, largest "
+         f"difference {qstats['max_abs']:.2e}; all {rows} KV rows: {band} "
          f"exponent(s) in the boundary band, {diff} of {rows * 448} codes one step "
          f"apart; deciding in double instead of fp32 would change {e_prec} of "
          f"{rows * 7} exponents and {c_prec} codes; {time.perf_counter() - t0:.0f} s "
@@ -516,7 +517,8 @@ def _check_packed_slices(x, got, what, chunk=32768):
             P.check_bf16(I.bits(got[a:b])[:, :nqk], ref[:, :nqk],
                          f"{what} tokens {a}..{b}", st)
     _say(f"{what}: all {st['n']} Q/K elements checked: {st['diff']} differ in bits, "
-         f"at most {st['max_steps']} bf16 step(s) apart")
+         f"at most {st['max_steps']} bf16 step(s) apart where |ref| >= 2^-7, "
+         f"largest difference {st['max_abs']:.2e}")
 
 
 @pytest.mark.parametrize("heads", [(16, 0, 8), (0, 8, 8), (5, 3, 1), (1, 1, 0),

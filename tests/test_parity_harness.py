@@ -98,7 +98,15 @@ def test_bf16_rule_statistics_and_nan():
     got[6] = 0x3A82          # two steps up at 2^-10, inside the absolute 1e-3
     st = {}
     frac = P.check_bf16(got, ref, "t", stats=st)
-    assert st == {"n": 2000, "diff": 2, "max_steps": 2} and frac == 2 / 2000
+    # the step count covers |ref| >= 2^-7 only; the absolute difference all
+    assert st == {"n": 2000, "diff": 2, "max_steps": 1, "max_abs": 2.0 ** -7}
+    assert frac == 2 / 2000
+    st = {}
+    small = np.full(2000, 0x3A80, np.uint16)     # 2^-10: the absolute term governs
+    off = small.copy()
+    off[5] = 0x3A82
+    P.check_bf16(off, small, "t", stats=st)
+    assert st == {"n": 2000, "diff": 1, "max_steps": 0, "max_abs": 2.0 ** -16}
     assert P.bf16_ordered(np.array([0x8000, 0x0000, 0x8001, 0x0001])).tolist() == [0, 0, -1, 1]
     nan_ref = ref.copy()
     nan_ref[3] = 0x7FC0
