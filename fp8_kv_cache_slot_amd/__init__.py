@@ -42,7 +42,8 @@ EXPORTED = ["qnorm_rope_kv_quant_insert", "qk_norm_rope_packed",
             "fp8kv_set_tiling", "fp8kv_get_tiling",
             "fp8kv_stream_copy", "fp8kv_stream_rmw",
             "kv_cache_gather_dequant_paged",
-            "kv_cache_gather_dequant_paged_scalar_scale"]
+            "kv_cache_gather_dequant_paged_scalar_scale",
+            "rms_norm_heads", "rope_neox_heads"]
 
 
 class Fp8kvError(RuntimeError):
@@ -94,6 +95,10 @@ def lib() -> ctypes.CDLL:
     L.rope_rows.restype = ctypes.c_int
     L.kv_quant_insert.argtypes = [P, P, P, P, I64, I64, I32, P]
     L.kv_quant_insert.restype = ctypes.c_int
+    L.rms_norm_heads.argtypes = [P, I64, P, P, I64, I32, I32, F, P]
+    L.rms_norm_heads.restype = ctypes.c_int
+    L.rope_neox_heads.argtypes = [P, P, P, I64, I32, I32, I64, P]
+    L.rope_neox_heads.restype = ctypes.c_int
     L.fp8kv_status_string.argtypes = [ctypes.c_int]
     L.fp8kv_status_string.restype = ctypes.c_char_p
     L.fp8kv_abi_version.argtypes = []
@@ -453,6 +458,66 @@ def unfused_prologue(q, kv, q_weight, kv_weight, cos_sin_cache, positions,
     rope_rows(q, cos_sin_cache, positions, stream=stream)
     rope_rows(kv_work.view(T, 1, D), cos_sin_cache, positions, stream=stream)
     kv_quant_insert(kv_work, slot_mapping, kv_cache, kv_scale, stream=stream)
+
+
+def rms_norm_heads(qkv, first_head: int, num_heads: int, head_dim: int, weight,
+                   out, eps: float = 1e-6, stream=None):
+    """RMSNorm of heads ``first_head .. first_head + num_heads - 1`` of every
+    row of ``qkv`` (bf16 [T, W]) into ``out`` (bf16 [T, num_heads,
+    head_dim]).  Returns ``out``."""
+    if qkv.dim() != 2:
+        raise ValueError("qkv must be [T, W]")
+    T, W = qkv.shape
+    _check(qkv, "qkv", torch.bfloat16)
+    if first_head < 0 or num_heads < 0 or (first_head + num_heads) * head_dim > W:
+        raise ValueError("heads outside the row")
+    _check(weight, "weight", torch.bfloat16, (head_dim,))
+    _check(out, "out", torch.bfloat16, (T, num_heads, head_dim))
+    _call("rms_norm_heads", (qkv, weight, out), stream,
+          qkv.data_ptr() + first_head * head_dim * qkv.element_size(), W,
+          out.data_ptr(), weight.data_ptr(), T, num_heads, head_dim, float(eps))
+    return out
+
+
+def rope_neox_heads(x, cos_sin_cache, positions, stream=None) -> None:
+    """In place: NeoX RoPE on every head of bf16 ``x`` [T, H, head_dim]."""
+    if x.dim() != 3:
+        raise ValueError("x must be [T, H, head_dim]")
+    T, H, D = x.shape
+    _check(x, "x", torch.bfloat16)
+    _check(cos_sin_cache, "cos_sin_cache", torch.float32)
+    if cos_sin_cache.dim() != 2 or cos_sin_cache.shape[1] != D:
+        raise ValueError("cos_sin_cache must be [max_position, head_dim]")
+    _check(positions, "positions", torch.int64, (T,))
+    _call("rope_neox_heads", (x, cos_sin_cache, positions), stream,
+          x.data_ptr(), cos_sin_cache.data_ptr(), positions.data_ptr(), T, H, D,
+          cos_sin_cache.shape[0])
+
+
+def unfused_qk_norm_rope_packed(qkv, num_heads_q: int, num_heads_k: int,
+                                num_heads_v: int, head_dim: int, eps: float,
+                                q_weight, k_weight, cos_sin_cache, position_ids,
+                                q_out=None, k_out=None, stream=None):
+    """The packed Q/K norm + NeoX RoPE as four separate launches (RMSNorm of
+    the Q heads and of the K heads into ``q_out`` [T, Hq, D] and ``k_out``
+    [T, Hk, D], then RoPE of each in place): the separate-launch baseline of
+    :func:`qk_norm_rope_packed`.  ``qkv`` is only read.  Returns
+    (q_out, k_out)."""
+    T = qkv.shape[0]
+    if q_out is None:
+        q_out = torch.empty((T, num_heads_q, head_dim), dtype=qkv.dtype,
+                            device=qkv.device)
+    if k_out is None:
+        k_out = torch.empty((T, num_heads_k, head_dim), dtype=qkv.dtype,
+                            device=qkv.device)
+    if qkv.dim() != 2 or qkv.shape[1] != (num_heads_q + num_heads_k + num_heads_v) * head_dim:
+        raise ValueError("qkv must be [T, (Hq + Hk + Hv) * head_dim]")
+    rms_norm_heads(qkv, 0, num_heads_q, head_dim, q_weight, q_out, eps, stream)
+    rms_norm_heads(qkv, num_heads_q, num_heads_k, head_dim, k_weight, k_out, eps,
+                   stream)
+    rope_neox_heads(q_out, cos_sin_cache, position_ids, stream)
+    rope_neox_heads(k_out, cos_sin_cache, position_ids, stream)
+    return q_out, k_out
 
 
 def set_dispatch_threshold(programs: int) -> None:

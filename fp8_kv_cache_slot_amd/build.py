@@ -21,7 +21,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libfp8kv.so")
 SOURCES = ["capi.hip", "dsv4_prologue.hip", "qk_norm_rope_packed.hip",
            "kv_cache_dequant.hip", "unfused.hip", "qk_norm_rope_packed_ex.hip",
-           "stream_ref.hip"]
+           "packed_unfused.hip", "stream_ref.hip"]
 ARCH = "gfx950"
 
 # Kernel arguments preloaded into SGPRs at wave start (gfx950 user-SGPR
@@ -31,10 +31,12 @@ ARCH = "gfx950"
 # latency is exposed.  Measured on MI355X with cold caches, 16/8/8 heads of
 # 128, 8192 tokens: 24.0 -> 22.9 us; head_dim 256: 38.0 -> 37.5 us; bit-identical
 # outputs.  The prologue and the read side measured the same with and without
-# it.
+# it.  The packed operator's separate stages are built the same way as the
+# fused packed kernels they are compared with.
 SOURCE_FLAGS = {
     "qk_norm_rope_packed.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=16"],
     "qk_norm_rope_packed_ex.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=16"],
+    "packed_unfused.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=16"],
 }
 
 

@@ -343,6 +343,39 @@ FP8KV_API int rope_rows(void* x, const float* cos_sin_cache,
                           static_cast<hipStream_t>(stream));
 }
 
+FP8KV_API int rms_norm_heads(const void* x, int64_t x_token_stride, void* out,
+                             const void* weight, int64_t num_tokens,
+                             int32_t num_heads, int32_t head_dim, float eps,
+                             void* stream) {
+  using namespace fp8kv;
+  if (!valid_eps(eps)) return FP8KV_ERR_VALUE;
+  int st = validate_rms_norm_heads(x, x_token_stride, out, weight, num_tokens,
+                                   num_heads, head_dim);
+  if (st != FP8KV_OK || num_tokens == 0 || num_heads == 0) return st;
+  st = check_device();
+  if (st != FP8KV_OK) return st;
+  return launch_rms_norm_heads(static_cast<const uint16_t*>(x), x_token_stride,
+                               static_cast<uint16_t*>(out),
+                               static_cast<const uint16_t*>(weight),
+                               static_cast<int32_t>(num_tokens), num_heads, eps,
+                               static_cast<hipStream_t>(stream));
+}
+
+FP8KV_API int rope_neox_heads(void* x, const float* cos_sin_cache,
+                              const int64_t* positions, int64_t num_tokens,
+                              int32_t num_heads, int32_t head_dim,
+                              int64_t max_position, void* stream) {
+  using namespace fp8kv;
+  int st = validate_rope_neox_heads(x, cos_sin_cache, positions, num_tokens,
+                                    num_heads, head_dim, max_position);
+  if (st != FP8KV_OK || num_tokens == 0 || num_heads == 0) return st;
+  st = check_device();
+  if (st != FP8KV_OK) return st;
+  return launch_rope_neox_heads(static_cast<uint16_t*>(x), cos_sin_cache, positions,
+                                static_cast<int32_t>(num_tokens), num_heads,
+                                max_position, static_cast<hipStream_t>(stream));
+}
+
 FP8KV_API int kv_quant_insert(const void* kv, const int64_t* slot_mapping,
                               uint8_t* kv_cache, uint8_t* kv_scale,
                               int64_t num_tokens, int64_t num_pages,

@@ -107,6 +107,13 @@ int launch_kv_quant_insert(const uint16_t* kv, const int64_t* slot_mapping,
                            int64_t num_cache_slots, hipStream_t stream);
 
 // Reference streaming kernels (16-byte vectors; n16 = number of vectors).
+int launch_rms_norm_heads(const uint16_t* x, int64_t x_token_stride, uint16_t* out,
+                          const uint16_t* weight, int32_t num_tokens,
+                          int32_t num_heads, float eps, hipStream_t stream);
+int launch_rope_neox_heads(uint16_t* x, const float* cos_sin,
+                           const int64_t* positions, int32_t num_tokens,
+                           int32_t num_heads, int64_t max_position,
+                           hipStream_t stream);
 int launch_stream_copy(void* dst, const void* src, int64_t n16, hipStream_t stream);
 int launch_stream_rmw(void* buf, int64_t n16, uint32_t mask, hipStream_t stream);
 

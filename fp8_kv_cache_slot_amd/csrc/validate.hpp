@@ -190,6 +190,47 @@ inline int validate_rope_rows(const void* x, const float* cos_sin_cache,
   return FP8KV_OK;
 }
 
+// The packed operator's separate stages: heads of 128, at most 2^31 - 1
+// heads in all; a head starts on a 16-byte boundary.
+inline int validate_heads(int64_t num_tokens, int32_t num_heads, int32_t head_dim) {
+  if (num_tokens < 0 || num_heads < 0) return FP8KV_ERR_SHAPE;
+  if (head_dim != 128) return FP8KV_ERR_UNSUPPORTED;
+  if (num_heads > 0 && num_tokens > 0x7FFFFFFF / num_heads) return FP8KV_ERR_SHAPE;
+  return FP8KV_OK;
+}
+
+inline int validate_rms_norm_heads(const void* x, int64_t x_token_stride,
+                                   const void* out, const void* weight,
+                                   int64_t num_tokens, int32_t num_heads,
+                                   int32_t head_dim) {
+  int st = validate_heads(num_tokens, num_heads, head_dim);
+  if (st != FP8KV_OK) return st;
+  if (num_tokens > 0 && num_heads > 0 &&
+      (x_token_stride < int64_t{num_heads} * head_dim ||
+       x_token_stride > (int64_t{1} << 40) / num_tokens))
+    return FP8KV_ERR_SHAPE;
+  if (num_tokens == 0 || num_heads == 0) return FP8KV_OK;
+  if (!x || !out || !weight) return FP8KV_ERR_NULL;
+  if (!aligned(x, 16) || !aligned(out, 16) || !aligned(weight, 16) ||
+      x_token_stride % 8 != 0)
+    return FP8KV_ERR_ALIGN;
+  return FP8KV_OK;
+}
+
+inline int validate_rope_neox_heads(const void* x, const float* cos_sin_cache,
+                                    const int64_t* positions, int64_t num_tokens,
+                                    int32_t num_heads, int32_t head_dim,
+                                    int64_t max_position) {
+  int st = validate_heads(num_tokens, num_heads, head_dim);
+  if (st != FP8KV_OK) return st;
+  if (max_position < 1) return FP8KV_ERR_SHAPE;
+  if (num_tokens == 0 || num_heads == 0) return FP8KV_OK;
+  if (!x || !cos_sin_cache || !positions) return FP8KV_ERR_NULL;
+  if (!aligned(x, 16) || !aligned(cos_sin_cache, 16) || !aligned(positions, 8))
+    return FP8KV_ERR_ALIGN;
+  return FP8KV_OK;
+}
+
 inline int validate_kv_quant_insert(const void* kv, const int64_t* slot_mapping,
                                     const uint8_t* kv_cache,
                                     const uint8_t* kv_scale, int64_t num_tokens,

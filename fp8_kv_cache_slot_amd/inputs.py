@@ -20,7 +20,9 @@ Workloads (tokens x heads, head width 512, one latent KV head per token):
   wide128    32768 x 128,  N(0,1), positions U[0,131072), 2048 pages
   long64     131072 x 64,  N(0,1), positions U[0,131072), 2048 pages, every
              slot of the cache written (a full permutation)
-Packed workloads: qkv [T, (16+8+8)*128] for T in {1, 17, 8192}.
+Packed workloads: qkv [T, (16+8+8)*128] for T in {1, 17, 1024, 4096, 8192}
+(1024, 4096 and 8192 are the token counts InfiniOps PR #1019 "Benchmark /
+Performance Impact" measures).
 """
 
 from __future__ import annotations
@@ -91,6 +93,8 @@ PACKED_WORKLOADS = {
     for w in [
         PackedWorkload("packed_t1", 1, seed=1004),
         PackedWorkload("packed_t17", 17, seed=1014),
+        PackedWorkload("packed_t1024", 1024, seed=1044),
+        PackedWorkload("packed_t4096", 4096, seed=1054),
         PackedWorkload("packed_t8192", 8192, seed=1024),
     ]
 }

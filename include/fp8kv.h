@@ -261,6 +261,39 @@ int kv_quant_insert(const void* kv, const int64_t* slot_mapping,
                     int64_t num_pages, int32_t page_size, void* stream);
 
 /*
+ * The packed Q/K operator taken apart into the four launches InfiniOps PR
+ * #1019 "Benchmark / Performance Impact" measures the fused call against: an
+ * RmsNorm of the Q heads and one of the K heads, each into its own
+ * preallocated output, then a RotaryEmbedding of each.  Every stage reads
+ * and writes bf16, so the composition rounds to bf16 between the norm and
+ * the rotation where qk_norm_rope_packed does not.
+ *
+ * rms_norm_heads: head h < num_heads of token t < num_tokens is the
+ *   head_dim = 128 bf16 values at x + t * x_token_stride + h * 128 (elements;
+ *   for the Q heads of packed qkv: x = qkv, stride (Hq + Hk + Hv) * 128; for
+ *   the K heads: x = qkv + Hq * 128).  out bf16 [num_tokens, num_heads, 128]
+ *   (contiguous) = bf16(head / sqrt(mean(head^2) + eps) * weight).
+ *   x_token_stride >= num_heads * 128 and a multiple of 8; x, out, weight
+ *   16-B aligned.  out must not overlap x unless it equals x with
+ *   x_token_stride = num_heads * 128 (in place).
+ * rope_neox_heads: in place on x bf16 [num_tokens, num_heads, 128]: the
+ *   NeoX pairs (i, i + 64), i < 64, of every head of token t rotate by
+ *   cos_sin_cache[positions[t]] (fp32 [max_position, 128] = 64 cosines then
+ *   64 sines; 16-B aligned) and are rounded to bf16.  A token whose position
+ *   is outside [0, max_position) is left as it was.
+ * Errors: head_dim != 128 -> FP8KV_ERR_UNSUPPORTED; negative counts, more
+ *   than 2^31 - 1 heads in all, a short stride or max_position < 1 ->
+ *   FP8KV_ERR_SHAPE; eps as for the fused calls.  Zero tokens or heads return
+ *   FP8KV_OK without a launch.
+ */
+int rms_norm_heads(const void* x, int64_t x_token_stride, void* out,
+                   const void* weight, int64_t num_tokens, int32_t num_heads,
+                   int32_t head_dim, float eps, void* stream);
+int rope_neox_heads(void* x, const float* cos_sin_cache, const int64_t* positions,
+                    int64_t num_tokens, int32_t num_heads, int32_t head_dim,
+                    int64_t max_position, void* stream);
+
+/*
  * The read side through block tables, as an attention consumer indexes the
  * paged cache (the layout of FlagGems PR #5449 "Performance": pages of 64
  * token rows of 576 bytes plus seven exponents each).  Sequence s holds

@@ -79,6 +79,10 @@ def _load():
     lib.oracle_qk_norm_rope_packed_ex.argtypes = [
         P, I64, I32, I32, I32, I32, I32, I32, I32, D, P, P, P, P]
     lib.oracle_qk_norm_rope_packed_ex.restype = None
+    lib.oracle_rms_norm_heads.argtypes = [P, I64, P, P, I64, I32, I32, D]
+    lib.oracle_rms_norm_heads.restype = None
+    lib.oracle_rope_neox_heads.argtypes = [P, P, P, I64, I32, I32]
+    lib.oracle_rope_neox_heads.restype = None
     _lib = lib
     return lib
 
@@ -341,3 +345,36 @@ def qk_norm_rope_packed_ex(qkv, num_heads_q, num_heads_k, num_heads_v,
         head_dim, rotary_dim, int(is_neox), int(is_fp16), float(eps),
         _ptr(q_weight, np.uint16), _ptr(k_weight, np.uint16),
         _ptr(cos_sin_cache, np.float32), _ptr(position_ids, np.int64))
+
+
+def rms_norm_heads(qkv, first_head, num_heads, head_dim, weight, eps):
+    """Separate-launch RMSNorm of heads first_head .. first_head+num_heads-1
+    of every row of ``qkv`` (uint16 [T, W]) -> new uint16 [T, num_heads,
+    head_dim]."""
+    T, W = qkv.shape
+    if first_head < 0 or num_heads < 0 or (first_head + num_heads) * head_dim > W:
+        raise ValueError("heads outside the row")
+    if weight.shape != (head_dim,):
+        raise ValueError("weight must be [head_dim]")
+    out = np.empty((T, num_heads, head_dim), np.uint16)
+    lib = _load()
+    _ptr(qkv, np.uint16)
+    base = qkv.ctypes.data + first_head * head_dim * 2
+    lib.oracle_rms_norm_heads(ctypes.c_void_p(base), W, _ptr(weight, np.uint16),
+                              _ptr(out, np.uint16, True), T, num_heads, head_dim,
+                              float(eps))
+    return out
+
+
+def rope_neox_heads(x, cos_sin_cache, positions):
+    """Separate-launch NeoX RoPE, in place on ``x`` (uint16 [T, H, D])."""
+    T, H, D = x.shape
+    if cos_sin_cache.ndim != 2 or cos_sin_cache.shape[1] != D or D % 2:
+        raise ValueError("cos_sin_cache must be [max_position, head_dim]")
+    if positions.shape != (T,):
+        raise ValueError("positions must be [T]")
+    if T and (positions.min() < 0 or positions.max() >= cos_sin_cache.shape[0]):
+        raise ValueError("position out of range")
+    _load().oracle_rope_neox_heads(_ptr(x, np.uint16, True),
+                                   _ptr(cos_sin_cache, np.float32),
+                                   _ptr(positions, np.int64), T, H, D)

@@ -504,6 +504,43 @@ void oracle_qk_norm_rope_packed(
   delete[] y;
 }
 
+// The packed operator's separate-launch baseline ([P3] "Benchmark /
+// Performance Impact": two RmsNorm calls into preallocated Q and K outputs,
+// then two RotaryEmbedding calls).  Each stage rounds its output to bf16.
+void oracle_rms_norm_heads(const uint16_t* x, int64_t x_token_stride,
+                           const uint16_t* weight, uint16_t* out,
+                           int64_t num_tokens, int32_t num_heads,
+                           int32_t head_dim, double eps) {
+  double* y = new double[head_dim];
+  for (int64_t t = 0; t < num_tokens; ++t)
+    for (int32_t h = 0; h < num_heads; ++h) {
+      rms_norm(x + t * x_token_stride + static_cast<int64_t>(h) * head_dim,
+               weight, head_dim, eps, y);
+      uint16_t* dst = out + (t * num_heads + h) * static_cast<int64_t>(head_dim);
+      for (int d = 0; d < head_dim; ++d) dst[d] = oracle_bf16_rne(y[d]);
+    }
+  delete[] y;
+}
+
+void oracle_rope_neox_heads(uint16_t* x, const float* cos_sin_cache,
+                            const int64_t* positions, int64_t num_tokens,
+                            int32_t num_heads, int32_t head_dim) {
+  const int half = head_dim / 2;
+  for (int64_t t = 0; t < num_tokens; ++t) {
+    const float* row = cos_sin_cache + positions[t] * head_dim;
+    for (int32_t h = 0; h < num_heads; ++h) {
+      uint16_t* xh = x + (t * num_heads + h) * static_cast<int64_t>(head_dim);
+      for (int i = 0; i < half; ++i) {
+        double a = oracle_bf16_to_double(xh[i]);
+        double b = oracle_bf16_to_double(xh[i + half]);
+        rotate_pair(&a, &b, row[i], row[half + i]);
+        xh[i] = oracle_bf16_rne(a);
+        xh[i + half] = oracle_bf16_rne(b);
+      }
+    }
+  }
+}
+
 void oracle_qk_norm_rope_packed_ex(
     uint16_t* qkv, int64_t num_tokens, int32_t num_heads_q,
     int32_t num_heads_k, int32_t num_heads_v, int32_t head_dim,

@@ -144,6 +144,28 @@ void oracle_kv_quant_insert(const uint16_t* kv, const int64_t* slot_mapping,
                             uint8_t* kv_cache, uint8_t* kv_scale,
                             int64_t num_tokens, int64_t num_pages);
 
+/*
+ * The packed Q/K operator taken apart as [P3] "Benchmark / Performance
+ * Impact" measures it: RmsNorm of the Q heads and of the K heads into
+ * separate, preallocated outputs, then RotaryEmbedding of each.
+ *
+ * oracle_rms_norm_heads: head h of token t starts at
+ *   x + t * x_token_stride + h * head_dim (elements);
+ *   out[t, h, :] = bf16(head / sqrt(mean(head^2) + eps) * weight), out
+ *   contiguous [num_tokens, num_heads, head_dim].
+ * oracle_rope_neox_heads: in place on x [num_tokens, num_heads, head_dim]:
+ *   the NeoX pairs (i, i + head_dim/2) of every head of token t rotate by
+ *   cos_sin_cache row positions[t] (fp32 [max_position, head_dim] = head_dim/2
+ *   cosines then head_dim/2 sines), each result rounded to bf16.
+ */
+void oracle_rms_norm_heads(const uint16_t* x, int64_t x_token_stride,
+                           const uint16_t* weight, uint16_t* out,
+                           int64_t num_tokens, int32_t num_heads,
+                           int32_t head_dim, double eps);
+void oracle_rope_neox_heads(uint16_t* x, const float* cos_sin_cache,
+                            const int64_t* positions, int64_t num_tokens,
+                            int32_t num_heads, int32_t head_dim);
+
 /* ---- read side of the cache ------------------------------------------------ */
 /*
  * Gather rows of the paged FP8/UE8M0 cache by slot and dequantise them:

@@ -208,6 +208,38 @@ def test_stage_argument_errors(fn, over, want):
     assert fn(**over) == want
 
 
+def _norm_heads(**over):
+    a = dict(x=FAKE, stride=4096, out=FAKE, w=FAKE, T=5, H=16, D=128, eps=1e-6,
+             stream=None)
+    a.update(over)
+    return K.lib().rms_norm_heads(*a.values())
+
+
+def _rope_heads(**over):
+    a = dict(x=FAKE, cs=FAKE, pos=FAKE, T=5, H=16, D=128, maxp=8, stream=None)
+    a.update(over)
+    return K.lib().rope_neox_heads(*a.values())
+
+
+@pytest.mark.parametrize("fn,over,want", [
+    (_norm_heads, dict(T=-1), 2), (_norm_heads, dict(H=-1), 2),
+    (_norm_heads, dict(stride=2047), 2), (_norm_heads, dict(T=2 ** 27, H=16), 2),
+    (_norm_heads, dict(D=64), 3), (_norm_heads, dict(eps=-1.0), 7),
+    (_norm_heads, dict(eps=float("nan")), 7),
+    (_norm_heads, dict(x=None), 1), (_norm_heads, dict(out=None), 1),
+    (_norm_heads, dict(w=None), 1), (_norm_heads, dict(x=FAKE + 8), 4),
+    (_norm_heads, dict(stride=4100), 4), (_norm_heads, dict(T=0, x=None), 0),
+    (_norm_heads, dict(H=0, x=None, stride=0), 0),
+    (_rope_heads, dict(T=-1), 2), (_rope_heads, dict(maxp=0), 2),
+    (_rope_heads, dict(D=256), 3), (_rope_heads, dict(x=None), 1),
+    (_rope_heads, dict(cs=None), 1), (_rope_heads, dict(pos=None), 1),
+    (_rope_heads, dict(cs=FAKE + 4), 4), (_rope_heads, dict(pos=FAKE + 4), 4),
+    (_rope_heads, dict(T=0, x=None), 0),
+])
+def test_packed_stage_argument_errors(fn, over, want):
+    assert fn(**over) == want
+
+
 def _paged(**over):
     a = dict(cache=FAKE, scale=FAKE, pages=2, page=64, table=FAKE, S=3, M=4,
              lens=FAKE, offs=FAKE, N=100, out=FAKE, stream=None)
@@ -278,6 +310,7 @@ def test_no_device_is_reported_not_launched():
     assert _dequant() == 5
     assert _dequant(pages=0, cache=None, scale=None) == 5
     assert _norm() == 5 and _rope() == 5 and _quant() == 5
+    assert _norm_heads() == 5 and _rope_heads() == 5
     assert _packed_ex() == 5 and _packed_ex(R=0, cs=None) == 5
     # without rotary dims no table is indexed: an empty one is accepted
     assert _packed_ex(R=0, cs=None, maxp=0) == 5

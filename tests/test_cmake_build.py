@@ -45,9 +45,10 @@ def test_cmake_builds_the_library(tmp_path):
     cmds = subprocess.run(["ninja", "-C", str(build), "-t", "commands", "fp8kv"],
                           capture_output=True, text=True, check=True).stdout
     hip = [c for c in cmds.splitlines() if ".hip" in c and " -c " in c]
-    assert len(hip) == 7
+    assert len(hip) == 8
     for c in hip:
         assert "--offload-arch=gfx950" in c and "-packed-fp32-ops" in c
         assert "-O3" in c and "-std=c++17" in c
-        packed = "qk_norm_rope_packed" in c.split(" -c ")[1]
+        src = c.split(" -c ")[1]
+        packed = "qk_norm_rope_packed" in src or "packed_unfused" in src
         assert ("-amdgpu-kernarg-preload-count=16" in c) == packed

@@ -218,6 +218,17 @@ MUTATIONS = [
     ("scalar_paged_scale_doubled",
      "                           kv_cache, kv_cache_scale, &slot, 1, num_pages,",
      "                           kv_cache, 2.0f * kv_cache_scale, &slot, 1, num_pages,"),
+    ("rms_norm_heads_token_stride",
+     "      rms_norm(x + t * x_token_stride + static_cast<int64_t>(h) * head_dim,",
+     "      rms_norm(x + t * num_heads * head_dim + static_cast<int64_t>(h) * head_dim,"),
+    ("rope_neox_heads_sine_sign",
+     "        rotate_pair(&a, &b, row[i], row[half + i]);\n        xh[i] = oracle_bf16_rne(a);",
+     "        rotate_pair(&a, &b, row[i], -row[half + i]);\n        xh[i] = oracle_bf16_rne(a);"),
+    ("rope_neox_heads_interleaved",
+     "        double a = oracle_bf16_to_double(xh[i]);\n"
+     "        double b = oracle_bf16_to_double(xh[i + half]);",
+     "        double a = oracle_bf16_to_double(xh[2 * i]);\n"
+     "        double b = oracle_bf16_to_double(xh[2 * i + 1]);"),
     ("quant_insert_stage_bound",
      "    if (slot < 0 || slot >= num_slots) continue;\n    for (int d = 0; d < kHeadDim; ++d) y[d]",
      "    if (slot < 0 || slot >= num_slots - 1) continue;\n    for (int d = 0; d < kHeadDim; ++d) y[d]"),

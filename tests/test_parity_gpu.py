@@ -469,7 +469,8 @@ def _compare_packed(x, got, what):
     P.check_bf16(g[:, :nqk], ref[:, :nqk], what)
 
 
-@pytest.mark.parametrize("name", ["packed_t1", "packed_t17", "packed_t8192"])
+@pytest.mark.parametrize("name", ["packed_t1", "packed_t17", "packed_t1024",
+                                  "packed_t4096", "packed_t8192"])
 def test_packed_workloads(name):
     _say(f"workload {name}")
     x = I.make_packed(I.PACKED_WORKLOADS[name], DEV)
