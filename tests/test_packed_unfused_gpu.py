@@ -1,8 +1,8 @@
 """Parity of the packed operator's separate stages (RMSNorm of a group of
 heads into its own output, NeoX RoPE in place: the four-launch baseline of
 InfiniOps PR #1019 "Benchmark / Performance Impact") with the oracle's stage
-functions, and of the composed launches with the composed oracle stages.
-Needs an MI355X."""
+functions, each on its own input bytes, and of the four composed launches
+stage by stage.  Needs an MI355X."""
 
 import numpy as np
 import pytest
@@ -71,25 +71,42 @@ def test_rope_neox_heads(T, H):
     assert torch.equal(got[0], x[0]) and torch.equal(got[-1], x[-1])
 
 
-@pytest.mark.parametrize("name", ["packed_t17", "packed_t8192"])
-def test_four_launches_match_composed_oracle_stages(name):
+@pytest.mark.parametrize("name", ["packed_t17", "packed_t1024", "packed_t8192"])
+def test_four_launches_stage_by_stage(name):
+    # Each launch is compared with the oracle's stage on the same input bytes:
+    # the norm on qkv, the rotation on the GPU's own normalised heads.  (The
+    # GPU and oracle compositions cannot be compared element by element: where
+    # the norm's bf16 result is one step from the oracle's, about 1e-5 of the
+    # values, the rotation carries that step into its partner's output.)  The
+    # composed binding gives the same bytes as the launches one by one.
     w = I.PACKED_WORKLOADS[name]
     x = I.make_packed(w, DEV)
     before = x["qkv"].clone()
-    q, k = K.unfused_qk_norm_rope_packed(
-        x["qkv"], w.num_heads_q, w.num_heads_k, w.num_heads_v, w.head_dim, w.eps,
-        x["q_weight"], x["k_weight"], x["cos_sin_cache"], x["position_ids"])
-    torch.cuda.synchronize()
-    assert torch.equal(x["qkv"], before)   # qkv is only read
+    T, hq, hk = w.num_tokens, w.num_heads_q, w.num_heads_k
     h = I.bits(x["qkv"])
     cs, pos = I.bits(x["cos_sin_cache"]), I.bits(x["position_ids"])
-    rq = O.rms_norm_heads(h, 0, w.num_heads_q, D, I.bits(x["q_weight"]), w.eps)
-    rk = O.rms_norm_heads(h, w.num_heads_q, w.num_heads_k, D, I.bits(x["k_weight"]),
-                          w.eps)
-    O.rope_neox_heads(rq, cs, pos)
-    O.rope_neox_heads(rk, cs, pos)
-    P.check_bf16(I.bits(q), rq, name + " q")
-    P.check_bf16(I.bits(k), rk, name + " k")
+    for first, n, wt, tag in ((0, hq, x["q_weight"], "q"), (hq, hk, x["k_weight"], "k")):
+        normed = torch.empty((T, n, D), dtype=torch.bfloat16, device=DEV)
+        K.rms_norm_heads(x["qkv"], first, n, D, wt, normed, w.eps)
+        torch.cuda.synchronize()
+        mid = I.bits(normed)
+        P.check_bf16(mid, O.rms_norm_heads(h, first, n, D, I.bits(wt), w.eps),
+                     f"{name} {tag} norm")
+        K.rope_neox_heads(normed, x["cos_sin_cache"], x["position_ids"])
+        torch.cuda.synchronize()
+        ref = mid.copy()
+        O.rope_neox_heads(ref, cs, pos)
+        P.check_bf16(I.bits(normed), ref, f"{name} {tag} rope")
+        if tag == "q":
+            q_steps = normed
+        else:
+            k_steps = normed
+    q, k = K.unfused_qk_norm_rope_packed(
+        x["qkv"], hq, hk, w.num_heads_v, w.head_dim, w.eps, x["q_weight"],
+        x["k_weight"], x["cos_sin_cache"], x["position_ids"])
+    torch.cuda.synchronize()
+    assert torch.equal(q, q_steps) and torch.equal(k, k_steps)
+    assert torch.equal(x["qkv"], before)   # qkv is only read
 
 
 def test_rejects():
