@@ -1,6 +1,7 @@
 // C ABI of libfp8kv.so (declared in include/fp8kv.h): argument validation on
 // the host, a cached gfx950 device check, the program-count dispatch between
-// the small-batch and the tiled prologue kernels, and the launches.
+// the small-batch and the tiled prologue kernels (on MI355X both default to
+// one kernel: there is no crossover), and the launches.
 #include <hip/hip_runtime.h>
 
 #include <atomic>
@@ -20,11 +21,15 @@ namespace {
 
 // Programs = num_tokens * (num_heads + 1) below which the small-batch kernel
 // runs (the quantity FlagGems PR #5449 "Dispatch threshold" dispatches on).
-// Below ~2k programs every shape sits on the same ~6.1 us launch floor.
-constexpr int64_t kDefaultThreshold = 2048;
-// Tiled shape: one wave per block, one Q head per wave, which is also the
-// small-batch shape, so by default both sides of the threshold launch the
-// same kernel.  Measured on MI355X, each launch after a cache-flushing read:
+// MI355X has no crossover: the small-batch shape (one head per one-wave
+// block) is the fastest shape at every size measured, from 1 to 262144
+// tokens at 16 to 128 heads (level with the others up to ~2k tokens, ahead
+// from ~4k), so the default threshold is 0 and every call takes the tiled
+// path, whose default shape is that same kernel.  The threshold and the
+// tiled shape stay settable for measurement.
+constexpr int64_t kDefaultThreshold = 0;
+// Tiled shape: one wave per block, one Q head per wave (the small-batch
+// shape).  Measured on MI355X, each launch after a cache-flushing read:
 // 672 us at 32768x64, 1322 us at 32768x128 and 2686 us at 131072x64, against
 // 688-690, 1379-1385 and 2792-2825 us for the best multi-head shapes (2x2,
 // 4x2, 8x2) and 710-713 / 1388-1399 / 2843-2893 us for 2-8 waves of one

@@ -359,7 +359,10 @@ int fp8kv_abi_version(void);
  * both head counts agree on).  Calls below it use the small-batch kernel
  * (one (token, head) slot per 64-lane block); calls at or above it the tiled
  * kernel.  programs < 0 restores the built-in default; 0 sends everything to
- * the tiled kernel; INT64_MAX everything to the small-batch kernel.
+ * the tiled kernel; INT64_MAX everything to the small-batch kernel.  MI355X
+ * has no crossover: the small-batch shape is the fastest at every size
+ * measured, so it is also the tiled kernel's default shape, and the built-in
+ * default threshold is 0.
  * Process-wide; returns FP8KV_OK.  When the library is loaded, the threshold
  * starts at the value of the environment variable FP8KV_DISPATCH_THRESHOLD if
  * that is a non-negative decimal integer, else at the built-in default.
