@@ -524,7 +524,11 @@ def _check_packed_slices(x, got, what, chunk=32768):
 
 @pytest.mark.parametrize("heads", [(16, 0, 8), (0, 8, 8), (5, 3, 1), (1, 1, 0),
                                    (32, 8, 8), (40, 4, 4), (7, 6, 2), (20, 5, 0),
-                                   (12, 0, 3)])
+                                   (12, 0, 3),
+                                   # more than 8 waves of 12 heads: a token
+                                   # spans several blocks, each reading the
+                                   # position and cos/sin row itself
+                                   (100, 8, 4), (200, 0, 1), (96, 0, 0)])
 def test_packed_head_mixes(heads):
     hq, hk, hv = heads
     w = I.PackedWorkload("mix", 33, hq, hk, hv, seed=5000 + hq * 7 + hk)
