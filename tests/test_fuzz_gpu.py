@@ -132,3 +132,37 @@ def test_packed_random_case(case):
                                   err_msg=f"case {case}: V changed")
     chk = P.check_fp16 if dtype == torch.float16 else P.check_bf16
     chk(got[:, :n], ref[:, :n], f"case {case}")
+
+
+@pytest.mark.parametrize("case", range(max(8, CASES // 2)))
+def test_packed_guarded_random_case(case):
+    # The guarded entry point (bf16, head_dim 128, full NeoX) on random head
+    # mixes, up to 160 Q/K heads: a token spans up to 14 waves of 12 heads,
+    # so up to two blocks, each reading the position and cos/sin row itself.
+    # A few positions are out of range: those tokens are left as they were.
+    rng = np.random.default_rng(8500 + case)
+    hq, hk, hv = int(rng.integers(0, 121)), int(rng.integers(0, 41)), int(rng.integers(0, 17))
+    if hq + hk == 0:
+        hk = 1
+    T = int(rng.integers(1, 3001))
+    _say(f"guarded case {case}: T={T} heads={hq},{hk},{hv}")
+    w = I.PackedWorkload("fuzz", T, hq, hk, hv, max_position=2048, seed=8600 + case)
+    x = I.make_packed(w, DEV)
+    bad = rng.choice(T, size=min(T, int(rng.integers(0, 4))), replace=False)
+    pos = x["position_ids"].clone()
+    for i, b in enumerate(bad):
+        pos[int(b)] = [-1, 2048, 2 ** 40][i % 3]
+    out = x["qkv"].clone()
+    K.qk_norm_rope_packed(out, hq, hk, hv, 128, w.eps, x["q_weight"], x["k_weight"],
+                          x["cos_sin_cache"], True, pos)
+    torch.cuda.synchronize()
+    n = (hq + hk) * 128
+    got, src = I.bits(out), I.bits(x["qkv"])
+    np.testing.assert_array_equal(got[:, n:], src[:, n:], err_msg=f"case {case}: V changed")
+    keep = np.setdiff1d(np.arange(T), bad)
+    np.testing.assert_array_equal(got[bad], src[bad], err_msg=f"case {case}: skipped token written")
+    ref = src[keep].copy()
+    O.qk_norm_rope_packed(ref, hq, hk, hv, 128, w.eps, I.bits(x["q_weight"]),
+                          I.bits(x["k_weight"]), I.bits(x["cos_sin_cache"]),
+                          I.bits(pos)[keep].copy())
+    P.check_bf16(got[keep][:, :n], ref[:, :n], f"guarded case {case}")

@@ -1,6 +1,6 @@
 """Parity of the separate-stage kernels (the unfused baseline) with the
 oracle's stage functions, each on its own seeded inputs, and of the composed
-five-launch pipeline with the composed oracle stages.  Needs an MI355X."""
+five-launch pipeline stage by stage.  Needs an MI355X."""
 
 import numpy as np
 import pytest
@@ -95,25 +95,52 @@ def test_golden_example_through_the_stages():
 
 
 @pytest.mark.parametrize("name", ["tiny", "decode"])
-def test_pipeline_matches_composed_oracle_stages(name):
+def test_pipeline_stage_by_stage(name):
+    # Each of the five launches is compared with the oracle's stage on the
+    # same input bytes: the norms on q and kv, each rotation on the GPU's own
+    # normalised rows, quantise+insert on the GPU's own rotated KV rows (bit
+    # for bit: bf16 inputs are exact in fp32).  The GPU and oracle
+    # compositions are not compared element by element: where a norm's bf16
+    # result is one step from the oracle's, the rotation carries that step
+    # into its partner's output and the quantiser may pick the next code.
+    # The composed binding gives the same bytes as the launches one by one.
     w = I.DSV4_WORKLOADS[name]
     x = I.make_dsv4(w, DEV)
     h = _host(x)
-    q = O.rms_norm_rows(h["q"], h["q_weight"], h["eps"])
-    O.rope_rows(q, h["cos_sin_cache"], h["positions"])
-    kv = O.rms_norm_rows(h["kv"], h["kv_weight"], h["eps"])
-    O.rope_rows(kv.reshape(-1, 1, 512), h["cos_sin_cache"], h["positions"])
-    ref_c, ref_s = h["kv_cache"].copy(), h["kv_scale"].copy()
-    O.kv_quant_insert(kv, h["slot_mapping"], ref_c, ref_s)
-    gq, gc, gs = x["q"].clone(), x["kv_cache"].clone(), x["kv_scale"].clone()
-    K.unfused_prologue(gq, x["kv"], x["q_weight"], x["kv_weight"],
-                       x["cos_sin_cache"], x["positions"], x["slot_mapping"],
-                       gc, gs, x["eps"])
+    cs, pos = h["cos_sin_cache"], h["positions"]
+    gq = x["q"].clone()
+    K.rms_norm_rows(gq, x["q_weight"], x["eps"], out=gq)
+    work = torch.empty((w.num_tokens, 512), dtype=torch.bfloat16, device=DEV)
+    K.rms_norm_rows(x["kv"], x["kv_weight"], x["eps"], out=work)
     torch.cuda.synchronize()
-    P.check_bf16(I.bits(gq), q, name + " q")
+    q_mid, kv_mid = I.bits(gq), I.bits(work)
+    P.check_bf16(q_mid, O.rms_norm_rows(h["q"], h["q_weight"], h["eps"]), name + " q norm")
+    P.check_bf16(kv_mid, O.rms_norm_rows(h["kv"], h["kv_weight"], h["eps"]),
+                 name + " kv norm")
+    K.rope_rows(gq, x["cos_sin_cache"], x["positions"])
+    K.rope_rows(work.view(w.num_tokens, 1, 512), x["cos_sin_cache"], x["positions"])
+    torch.cuda.synchronize()
+    ref = q_mid.copy()
+    O.rope_rows(ref, cs, pos)
+    P.check_bf16(I.bits(gq), ref, name + " q rope")
+    ref = kv_mid.copy()
+    O.rope_rows(ref.reshape(-1, 1, 512), cs, pos)
+    kv_rot = I.bits(work)
+    P.check_bf16(kv_rot, ref, name + " kv rope")
+    gc, gs = x["kv_cache"].clone(), x["kv_scale"].clone()
+    K.kv_quant_insert(work, x["slot_mapping"], gc, gs)
+    torch.cuda.synchronize()
+    ref_c, ref_s = h["kv_cache"].copy(), h["kv_scale"].copy()
+    O.kv_quant_insert(kv_rot.copy(), h["slot_mapping"], ref_c, ref_s)
+    np.testing.assert_array_equal(I.bits(gc), ref_c)
+    np.testing.assert_array_equal(I.bits(gs), ref_s)
     v = P.valid_slots(h["slot_mapping"], w.num_pages * 64)
-    y = P.bf16_val(kv[v])
-    P.check_cache(I.bits(gc), I.bits(gs), ref_c, ref_s, h["slot_mapping"][v], y,
-                  I.CACHE_CANARY, I.SCALE_CANARY, name)
     P.check_untouched(I.bits(gc), I.bits(gs), h["slot_mapping"][v],
                       I.CACHE_CANARY, I.SCALE_CANARY, name)
+    q2, c2, s2 = x["q"].clone(), x["kv_cache"].clone(), x["kv_scale"].clone()
+    K.unfused_prologue(q2, x["kv"], x["q_weight"], x["kv_weight"],
+                       x["cos_sin_cache"], x["positions"], x["slot_mapping"],
+                       c2, s2, x["eps"])
+    torch.cuda.synchronize()
+    assert torch.equal(q2, gq) and torch.equal(c2, gc) and torch.equal(s2, gs)
+    assert np.array_equal(I.bits(x["kv"]), h["kv"])   # kv is only read
