@@ -20,6 +20,7 @@
 
 #include <cstdint>
 
+#include "occupancy.hpp"
 #include "prologue_launch.hpp"
 #include "wave_ops.hpp"
 
@@ -141,6 +142,25 @@ __global__ void __launch_bounds__(kMaxBlockWaves * 64) qk_norm_rope_packed_kerne
   }
 }
 
+// The kernel's LDS: the token's cos/sin row and its validity flag.
+static_assert(32 * sizeof(f32x4_t) + sizeof(int32_t) + 16 <= kMaxStaticLds,
+              "the occupancy cap assumes the kernel's own LDS fits kMaxStaticLds");
+
+// Occupancy cap for large launches, by waves per block (index).  Measured on
+// MI355X with cold caches against the same launch uncapped, outputs
+// identical: at 16/8/8 heads (two-wave blocks) 7 blocks per CU takes 36.20 /
+// 65.73 / 124.97 / 245.6 us at 16384 / 32768 / 65536 / 131072 tokens against
+// 36.76 / 68.85 / 132.86 / 266.4 (8 blocks per CU: 36.70 / 67.85 / 130.14 /
+// 262.6; 5 blocks: 273.9 at 131072), but 21.36 against 21.32 at 8192 tokens
+// and 13.50 against 12.90 at 4096.  At about 65536 waves and more: 32/4/4
+// heads (3 waves) with 5 blocks -2.6% / -3.9% at 8 / 16 chip fills of 8192
+// waves, 40/8/8 (4 waves) with 4 blocks -1.7% / -4.3%, 48/8/8 (5 waves) with
+// 4 blocks -1.7% / -2.5%; 8/2/2 (one wave) with 16 blocks -3.2% at 16 fills
+// and level at 8.  Blocks of 6 to 8 waves gained nothing from any cap.
+constexpr int kCapBlocksPerCu[kMaxBlockWaves + 1] = {0, 16, 7, 5, 4, 4, 0, 0, 0};
+constexpr int64_t kCapMinWaves = 65536;     // blocks of 2-5 waves
+constexpr int64_t kCapMinWaves1 = 131072;   // one-wave blocks
+
 }  // namespace
 
 int launch_packed(const PackedArgs& a, hipStream_t stream) {
@@ -152,6 +172,10 @@ int launch_packed(const PackedArgs& a, hipStream_t stream) {
   int32_t waves_per_block = (waves_per_token + blocks_per_token - 1) / blocks_per_token;
   const int64_t blocks = static_cast<int64_t>(a.num_tokens) * blocks_per_token;
   if (blocks > 0x7FFFFFFF) return FP8KV_ERR_SHAPE;
+  const int64_t waves = blocks * waves_per_block;
+  const int cap = kCapBlocksPerCu[waves_per_block];
+  const bool capped = cap > 0 && waves >= (waves_per_block == 1 ? kCapMinWaves1 : kCapMinWaves);
+  const unsigned lds = capped ? static_cast<unsigned>(lds_for_blocks_per_cu(cap)) : 0u;
   void* args[] = {const_cast<uint16_t**>(&a.qkv),
                   const_cast<const float**>(&a.cos_sin),
                   const_cast<const int64_t**>(&a.position_ids),
@@ -165,7 +189,7 @@ int launch_packed(const PackedArgs& a, hipStream_t stream) {
                   const_cast<float*>(&a.eps)};
   hipError_t err = hipLaunchKernel(
       reinterpret_cast<const void*>(&qk_norm_rope_packed_kernel),
-      dim3(static_cast<uint32_t>(blocks)), dim3(waves_per_block * 64), args, 0,
+      dim3(static_cast<uint32_t>(blocks)), dim3(waves_per_block * 64), args, lds,
       stream);
   return err == hipSuccess ? FP8KV_OK : FP8KV_ERR_LAUNCH;
 }

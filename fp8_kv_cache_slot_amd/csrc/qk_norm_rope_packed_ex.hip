@@ -23,6 +23,7 @@
 #include <cstdint>
 
 #include "prologue_launch.hpp"
+#include "occupancy.hpp"
 #include "wave_ops.hpp"
 
 namespace fp8kv {
@@ -206,6 +207,16 @@ __global__ void __launch_bounds__(WAVES * 64) qk_norm_rope_packed_ex_kernel(
 constexpr int kExWaves = 1;
 constexpr int kExUnroll = 3;
 
+// Occupancy cap for large launches: at most 16 one-wave blocks per CU from
+// 131072 waves (16 fills of the chip's 8192 wave slots) up.  Measured on
+// MI355X with cold caches at 16/8/8 heads and 16 fills, against the same
+// launch uncapped, outputs identical: D=64 interleaved fp16 130.3 against
+// 134.8 us, D=256 NeoX R=128 127.6 against 132.0, D=128 NeoX R=64 131.3
+// against 134.0, D=128 NeoX R=128 134.5 against 133.2 (level).  At 8 fills the
+// cap was level to 1% faster, at 1 to 4 fills 1-8% slower.
+constexpr int kExCapBlocksPerCu = 16;
+constexpr int64_t kExCapMinWaves = 131072;
+
 template <int D, bool FP16, bool NEOX>
 int launch_ex(const PackedExArgs& a, hipStream_t stream) {
   constexpr int kHeadsPerWave = kExUnroll * (512 / D);
@@ -231,7 +242,10 @@ int launch_ex(const PackedExArgs& a, hipStream_t stream) {
   hipError_t err = hipLaunchKernel(
       reinterpret_cast<const void*>(
           &qk_norm_rope_packed_ex_kernel<D, FP16, NEOX, kExWaves, kExUnroll>),
-      dim3(static_cast<uint32_t>(blocks)), dim3(kExWaves * 64), args, 0, stream);
+      dim3(static_cast<uint32_t>(blocks)), dim3(kExWaves * 64), args,
+      waves >= kExCapMinWaves ? static_cast<unsigned>(lds_for_blocks_per_cu(kExCapBlocksPerCu))
+                              : 0u,
+      stream);
   return err == hipSuccess ? FP8KV_OK : FP8KV_ERR_LAUNCH;
 }
 

@@ -10,6 +10,7 @@
 
 #include <cstdint>
 
+#include "occupancy.hpp"
 #include "prologue_launch.hpp"
 #include "wave_ops.hpp"
 
@@ -20,6 +21,22 @@ namespace {
 // moves 6.77 TB/s over 2 GiB and 8 GiB with 64-lane blocks, against 6.56-6.58
 // with 128 or 256 lanes and 6.25-6.38 with 512 or 1024.
 constexpr int kThreads = 64;
+
+// From 128 MiB up, at most 25 blocks per CU (the uncapped launch holds 32).
+// Measured on MI355X with cold caches, uncapped against capped: in-place RMW
+// 43.20 / 42.79, 82.49 / 81.19, 161.04 / 158.86, 634.4 / 620.7 and 2537 / 2473
+// us over 128 MiB, 256 MiB, 512 MiB, 2 GiB and 8 GiB; copy 43.22 / 42.76,
+// 82.63 / 81.49, 322.1 / 316.2 and 1280.5 / 1254.5 us over 128 MiB, 256 MiB,
+// 1 GiB and 4 GiB each way.  At 64 MiB both were level (23.80 / 23.80 and
+// 23.88 / 23.78 us).  21 blocks per CU was level with no cap; 18 and fewer
+// were slower.
+constexpr int kCapBlocksPerCu = 25;
+constexpr int64_t kCapMinBytes = int64_t{128} << 20;
+
+unsigned cap_lds(int64_t bytes) {
+  return bytes >= kCapMinBytes ? static_cast<unsigned>(lds_for_blocks_per_cu(kCapBlocksPerCu))
+                               : 0u;
+}
 
 __global__ void __launch_bounds__(kThreads) stream_copy_kernel(
     u32x4_t* __restrict__ dst, const u32x4_t* __restrict__ src, int64_t n16) {
@@ -49,7 +66,8 @@ int launch_stream_copy(void* dst, const void* src, int64_t n16, hipStream_t stre
   const u32x4_t* s = static_cast<const u32x4_t*>(src);
   void* args[] = {&d, &s, &n16};
   return hipLaunchKernel(reinterpret_cast<const void*>(&stream_copy_kernel),
-                         dim3(blocks), dim3(kThreads), args, 0, stream) == hipSuccess
+                         dim3(blocks), dim3(kThreads), args, cap_lds(n16 * 16),
+                         stream) == hipSuccess
              ? FP8KV_OK
              : FP8KV_ERR_LAUNCH;
 }
@@ -60,7 +78,8 @@ int launch_stream_rmw(void* buf, int64_t n16, uint32_t mask, hipStream_t stream)
   u32x4_t* b = static_cast<u32x4_t*>(buf);
   void* args[] = {&b, &n16, &mask};
   return hipLaunchKernel(reinterpret_cast<const void*>(&stream_rmw_kernel),
-                         dim3(blocks), dim3(kThreads), args, 0, stream) == hipSuccess
+                         dim3(blocks), dim3(kThreads), args, cap_lds(n16 * 16),
+                         stream) == hipSuccess
              ? FP8KV_OK
              : FP8KV_ERR_LAUNCH;
 }

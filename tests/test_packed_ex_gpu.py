@@ -106,22 +106,15 @@ def test_no_rotation_and_large_token_count():
            "T=8192 D=64")
 
 
-@pytest.mark.timeout(600)
-def test_past_4_gib():
-    # 262144 tokens of 16/8/8 fp16 heads of 256 with interleaved rotation on
-    # 128 dims: qkv is 4 GiB, so row offsets run past 2^32 bytes.  Every Q/K
-    # element against the oracle, in token slices on the host's cores; the
-    # whole V section unchanged.
-    T, D, R = 262144, 256, 128
-    qkv, qw, kw, cs, pos = _make(T, 16, 8, 8, D, R, torch.float16, seed=93)
-    out = qkv.clone()
-    K.qk_norm_rope_packed_ex(out, 16, 8, 8, D, 1e-6, qw, kw, cs, False, pos,
-                             rotary_dim=R)
-    torch.cuda.synchronize()
-    n = 24 * D
+def _check_slices(qkv, out, hq, hk, hv, D, R, neox, fp16, qw, kw, cs, pos, what):
+    """Every Q/K element against the oracle, in token slices on the host's
+    cores; the whole V section unchanged."""
+    T = qkv.shape[0]
+    n = (hq + hk) * D
     assert torch.equal(out[:, n:], qkv[:, n:])
     threads = max(1, min(16, len(os.sched_getaffinity(0))))
     hqw, hkw, hcs = _bits(qw), _bits(kw), I.bits(cs).copy()
+    chk = P.check_fp16 if fp16 else P.check_bf16
     st = {"diff": 0}
     with cf.ThreadPoolExecutor(threads) as ex:
         for a in range(0, T, 32768):
@@ -131,14 +124,43 @@ def test_past_4_gib():
 
             def run(i, ref=ref, hpos=hpos, cuts=cuts):
                 u, v = cuts[i], cuts[i + 1]
-                O.qk_norm_rope_packed_ex(ref[u:v], 16, 8, 8, D, R, 0, 1, 1e-6,
-                                         hqw, hkw, hcs, hpos[u:v])
+                O.qk_norm_rope_packed_ex(ref[u:v], hq, hk, hv, D, R, int(neox), int(fp16),
+                                         1e-6, hqw, hkw, hcs, hpos[u:v])
             list(ex.map(run, range(threads)))
             got = _bits(out[a:b])[:, :n]
             st["diff"] += int(np.count_nonzero(got != ref[:, :n]))
-            P.check_fp16(got, ref[:, :n], f"T=262144 D=256 tokens {a}..{b}")
-    print(f"T=262144 D=256 fp16: all {T * n} Q/K elements checked, "
-          f"{st['diff']} differ in bits", flush=True)
+            chk(got, ref[:, :n], f"{what} tokens {a}..{b}")
+    print(f"{what}: all {T * n} Q/K elements checked, {st['diff']} differ in bits",
+          flush=True)
+
+
+@pytest.mark.timeout(600)
+def test_past_4_gib():
+    # 262144 tokens of 16/8/8 fp16 heads of 256 with interleaved rotation on
+    # 128 dims: qkv is 4 GiB, so row offsets run past 2^32 bytes.  The launch
+    # is large enough for the occupancy cap.
+    T, D, R = 262144, 256, 128
+    qkv, qw, kw, cs, pos = _make(T, 16, 8, 8, D, R, torch.float16, seed=93)
+    out = qkv.clone()
+    K.qk_norm_rope_packed_ex(out, 16, 8, 8, D, 1e-6, qw, kw, cs, False, pos,
+                             rotary_dim=R)
+    torch.cuda.synchronize()
+    _check_slices(qkv, out, 16, 8, 8, D, R, False, True, qw, kw, cs, pos,
+                  "T=262144 D=256 fp16")
+
+
+@pytest.mark.timeout(300)
+def test_capped_launch_at_the_threshold():
+    # D=64: 24 heads per wave, so one wave per token; 131072 waves and more
+    # take the occupancy cap.  A ragged count just past it.
+    T, D, R = 131072 + 9, 64, 32
+    qkv, qw, kw, cs, pos = _make(T, 16, 8, 8, D, R, torch.bfloat16, seed=94)
+    out = qkv.clone()
+    K.qk_norm_rope_packed_ex(out, 16, 8, 8, D, 1e-6, qw, kw, cs, True, pos,
+                             rotary_dim=R)
+    torch.cuda.synchronize()
+    _check_slices(qkv, out, 16, 8, 8, D, R, True, False, qw, kw, cs, pos,
+                  "capped T=131081 D=64 bf16")
 
 
 def test_no_rotation_ignores_positions():

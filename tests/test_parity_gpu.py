@@ -522,6 +522,24 @@ def _check_packed_slices(x, got, what, chunk=32768):
          f"largest difference {st['max_abs']:.2e}")
 
 
+@pytest.mark.timeout(300)
+@pytest.mark.parametrize("heads,T", [((8, 2, 2), 131077), ((16, 8, 8), 32771),
+                                     ((32, 4, 4), 21846), ((40, 8, 8), 16385),
+                                     ((48, 8, 8), 13108), ((100, 8, 4), 6554)])
+def test_packed_occupancy_capped_launches(heads, T):
+    # Launches large enough for the occupancy cap (blocks of one to five
+    # waves; the last mix has two blocks of five waves per token), every Q/K
+    # element against the oracle, V unchanged.
+    hq, hk, hv = heads
+    w = I.PackedWorkload("capped", T, hq, hk, hv, seed=5200 + hq)
+    _say(f"capped launch heads={heads} T={T}")
+    x = I.make_packed(w, DEV)
+    got = _run_packed(x)
+    nqk = (hq + hk) * w.head_dim
+    assert torch.equal(got[:, nqk:], x["qkv"][:, nqk:])
+    _check_packed_slices(x, got, f"capped {heads} T={T}")
+
+
 @pytest.mark.parametrize("heads", [(16, 0, 8), (0, 8, 8), (5, 3, 1), (1, 1, 0),
                                    (32, 8, 8), (40, 4, 4), (7, 6, 2), (20, 5, 0),
                                    (12, 0, 3),
