@@ -19,6 +19,7 @@
 #include <cstdint>
 
 #include "kv_quant.hpp"
+#include "occupancy.hpp"
 #include "prologue_launch.hpp"
 #include "wave_ops.hpp"
 
@@ -36,6 +37,16 @@ namespace {
 // with.
 constexpr int kWaves = 1;
 constexpr int kRowsPerWave = 2;
+
+// The RMSNorm stage caps its large launches at 16 blocks per CU (the same
+// LDS request as the packed kernels; uncapped, 32 blocks fit).  Measured on
+// MI355X with cold caches: the in-place norm of the prefill q (2097152 rows,
+// 1048576 one-wave blocks) 646.2 against 671.8 us, and the five-launch
+// pipeline 770.0 against 795.3 us; at 1024 x 64 (32768 blocks) the cap was
+// 3% slower (25.50 against 24.80 us).  The RoPE stage was slower with every
+// cap tried (111-242 against 98.1 us at prefill).
+constexpr int kNormCapBlocksPerCu = 16;
+constexpr int64_t kNormCapMinBlocks = 131072;
 
 template <int RS>
 __global__ void __launch_bounds__(kWaves * 64) rms_norm_rows_kernel(
@@ -138,9 +149,12 @@ int launch_rms_norm_rows(const uint16_t* x, uint16_t* out, const uint16_t* weigh
   const int64_t blocks = (num_rows + per_block - 1) / per_block;
   if (blocks > 0x7FFFFFFF) return FP8KV_ERR_SHAPE;
   void* args[] = {&x, &out, &weight, &num_rows, &eps};
+  const unsigned lds = blocks >= kNormCapMinBlocks
+                           ? static_cast<unsigned>(lds_for_blocks_per_cu(kNormCapBlocksPerCu))
+                           : 0u;
   return to_status(hipLaunchKernel(
       reinterpret_cast<const void*>(&rms_norm_rows_kernel<kRowsPerWave>),
-      dim3(static_cast<uint32_t>(blocks)), dim3(kWaves * 64), args, 0, stream));
+      dim3(static_cast<uint32_t>(blocks)), dim3(kWaves * 64), args, lds, stream));
 }
 
 int launch_rope_rows(uint16_t* x, const float* cos_sin, const int64_t* positions,
