@@ -22,14 +22,16 @@ namespace {
 // with 128 or 256 lanes and 6.25-6.38 with 512 or 1024.
 constexpr int kThreads = 64;
 
-// From 128 MiB up, at most 25 blocks per CU (the uncapped launch holds 32).
-// Measured on MI355X with cold caches, uncapped against capped: in-place RMW
-// 43.20 / 42.79, 82.49 / 81.19, 161.04 / 158.86, 634.4 / 620.7 and 2537 / 2473
-// us over 128 MiB, 256 MiB, 512 MiB, 2 GiB and 8 GiB; copy 43.22 / 42.76,
-// 82.63 / 81.49, 322.1 / 316.2 and 1280.5 / 1254.5 us over 128 MiB, 256 MiB,
-// 1 GiB and 4 GiB each way.  At 64 MiB both were level (23.80 / 23.80 and
-// 23.88 / 23.78 us).  21 blocks per CU was level with no cap; 18 and fewer
-// were slower.
+// The in-place RMW caps its launches from 128 MiB up at 25 blocks per CU
+// (the uncapped launch holds 32).  Measured on MI355X, uncapped against
+// capped: with cold caches 43.20 / 42.79, 82.49 / 81.19, 161.04 / 158.86,
+// 634.4 / 620.7 and 2537 / 2473 us over 128 MiB, 256 MiB, 512 MiB, 2 GiB and
+// 8 GiB (level at 64 MiB: 23.80 / 23.80); launched back to back over 2 GiB,
+// 6.74-6.82 against 6.89-6.96 TB/s.  21 blocks per CU was level with no cap,
+// 18 and fewer slower.  The copy is not capped: with cold caches the cap
+// gained 1-2% from 128 MiB up, but launched back to back, as the copy
+// ceiling of the benchmark is, it lost 2-3% (6.42-6.43 against 6.59-6.63
+// TB/s over 512 MiB each way).
 constexpr int kCapBlocksPerCu = 25;
 constexpr int64_t kCapMinBytes = int64_t{128} << 20;
 
@@ -66,8 +68,7 @@ int launch_stream_copy(void* dst, const void* src, int64_t n16, hipStream_t stre
   const u32x4_t* s = static_cast<const u32x4_t*>(src);
   void* args[] = {&d, &s, &n16};
   return hipLaunchKernel(reinterpret_cast<const void*>(&stream_copy_kernel),
-                         dim3(blocks), dim3(kThreads), args, cap_lds(n16 * 16),
-                         stream) == hipSuccess
+                         dim3(blocks), dim3(kThreads), args, 0, stream) == hipSuccess
              ? FP8KV_OK
              : FP8KV_ERR_LAUNCH;
 }

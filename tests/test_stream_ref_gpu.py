@@ -18,8 +18,7 @@ def _bytes(n, seed):
     return torch.randint(0, 256, (n,), dtype=torch.uint8, generator=g, device=DEV)
 
 
-# 8_388_608 vectors (128 MiB) and more take the occupancy cap
-@pytest.mark.parametrize("n16", [1, 255, 256, 257, 4097, 100_003, 8_388_611])
+@pytest.mark.parametrize("n16", [1, 255, 256, 257, 4097, 100_003])
 def test_copy_exact_with_guards(n16):
     src = _bytes(n16 * 16 + 64, n16)
     dst = torch.full((n16 * 16 + 64,), 0x5A, dtype=torch.uint8, device=DEV)
@@ -30,6 +29,7 @@ def test_copy_exact_with_guards(n16):
     assert bool((dst[:32] == 0x5A).all()) and bool((dst[32 + n16 * 16:] == 0x5A).all())
 
 
+# 8_388_608 vectors (128 MiB) and more take the occupancy cap
 @pytest.mark.parametrize("n16", [1, 257, 100_003, 8_388_608])
 def test_rmw_exact_with_guards(n16):
     buf = _bytes(n16 * 16 + 64, 7 + n16)
