@@ -101,3 +101,38 @@ def test_packed_and_read_side():
         assert torch.equal(pout, ref_pout)
         assert torch.equal(sout.view(torch.int16), ref_sout.view(torch.int16))
         assert torch.equal(spout.view(torch.int16), ref_spout.view(torch.int16))
+
+
+def test_occupancy_capped_launches():
+    # Launches large enough for the occupancy cap (their LDS request is a
+    # launch parameter of the captured node): the packed kernel at 32771
+    # tokens of 16/8/8 heads and the variants kernel at 131081 tokens of
+    # head_dim 64, in one graph.
+    pw = I.PackedWorkload("capped", 32771, seed=77)
+    px = I.make_packed(pw, DEV)
+    qkv = px["qkv"].clone()
+    g0 = torch.Generator(device=DEV)
+    g0.manual_seed(78)
+    T = 131072 + 9
+    ex_in = torch.randn((T, 32 * 64), generator=g0, device=DEV).to(torch.float16)
+    ex = ex_in.clone()
+    ew = (torch.rand(64, generator=g0, device=DEV) + 0.5).to(torch.float16)
+    ecs = I.cos_sin_cache(4096, 64, device=DEV)
+    epos = torch.randint(0, 4096, (T,), generator=g0, device=DEV)
+
+    def run():
+        K.qk_norm_rope_packed(qkv, pw.num_heads_q, pw.num_heads_k, pw.num_heads_v,
+                              pw.head_dim, pw.eps, px["q_weight"], px["k_weight"],
+                              px["cos_sin_cache"], True, px["position_ids"])
+        K.qk_norm_rope_packed_ex(ex, 16, 8, 8, 64, 1e-6, ew, ew, ecs, False, epos)
+    run()
+    ref_qkv, ref_ex = qkv.clone(), ex.clone()
+    g = _capture(run)
+    for _ in range(REPLAYS):
+        qkv.copy_(px["qkv"])
+        ex.copy_(ex_in)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(qkv, ref_qkv)
+        assert torch.equal(ex.view(torch.int16), ref_ex.view(torch.int16))
