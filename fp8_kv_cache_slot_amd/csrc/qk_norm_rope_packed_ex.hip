@@ -70,60 +70,20 @@ __device__ __forceinline__ float head_sum(float v) {
   return v;
 }
 
-template <int D, bool FP16, bool NEOX, int WAVES, int U>
-__global__ void __launch_bounds__(WAVES * 64) qk_norm_rope_packed_ex_kernel(
-    uint16_t* __restrict__ qkv, const uint16_t* __restrict__ q_weight,
-    const uint16_t* __restrict__ k_weight, const float* __restrict__ cos_sin,
-    const int64_t* __restrict__ position_ids, int32_t num_heads_q,
-    int32_t num_heads_k, int32_t row_elems, int32_t rotary_dim,
-    int32_t waves_per_token, int32_t num_waves, int64_t max_position,
-    float eps) {
-  constexpr int LPH = D / 8;   // lanes per head
-  constexpr int HPW = 64 / LPH;  // heads per wave access
-  const int lane = lane_id();
-  const int32_t wv = static_cast<int32_t>(blockIdx.x) * WAVES + wave_id();
-  if (wv >= num_waves) return;
-  const int32_t t = wv / waves_per_token;
-  const int32_t h0 = (wv - t * waves_per_token) * U * HPW;  // first head of the wave
-  const int g = lane / LPH;    // head slot within an access
-  const int lh = lane % LPH;   // lane within the head: dims 8lh .. 8lh+7
-  const int32_t nh = num_heads_q + num_heads_k;
-  uint16_t* base = qkv + static_cast<int64_t>(t) * row_elems + lh * 8;
-
-  // Load order: the U head loads, both weight vectors, then the position and
-  // (depending on it) the cos/sin row, with nothing between them that waits.
-  // A weight of a group without heads may be null, so that group borrows the
-  // other pointer (Hq + Hk >= 1).  Every lane loads cos/sin, at offset 0
-  // outside the rotary dims, behind a test of rotary_dim > 0 only (uniform),
-  // and selects afterwards.  (Branches around the weight loads and around
-  // the cos/sin loads of the rotary lanes each added a wait for every
-  // outstanding load; a branch on the wave's first access holding a head,
-  // which it always does, let hipcc sink the head loads below the position's
-  // round trip.)  A position out of range makes the token's stores, not an
-  // early return, conditional; its cos/sin reads use row 0.  Heads past the
-  // last one re-read head 0 (in bounds) and are not stored.
-  u32x4_t x[U];
-#pragma unroll
-  for (int u = 0; u < U; ++u) {
-    const int32_t h = h0 + u * HPW + g;
-    x[u] = load16<true>(base + static_cast<int64_t>(h < nh ? h : 0) * D);
-  }
-  const u32x4_t wqr = load16<false>((num_heads_q > 0 ? q_weight : k_weight) + lh * 8);
-  const u32x4_t wkr = load16<false>((num_heads_k > 0 ? k_weight : q_weight) + lh * 8);
-  __builtin_amdgcn_sched_barrier(0);  // keep the position load after these
-  const int64_t pos_in = position_ids[t];
-  // Without rotary dims no table row is read, so every token is stored.
-  const bool in_range = pos_in >= 0 && pos_in < max_position;
-  const bool valid = in_range || rotary_dim == 0;
-  const int64_t pos = in_range ? pos_in : 0;
-
-  // Rotation coefficients of this lane: identity outside the rotary dims.
+// Rotation coefficients of one lane (lh: its lane within the head) from the
+// token's cos/sin row (R/2 cosines, then R/2 sines), in global memory or in
+// LDS: identity outside the rotary dims.  Returns the ds_bpermute byte
+// address of the lane's NeoX partner (its own lane otherwise).  Every lane
+// reads, at offset 0 outside the rotary dims, behind a test of
+// rotary_dim > 0 only (uniform), and selects afterwards: a branch around the
+// rotary lanes' reads added a wait for every outstanding load.
+template <bool NEOX>
+__device__ __forceinline__ int rotation_coefficients(const float* row, int rotary_dim,
+                                                     int lh, int lane, float* c, float* s) {
   const int rot_lanes = rotary_dim / 8;
   const bool rotary = lh < rot_lanes;
-  float c[8], s[8];
   int partner = lane;
   const int half = rotary_dim / 2;
-  const float* row = cos_sin + pos * rotary_dim;
   if constexpr (NEOX) {
     // dims 8lh.. pair with dims 8lh +- R/2, R/16 lanes away; the first half
     // takes n c - n' s, the second half n c + n' s.  i0 <= R/2 - 8, so every
@@ -158,8 +118,18 @@ __global__ void __launch_bounds__(WAVES * 64) qk_norm_rope_packed_ex_kernel(
       s[2 * k + 1] = rotary ? ss[k] : 0.0f;
     }
   }
-  const int partner_addr = partner * 4;  // ds_bpermute byte address
+  return partner * 4;
+}
 
+// RMSNorm, weight and rotation of a wave's U accesses (heads h0 + u*HPW + g),
+// stored in place where the token is valid and the head exists.
+template <int D, bool FP16, bool NEOX, int U>
+__device__ __forceinline__ void normalise_rotate_store(
+    const u32x4_t* x, u32x4_t wqr, u32x4_t wkr, const float* c, const float* s,
+    int partner_addr, uint16_t* base, int32_t h0, int g, int32_t num_heads_q,
+    int32_t nh, bool valid, float eps) {
+  constexpr int LPH = D / 8;
+  constexpr int HPW = 64 / LPH;
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     const int32_t h = h0 + u * HPW + g;
@@ -195,6 +165,120 @@ __global__ void __launch_bounds__(WAVES * 64) qk_norm_rope_packed_ex_kernel(
   }
 }
 
+// One wave per block.  Load order: the U head loads, both weight vectors,
+// then the position and (depending on it) the cos/sin row, with nothing
+// between them that waits.  A weight of a group without heads may be null,
+// so that group borrows the other pointer (Hq + Hk >= 1).  (A branch on the
+// wave's first access holding a head, which it always does, let hipcc sink
+// the head loads below the position's round trip.)  A position out of range
+// makes the token's stores, not an early return, conditional; its cos/sin
+// reads use row 0.  Heads past the last one re-read head 0 (in bounds) and
+// are not stored.
+template <int D, bool FP16, bool NEOX, int U>
+__global__ void __launch_bounds__(64) qk_norm_rope_packed_ex_kernel(
+    uint16_t* __restrict__ qkv, const uint16_t* __restrict__ q_weight,
+    const uint16_t* __restrict__ k_weight, const float* __restrict__ cos_sin,
+    const int64_t* __restrict__ position_ids, int32_t num_heads_q,
+    int32_t num_heads_k, int32_t row_elems, int32_t rotary_dim,
+    int32_t waves_per_token, int32_t num_waves, int64_t max_position,
+    float eps) {
+  constexpr int LPH = D / 8;   // lanes per head
+  constexpr int HPW = 64 / LPH;  // heads per wave access
+  const int lane = lane_id();
+  const int32_t wv = static_cast<int32_t>(blockIdx.x);
+  if (wv >= num_waves) return;
+  const int32_t t = wv / waves_per_token;
+  const int32_t h0 = (wv - t * waves_per_token) * U * HPW;  // first head of the wave
+  const int g = lane / LPH;    // head slot within an access
+  const int lh = lane % LPH;   // lane within the head: dims 8lh .. 8lh+7
+  const int32_t nh = num_heads_q + num_heads_k;
+  uint16_t* base = qkv + static_cast<int64_t>(t) * row_elems + lh * 8;
+
+  u32x4_t x[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int32_t h = h0 + u * HPW + g;
+    x[u] = load16<true>(base + static_cast<int64_t>(h < nh ? h : 0) * D);
+  }
+  const u32x4_t wqr = load16<false>((num_heads_q > 0 ? q_weight : k_weight) + lh * 8);
+  const u32x4_t wkr = load16<false>((num_heads_k > 0 ? k_weight : q_weight) + lh * 8);
+  __builtin_amdgcn_sched_barrier(0);  // keep the position load after these
+  const int64_t pos_in = position_ids[t];
+  // Without rotary dims no table row is read, so every token is stored.
+  const bool in_range = pos_in >= 0 && pos_in < max_position;
+  const bool valid = in_range || rotary_dim == 0;
+  const int64_t pos = in_range ? pos_in : 0;
+  float c[8], s[8];
+  const int partner_addr =
+      rotation_coefficients<NEOX>(cos_sin + pos * rotary_dim, rotary_dim, lh, lane, c, s);
+  normalise_rotate_store<D, FP16, NEOX, U>(x, wqr, wkr, c, s, partner_addr, base, h0, g,
+                                           num_heads_q, nh, valid, eps);
+}
+
+// A token's waves as one block (a token with more than kExMaxBlockWaves
+// waves takes several blocks).  The block's first wave reads the position
+// and requests the token's rotary row (R floats, up to 1 KiB) before its own
+// head loads, writes it to LDS and the block meets at one barrier; the other
+// waves go straight to their head loads.  No wave returns early.  The
+// arguments a wave needs before its first loads come first, inside the
+// argument dwords the build preloads into SGPRs.
+template <int D, bool FP16, bool NEOX, int U>
+__global__ void __launch_bounds__(512) qk_norm_rope_packed_ex_token_kernel(
+    uint16_t* __restrict__ qkv, const float* __restrict__ cos_sin,
+    const int64_t* __restrict__ position_ids, int32_t num_heads_q,
+    int32_t num_heads_k, int32_t row_elems, int32_t rotary_dim,
+    int32_t blocks_per_token, int32_t waves_per_block,
+    const uint16_t* __restrict__ q_weight, const uint16_t* __restrict__ k_weight,
+    int64_t max_position, float eps) {
+  constexpr int LPH = D / 8;
+  constexpr int HPW = 64 / LPH;
+  __shared__ f32x4_t cs_lds[64];  // the token's row: R/2 cosines, R/2 sines
+  __shared__ int32_t valid_lds;
+  const int lane = lane_id();
+  const int wave = wave_id();
+  const int32_t t = blocks_per_token == 1
+                        ? static_cast<int32_t>(blockIdx.x)
+                        : static_cast<int32_t>(blockIdx.x) / blocks_per_token;
+  const int32_t part = static_cast<int32_t>(blockIdx.x) - t * blocks_per_token;
+  const int32_t h0 = (part * waves_per_block + wave) * U * HPW;
+  const int g = lane / LPH;
+  const int lh = lane % LPH;
+  const int32_t nh = num_heads_q + num_heads_k;
+  uint16_t* base = qkv + static_cast<int64_t>(t) * row_elems + lh * 8;
+
+  f32x4_t row_v = {0.f, 0.f, 0.f, 0.f};
+  bool valid0 = false;
+  if (wave == 0) {
+    const int64_t pos_in = position_ids[t];
+    const bool in_range = pos_in >= 0 && pos_in < max_position;
+    valid0 = in_range || rotary_dim == 0;
+    const int64_t pos = in_range ? pos_in : 0;
+    if (lane * 4 < rotary_dim) row_v = load16f(cos_sin + pos * rotary_dim + lane * 4);
+  }
+  __builtin_amdgcn_sched_barrier(0);  // the head loads after these
+
+  u32x4_t x[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int32_t h = h0 + u * HPW + g;
+    x[u] = load16<true>(base + static_cast<int64_t>(h < nh ? h : 0) * D);
+  }
+  const u32x4_t wqr = load16<false>((num_heads_q > 0 ? q_weight : k_weight) + lh * 8);
+  const u32x4_t wkr = load16<false>((num_heads_k > 0 ? k_weight : q_weight) + lh * 8);
+  __builtin_amdgcn_sched_barrier(0);
+  if (wave == 0) {
+    if (lane * 4 < rotary_dim) cs_lds[lane] = row_v;
+    if (lane == 0) valid_lds = valid0 ? 1 : 0;
+  }
+  __syncthreads();
+  const bool valid = valid_lds != 0;
+  float c[8], s[8];
+  const int partner_addr = rotation_coefficients<NEOX>(
+      reinterpret_cast<const float*>(cs_lds), rotary_dim, lh, lane, c, s);
+  normalise_rotate_store<D, FP16, NEOX, U>(x, wqr, wkr, c, s, partner_addr, base, h0, g,
+                                           num_heads_q, nh, valid, eps);
+}
+
 // One wave per block, three accesses (3 KiB) per wave, as for the guarded
 // kernel.  Measured on MI355X with cold caches at 8192 tokens of 16/8/8
 // heads: D=64 interleaved fp16 14.3 us, D=256 NeoX R=128 bf16 41.8 us, D=128
@@ -204,7 +288,6 @@ __global__ void __launch_bounds__(WAVES * 64) qk_norm_rope_packed_ex_kernel(
 // 24.9 us; four waves per block: 14.4 / 41.2 / 24.2 us.  Those figures
 // predate the load order above, which took the three forms from 14.2 / 41.8
 // / 23.1 us to 13.6 / 37.7 / 22.2 us.
-constexpr int kExWaves = 1;
 constexpr int kExUnroll = 3;
 
 // Occupancy cap for large launches: at most 16 one-wave blocks per CU from
@@ -217,6 +300,24 @@ constexpr int kExUnroll = 3;
 constexpr int kExCapBlocksPerCu = 16;
 constexpr int64_t kExCapMinWaves = 131072;
 
+// The token-block form is used when a token spans two waves or more and the
+// whole launch fits on the chip at once (at most 8192 waves).  Measured on
+// MI355X with cold caches, against the one-wave form, outputs identical
+// (us, one-wave / token blocks): 16/8/8 heads, D=256 NeoX R=128 at 1024 /
+// 2048 tokens 9.24 / 8.56 and 13.88 / 12.58; D=128 interleaved at 3072 /
+// 4096 tokens 11.16 / 10.44 and 13.56 / 12.32; D=128 NeoX R=64 fp16 at 3072
+// tokens 11.68 / 10.62; 32/8/0 heads, D=128 NeoX R=64 fp16 at 1024 / 2048
+// tokens 9.16 / 8.42 and 12.60 / 11.08; D=64 at 4096 tokens 12.14 / 11.32.
+// Below the limit it was never slower by more than 1%.  Beyond it: 1-3%
+// faster for some forms and up to 5% slower for others (D=128 interleaved
+// at 6144 / 8192 tokens 17.42 / 18.24 and 21.40 / 22.42), and a token of
+// one wave gains nothing from sharing (D=64 with 16/8/8 heads: 2-5% slower
+// at 2048-6144 tokens).
+constexpr int kExMaxBlockWaves = 8;
+constexpr int64_t kExTokenBlockMaxWaves = 8192;
+
+static_assert(sizeof(f32x4_t) * 64 + sizeof(int32_t) <= 64 * 1024, "LDS row");
+
 template <int D, bool FP16, bool NEOX>
 int launch_ex(const PackedExArgs& a, hipStream_t stream) {
   constexpr int kHeadsPerWave = kExUnroll * (512 / D);
@@ -225,27 +326,49 @@ int launch_ex(const PackedExArgs& a, hipStream_t stream) {
   if (waves_per_token < 1) waves_per_token = 1;
   const int64_t waves = static_cast<int64_t>(a.num_tokens) * waves_per_token;
   if (waves > 0x7FFFFFFF) return FP8KV_ERR_SHAPE;
-  int32_t num_waves = static_cast<int32_t>(waves);
-  const int64_t blocks = (waves + kExWaves - 1) / kExWaves;
-  void* args[] = {const_cast<uint16_t**>(&a.qkv),
-                  const_cast<const uint16_t**>(&a.q_weight),
-                  const_cast<const uint16_t**>(&a.k_weight),
-                  const_cast<const float**>(&a.cos_sin),
-                  const_cast<const int64_t**>(&a.position_ids),
-                  const_cast<int32_t*>(&a.num_heads_q),
-                  const_cast<int32_t*>(&a.num_heads_k),
-                  const_cast<int32_t*>(&a.row_elems),
-                  const_cast<int32_t*>(&a.rotary_dim),
-                  &waves_per_token, &num_waves,
-                  const_cast<int64_t*>(&a.max_position),
-                  const_cast<float*>(&a.eps)};
-  hipError_t err = hipLaunchKernel(
-      reinterpret_cast<const void*>(
-          &qk_norm_rope_packed_ex_kernel<D, FP16, NEOX, kExWaves, kExUnroll>),
-      dim3(static_cast<uint32_t>(blocks)), dim3(kExWaves * 64), args,
-      waves >= kExCapMinWaves ? static_cast<unsigned>(lds_for_blocks_per_cu(kExCapBlocksPerCu))
-                              : 0u,
-      stream);
+  hipError_t err;
+  if (waves_per_token >= 2 && waves <= kExTokenBlockMaxWaves) {
+    int32_t blocks_per_token = (waves_per_token + kExMaxBlockWaves - 1) / kExMaxBlockWaves;
+    int32_t waves_per_block = (waves_per_token + blocks_per_token - 1) / blocks_per_token;
+    const int64_t blocks = static_cast<int64_t>(a.num_tokens) * blocks_per_token;
+    void* args[] = {const_cast<uint16_t**>(&a.qkv),
+                    const_cast<const float**>(&a.cos_sin),
+                    const_cast<const int64_t**>(&a.position_ids),
+                    const_cast<int32_t*>(&a.num_heads_q),
+                    const_cast<int32_t*>(&a.num_heads_k),
+                    const_cast<int32_t*>(&a.row_elems),
+                    const_cast<int32_t*>(&a.rotary_dim),
+                    &blocks_per_token, &waves_per_block,
+                    const_cast<const uint16_t**>(&a.q_weight),
+                    const_cast<const uint16_t**>(&a.k_weight),
+                    const_cast<int64_t*>(&a.max_position),
+                    const_cast<float*>(&a.eps)};
+    err = hipLaunchKernel(
+        reinterpret_cast<const void*>(
+            &qk_norm_rope_packed_ex_token_kernel<D, FP16, NEOX, kExUnroll>),
+        dim3(static_cast<uint32_t>(blocks)), dim3(waves_per_block * 64), args, 0, stream);
+  } else {
+    int32_t num_waves = static_cast<int32_t>(waves);
+    void* args[] = {const_cast<uint16_t**>(&a.qkv),
+                    const_cast<const uint16_t**>(&a.q_weight),
+                    const_cast<const uint16_t**>(&a.k_weight),
+                    const_cast<const float**>(&a.cos_sin),
+                    const_cast<const int64_t**>(&a.position_ids),
+                    const_cast<int32_t*>(&a.num_heads_q),
+                    const_cast<int32_t*>(&a.num_heads_k),
+                    const_cast<int32_t*>(&a.row_elems),
+                    const_cast<int32_t*>(&a.rotary_dim),
+                    &waves_per_token, &num_waves,
+                    const_cast<int64_t*>(&a.max_position),
+                    const_cast<float*>(&a.eps)};
+    err = hipLaunchKernel(
+        reinterpret_cast<const void*>(&qk_norm_rope_packed_ex_kernel<D, FP16, NEOX, kExUnroll>),
+        dim3(static_cast<uint32_t>(waves)), dim3(64), args,
+        waves >= kExCapMinWaves
+            ? static_cast<unsigned>(lds_for_blocks_per_cu(kExCapBlocksPerCu))
+            : 0u,
+        stream);
+  }
   return err == hipSuccess ? FP8KV_OK : FP8KV_ERR_LAUNCH;
 }
 

@@ -209,3 +209,53 @@ def test_rejects_and_out_of_range_positions():
     keep = torch.tensor([0, 1, 2, 4], device=DEV)
     _check(qkv[keep].contiguous(), out[keep].contiguous(), 4, 2, 2, 64, 32, False,
            torch.float16, qw, kw, cs, pos[keep].contiguous(), "in-range tokens")
+
+
+# (D, heads, T): a token spans two waves or more, so a launch of at most
+# 8192 waves takes the token-block form (the first wave of a token's block
+# shares the rotary row through LDS) and one of more takes the one-wave
+# form.  T and T + 1 straddle that limit; 100/8/4 heads of 256 are 18 waves,
+# three blocks of six per token.
+BOUNDARY = [(128, (16, 8, 8), 4096), (256, (16, 8, 8), 2048), (64, (40, 8, 8), 4096),
+            (256, (100, 8, 4), 455)]
+
+
+@pytest.mark.timeout(300)
+@pytest.mark.parametrize("D,heads,T", BOUNDARY, ids=[f"D{b[0]}-{b[1][0]}q" for b in BOUNDARY])
+def test_both_forms_at_the_token_block_limit(D, heads, T):
+    hq, hk, hv = heads
+    for n in (T, T + 1):
+        for neox, dtype in ((True, torch.bfloat16), (False, torch.float16)):
+            R = D // 2
+            qkv, qw, kw, cs, pos = _make(n, hq, hk, hv, D, R, dtype, seed=D + n + neox)
+            pos[n // 2] = cs.shape[0]       # one token out of range: left as it was
+            out = qkv.clone()
+            K.qk_norm_rope_packed_ex(out, hq, hk, hv, D, 1e-6, qw, kw, cs, neox, pos,
+                                     rotary_dim=R)
+            torch.cuda.synchronize()
+            assert torch.equal(out[n // 2], qkv[n // 2])
+            keep = torch.cat([torch.arange(0, n // 2), torch.arange(n // 2 + 1, n)]).to(DEV)
+            _check(qkv[keep].contiguous(), out[keep].contiguous(), hq, hk, hv, D, R, neox,
+                   dtype, qw, kw, cs, pos[keep].contiguous(),
+                   f"D={D} heads={heads} T={n} neox={neox} {dtype}")
+
+
+@pytest.mark.parametrize("D,heads,T", BOUNDARY, ids=[f"D{b[0]}-{b[1][0]}q" for b in BOUNDARY])
+def test_result_does_not_depend_on_the_form(D, heads, T):
+    # The same tokens through the one-wave form (a launch of T + 1 tokens,
+    # over the limit) and the token-block form (the first T tokens alone):
+    # bit-identical, for every pairing, rotary width and dtype.
+    hq, hk, hv = heads
+    for R in (D, D // 2, 16):
+        for neox in (True, False):
+            for dtype in (torch.bfloat16, torch.float16):
+                qkv, qw, kw, cs, pos = _make(T + 1, hq, hk, hv, D, R, dtype, seed=D + R)
+                big = qkv.clone()
+                K.qk_norm_rope_packed_ex(big, hq, hk, hv, D, 1e-6, qw, kw, cs, neox, pos,
+                                         rotary_dim=R)
+                small = qkv[:T].clone()
+                K.qk_norm_rope_packed_ex(small, hq, hk, hv, D, 1e-6, qw, kw, cs, neox,
+                                         pos[:T].contiguous(), rotary_dim=R)
+                torch.cuda.synchronize()
+                assert torch.equal(small.view(torch.int16), big[:T].view(torch.int16)), \
+                    f"D={D} heads={heads} R={R} neox={neox} {dtype}"
