@@ -11,9 +11,12 @@
 //
 // Layout of the work.  A head is D/8 lanes of one 16-byte vector each, so a
 // wave covers 512/D heads per access.  A token's Q and K heads are split over
-// waves of U accesses each (U * 512/D heads), one wave per block; a wave
-// issues its U loads before it reads the token's position, so every wave
-// waits for one memory round trip, not one per batch of heads.  The sum of
+// waves of U accesses each (U * 512/D heads).  Large launches put one wave in
+// a block, and each wave issues its U loads before it reads the token's
+// position, so it waits for one memory round trip, not one per batch of
+// heads.  Launches that fit on the chip at once put a token's waves in one
+// block whose first wave fetches the position and rotary row for all of them
+// (the token-block form below); both forms run the same arithmetic.  The sum of
 // squares is reduced over the head's lanes (DPP row steps, plus one lane
 // shuffle across rows for D = 256).  Interleaved pairs sit inside a lane;
 // a NeoX partner sits R/16 lanes away within the head and arrives through
