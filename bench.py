@@ -722,14 +722,15 @@ def main():
                 extra[name]["oracle"] = oracle_beside(pk_run, pw.num_tokens)
             log(f"{name}: {extra[name]}")
             del px, qkv, q_out, k_out
-        # packed variants the guarded fast path does not cover
-        for label, D, R, neox, dt in [("packed_ex_d64_inter_f16", 64, 64, False, torch.float16),
-                                      ("packed_ex_d256_neox_r128_bf16", 256, 128, True,
-                                       torch.bfloat16)]:
+        # packed variants the guarded fast path does not cover, at 8192 tokens
+        # (one wave per block) and at 2048 (a token's four waves in one block)
+        for label, D, R, neox, dt, T in [
+                ("packed_ex_d64_inter_f16", 64, 64, False, torch.float16, 8192),
+                ("packed_ex_d256_neox_r128_bf16", 256, 128, True, torch.bfloat16, 8192),
+                ("packed_ex_d256_neox_r128_bf16_t2048", 256, 128, True, torch.bfloat16, 2048)]:
             g = torch.Generator(device=dev)
             g.manual_seed(D + R)
             hq, hk, hv = 16, 8, 8
-            T = 8192
             vq = torch.randn((T, (hq + hk + hv) * D), generator=g, device=dev).to(dt)
             vw = (torch.rand(D, generator=g, device=dev) + 0.5).to(dt)
             vcs = I.cos_sin_cache(8192, R, device=dev)
