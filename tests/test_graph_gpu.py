@@ -103,7 +103,7 @@ def test_packed_and_read_side():
         assert torch.equal(spout.view(torch.int16), ref_spout.view(torch.int16))
 
 
-def test_occupancy_capped_launches():
+def test_capped_and_token_block_launches():
     # Launches large enough for the occupancy cap (their LDS request is a
     # launch parameter of the captured node): the packed kernel at 32771
     # tokens of 16/8/8 heads and the variants kernel at 131081 tokens of
@@ -120,19 +120,31 @@ def test_occupancy_capped_launches():
     ecs = I.cos_sin_cache(4096, 64, device=DEV)
     epos = torch.randint(0, 4096, (T,), generator=g0, device=DEV)
 
+    # and the variants kernel's token-block form (a small launch whose
+    # tokens span several waves: head_dim 256, three blocks per token)
+    sm_in = torch.randn((37, 112 * 256), generator=g0, device=DEV).to(torch.bfloat16)
+    sm = sm_in.clone()
+    sw = (torch.rand(256, generator=g0, device=DEV) + 0.5).to(torch.bfloat16)
+    scs = I.cos_sin_cache(4096, 128, device=DEV)
+    spos = torch.randint(0, 4096, (37,), generator=g0, device=DEV)
+
     def run():
         K.qk_norm_rope_packed(qkv, pw.num_heads_q, pw.num_heads_k, pw.num_heads_v,
                               pw.head_dim, pw.eps, px["q_weight"], px["k_weight"],
                               px["cos_sin_cache"], True, px["position_ids"])
         K.qk_norm_rope_packed_ex(ex, 16, 8, 8, 64, 1e-6, ew, ew, ecs, False, epos)
+        K.qk_norm_rope_packed_ex(sm, 100, 8, 4, 256, 1e-6, sw, sw, scs, True, spos,
+                                 rotary_dim=128)
     run()
-    ref_qkv, ref_ex = qkv.clone(), ex.clone()
+    ref_qkv, ref_ex, ref_sm = qkv.clone(), ex.clone(), sm.clone()
     g = _capture(run)
     for _ in range(REPLAYS):
         qkv.copy_(px["qkv"])
         ex.copy_(ex_in)
+        sm.copy_(sm_in)
         torch.cuda.synchronize()
         g.replay()
         torch.cuda.synchronize()
         assert torch.equal(qkv, ref_qkv)
         assert torch.equal(ex.view(torch.int16), ref_ex.view(torch.int16))
+        assert torch.equal(sm.view(torch.int16), ref_sm.view(torch.int16))
