@@ -722,6 +722,24 @@ def main():
                 extra[name]["oracle"] = oracle_beside(pk_run, pw.num_tokens)
             log(f"{name}: {extra[name]}")
             del px, qkv, q_out, k_out
+        # packed at long-prefill token counts, where launches of 65536 waves
+        # and more run occupancy-capped (7 two-wave blocks per CU)
+        for T, seed in ((32768, 1064), (131072, 1074)):
+            lw = I.PackedWorkload(f"packed_t{T}", T, seed=seed)
+            lx = I.make_packed(lw, dev)
+            per = time_flushed(lambda: K.qk_norm_rope_packed(
+                lx["qkv"], lw.num_heads_q, lw.num_heads_k, lw.num_heads_v, lw.head_dim,
+                lw.eps, lx["q_weight"], lx["k_weight"], lx["cos_sin_cache"], True,
+                lx["position_ids"]), 20, 3)
+            m = statistics.median(per)
+            nb = A.packed_bytes(T, lw.num_heads_q, lw.num_heads_k, lw.head_dim)
+            extra[lw.name] = {"tokens": T, "heads": "16q/8k/8v x 128", "bytes": nb,
+                              "median_us": round(m * 1e6, 2),
+                              "min_us": round(min(per) * 1e6, 2),
+                              "gbps": round(nb / m / 1e9, 1)}
+            annotate(extra[lw.name], nb, m, "rmw")
+            log(f"{lw.name}: {extra[lw.name]}")
+            del lx
         # packed variants the guarded fast path does not cover, at 8192 tokens
         # (one wave per block) and at 2048 (a token's four waves in one block)
         for label, D, R, neox, dt, T in [
