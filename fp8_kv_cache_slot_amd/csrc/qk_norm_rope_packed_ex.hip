@@ -282,6 +282,74 @@ __global__ void __launch_bounds__(512) qk_norm_rope_packed_ex_token_kernel(
                                            num_heads_q, nh, valid, eps);
 }
 
+// kExTokensPerBlock tokens of one wave each per block.  The block's first
+// wave reads their positions and requests their rotary rows (up to 64 floats
+// each: 16 lanes of 16 bytes per token) before its own head loads, writes
+// them to LDS, and the block meets at one barrier.  Tokens past the last one
+// re-read the last token (in bounds) and store nothing.
+constexpr int kExTokensPerBlock = 4;
+constexpr int kExTokenRowLanes = 64 / kExTokensPerBlock;  // lanes per token row
+constexpr int kExTokensMaxRotary = 4 * kExTokenRowLanes;  // floats per row
+
+template <int D, bool FP16, bool NEOX, int U>
+__global__ void __launch_bounds__(kExTokensPerBlock * 64) qk_norm_rope_packed_ex_tokens_kernel(
+    uint16_t* __restrict__ qkv, const float* __restrict__ cos_sin,
+    const int64_t* __restrict__ position_ids, int32_t num_heads_q,
+    int32_t num_heads_k, int32_t row_elems, int32_t rotary_dim, int32_t num_tokens,
+    const uint16_t* __restrict__ q_weight, const uint16_t* __restrict__ k_weight,
+    int64_t max_position, float eps) {
+  constexpr int LPH = D / 8;
+  constexpr int HPW = 64 / LPH;
+  constexpr int P = kExTokensPerBlock;
+  __shared__ f32x4_t cs_lds[P][kExTokenRowLanes];
+  __shared__ int32_t valid_lds[P];
+  const int lane = lane_id();
+  const int wave = wave_id();
+  const int32_t t0 = static_cast<int32_t>(blockIdx.x) * P;
+  const int32_t t = t0 + wave;
+  const bool real = t < num_tokens;
+  const int g = lane / LPH;
+  const int lh = lane % LPH;
+  const int32_t nh = num_heads_q + num_heads_k;
+  uint16_t* base =
+      qkv + static_cast<int64_t>(real ? t : num_tokens - 1) * row_elems + lh * 8;
+
+  // the first wave: lanes 16p .. 16p+15 fetch token t0 + p's row
+  const int rp = lane / kExTokenRowLanes, rl = lane % kExTokenRowLanes;
+  f32x4_t row_v = {0.f, 0.f, 0.f, 0.f};
+  bool valid0 = false;
+  if (wave == 0) {
+    const int32_t tp = t0 + rp < num_tokens ? t0 + rp : num_tokens - 1;
+    const int64_t pos_in = position_ids[tp];
+    const bool in_range = pos_in >= 0 && pos_in < max_position;
+    valid0 = in_range || rotary_dim == 0;
+    const int64_t pos = in_range ? pos_in : 0;
+    if (rl * 4 < rotary_dim) row_v = load16f(cos_sin + pos * rotary_dim + rl * 4);
+  }
+  __builtin_amdgcn_sched_barrier(0);  // the head loads after these
+
+  u32x4_t x[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int32_t h = u * HPW + g;
+    x[u] = load16<true>(base + static_cast<int64_t>(h < nh ? h : 0) * D);
+  }
+  const u32x4_t wqr = load16<false>((num_heads_q > 0 ? q_weight : k_weight) + lh * 8);
+  const u32x4_t wkr = load16<false>((num_heads_k > 0 ? k_weight : q_weight) + lh * 8);
+  __builtin_amdgcn_sched_barrier(0);
+  if (wave == 0) {
+    if (rl * 4 < rotary_dim) cs_lds[rp][rl] = row_v;
+    if (rl == 0) valid_lds[rp] = valid0 ? 1 : 0;
+  }
+  __syncthreads();
+  const bool valid = real && valid_lds[wave] != 0;
+  float c[8], s[8];
+  const int partner_addr = rotation_coefficients<NEOX>(
+      reinterpret_cast<const float*>(cs_lds[wave]), rotary_dim, lh, lane, c, s);
+  normalise_rotate_store<D, FP16, NEOX, U>(x, wqr, wkr, c, s, partner_addr, base, 0, g,
+                                           num_heads_q, nh, valid, eps);
+}
+
 // One wave per block, three accesses (3 KiB) per wave, as for the guarded
 // kernel.  Measured on MI355X with cold caches at 8192 tokens of 16/8/8
 // heads: D=64 interleaved fp16 14.3 us, D=256 NeoX R=128 bf16 41.8 us, D=128
@@ -303,19 +371,27 @@ constexpr int kExUnroll = 3;
 constexpr int kExCapBlocksPerCu = 16;
 constexpr int64_t kExCapMinWaves = 131072;
 
-// The token-block form is used when a token spans two waves or more and the
-// whole launch fits on the chip at once (at most 8192 waves).  Measured on
-// MI355X with cold caches, against the one-wave form, outputs identical
-// (us, one-wave / token blocks): 16/8/8 heads, D=256 NeoX R=128 at 1024 /
-// 2048 tokens 9.24 / 8.56 and 13.88 / 12.58; D=128 interleaved at 3072 /
-// 4096 tokens 11.16 / 10.44 and 13.56 / 12.32; D=128 NeoX R=64 fp16 at 3072
-// tokens 11.68 / 10.62; 32/8/0 heads, D=128 NeoX R=64 fp16 at 1024 / 2048
-// tokens 9.16 / 8.42 and 12.60 / 11.08; D=64 at 4096 tokens 12.14 / 11.32.
-// Below the limit it was never slower by more than 1%.  Beyond it: 1-3%
-// faster for some forms and up to 5% slower for others (D=128 interleaved
-// at 6144 / 8192 tokens 17.42 / 18.24 and 21.40 / 22.42), and a token of
-// one wave gains nothing from sharing (D=64 with 16/8/8 heads: 2-5% slower
-// at 2048-6144 tokens).
+// Launches that fit on the chip at once (at most 8192 waves) share each
+// token's position and rotary-row fetch within a block: a token's waves in
+// one block when it spans two waves or more, four one-wave tokens per block
+// with NeoX pairs (rotary rows of up to 64 floats).  Measured on MI355X with cold
+// caches, against the one-wave form, outputs identical (us):
+//   token blocks: 16/8/8 heads, D=256 NeoX R=128 at 1024 / 2048 tokens 9.24 /
+//   8.56 and 13.88 / 12.58; D=128 interleaved at 3072 / 4096 tokens 11.16 /
+//   10.44 and 13.56 / 12.32; 32/8/0 heads, D=128 NeoX R=64 fp16 at 1024 /
+//   2048 tokens 9.16 / 8.42 and 12.60 / 11.08.  Never more than 1% slower
+//   below the limit; beyond it 1-3% faster for some forms and up to 5% slower
+//   for others (D=128 interleaved at 6144 / 8192 tokens 17.42 / 18.24 and
+//   21.40 / 22.42).  A token of one wave alone in a block gained nothing
+//   (2-5% slower at D=64 with 16/8/8 heads).
+//   four tokens per block, NeoX pairs: 16/8/8 heads, D=64 R=32 at 4096 /
+//   6144 / 8192 tokens 9.18 / 8.38, 11.42 / 10.10 and 13.80 / 11.72; D=64
+//   R=64 fp16 at 5120 / 6144 tokens 10.00 / 9.48 and 11.50 / 10.28; 8/2/2
+//   heads, D=128 R=64 at 4096 / 8192 tokens 8.76 / 8.20 and 12.60 / 11.24;
+//   never more than 2% slower below the limit.  With interleaved pairs it was mixed (D=64
+//   fp16: 3-7% faster at 8192 tokens, 2-7% slower at 4096-5120), so
+//   interleaved one-wave tokens keep one-wave blocks.  Two tokens per block
+//   gained less.
 constexpr int kExMaxBlockWaves = 8;
 constexpr int64_t kExTokenBlockMaxWaves = 8192;
 
@@ -330,7 +406,26 @@ int launch_ex(const PackedExArgs& a, hipStream_t stream) {
   const int64_t waves = static_cast<int64_t>(a.num_tokens) * waves_per_token;
   if (waves > 0x7FFFFFFF) return FP8KV_ERR_SHAPE;
   hipError_t err;
-  if (waves_per_token >= 2 && waves <= kExTokenBlockMaxWaves) {
+  if (NEOX && waves_per_token == 1 && waves <= kExTokenBlockMaxWaves &&
+      a.rotary_dim <= kExTokensMaxRotary) {
+    int32_t num_tokens = a.num_tokens;
+    const int64_t blocks = (waves + kExTokensPerBlock - 1) / kExTokensPerBlock;
+    void* args[] = {const_cast<uint16_t**>(&a.qkv),
+                    const_cast<const float**>(&a.cos_sin),
+                    const_cast<const int64_t**>(&a.position_ids),
+                    const_cast<int32_t*>(&a.num_heads_q),
+                    const_cast<int32_t*>(&a.num_heads_k),
+                    const_cast<int32_t*>(&a.row_elems),
+                    const_cast<int32_t*>(&a.rotary_dim), &num_tokens,
+                    const_cast<const uint16_t**>(&a.q_weight),
+                    const_cast<const uint16_t**>(&a.k_weight),
+                    const_cast<int64_t*>(&a.max_position),
+                    const_cast<float*>(&a.eps)};
+    err = hipLaunchKernel(
+        reinterpret_cast<const void*>(
+            &qk_norm_rope_packed_ex_tokens_kernel<D, FP16, NEOX, kExUnroll>),
+        dim3(static_cast<uint32_t>(blocks)), dim3(kExTokensPerBlock * 64), args, 0, stream);
+  } else if (waves_per_token >= 2 && waves <= kExTokenBlockMaxWaves) {
     int32_t blocks_per_token = (waves_per_token + kExMaxBlockWaves - 1) / kExMaxBlockWaves;
     int32_t waves_per_block = (waves_per_token + blocks_per_token - 1) / blocks_per_token;
     const int64_t blocks = static_cast<int64_t>(a.num_tokens) * blocks_per_token;

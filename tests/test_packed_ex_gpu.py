@@ -211,13 +211,15 @@ def test_rejects_and_out_of_range_positions():
            torch.float16, qw, kw, cs, pos[keep].contiguous(), "in-range tokens")
 
 
-# (D, heads, T): a token spans two waves or more, so a launch of at most
-# 8192 waves takes the token-block form (the first wave of a token's block
-# shares the rotary row through LDS) and one of more takes the one-wave
-# form.  T and T + 1 straddle that limit; 100/8/4 heads of 256 are 18 waves,
-# three blocks of six per token.
+# (D, heads, T): a launch of at most 8192 waves shares each token's rotary
+# row through LDS (a token's waves in one block, or four one-wave tokens per
+# block), one of more takes the one-wave form.  T and T + 1 straddle that
+# limit; 100/8/4 heads of 256 are 18 waves, three blocks of six per token.
 BOUNDARY = [(128, (16, 8, 8), 4096), (256, (16, 8, 8), 2048), (64, (40, 8, 8), 4096),
-            (256, (100, 8, 4), 455)]
+            (256, (100, 8, 4), 455),
+            # one-wave tokens: four to a block below the limit (rotary rows of
+            # up to 64 floats), one-wave blocks above it
+            (64, (16, 8, 8), 8192), (128, (8, 2, 2), 8192)]
 
 
 @pytest.mark.timeout(300)
