@@ -15,8 +15,9 @@
 // a block, and each wave issues its U loads before it reads the token's
 // position, so it waits for one memory round trip, not one per batch of
 // heads.  Launches that fit on the chip at once put a token's waves in one
-// block whose first wave fetches the position and rotary row for all of them
-// (the token-block form below); both forms run the same arithmetic.  The sum of
+// block, or four one-wave tokens in one block, whose first wave fetches the
+// positions and rotary rows for all of them (the forms below); every form
+// runs the same arithmetic.  The sum of
 // squares is reduced over the head's lanes (DPP row steps, plus one lane
 // shuffle across rows for D = 256).  Interleaved pairs sit inside a lane;
 // a NeoX partner sits R/16 lanes away within the head and arrives through

@@ -128,6 +128,10 @@ def test_capped_and_token_block_launches():
     scs = I.cos_sin_cache(4096, 128, device=DEV)
     spos = torch.randint(0, 4096, (37,), generator=g0, device=DEV)
 
+    # and four one-wave tokens per block (head_dim 64, NeoX, 37 tokens)
+    fo_in = torch.randn((37, 32 * 64), generator=g0, device=DEV).to(torch.float16)
+    fo = fo_in.clone()
+
     def run():
         K.qk_norm_rope_packed(qkv, pw.num_heads_q, pw.num_heads_k, pw.num_heads_v,
                               pw.head_dim, pw.eps, px["q_weight"], px["k_weight"],
@@ -135,16 +139,19 @@ def test_capped_and_token_block_launches():
         K.qk_norm_rope_packed_ex(ex, 16, 8, 8, 64, 1e-6, ew, ew, ecs, False, epos)
         K.qk_norm_rope_packed_ex(sm, 100, 8, 4, 256, 1e-6, sw, sw, scs, True, spos,
                                  rotary_dim=128)
+        K.qk_norm_rope_packed_ex(fo, 16, 8, 8, 64, 1e-6, ew, ew, ecs, True, spos)
     run()
-    ref_qkv, ref_ex, ref_sm = qkv.clone(), ex.clone(), sm.clone()
+    ref_qkv, ref_ex, ref_sm, ref_fo = qkv.clone(), ex.clone(), sm.clone(), fo.clone()
     g = _capture(run)
     for _ in range(REPLAYS):
         qkv.copy_(px["qkv"])
         ex.copy_(ex_in)
         sm.copy_(sm_in)
+        fo.copy_(fo_in)
         torch.cuda.synchronize()
         g.replay()
         torch.cuda.synchronize()
         assert torch.equal(qkv, ref_qkv)
         assert torch.equal(ex.view(torch.int16), ref_ex.view(torch.int16))
         assert torch.equal(sm.view(torch.int16), ref_sm.view(torch.int16))
+        assert torch.equal(fo.view(torch.int16), ref_fo.view(torch.int16))
