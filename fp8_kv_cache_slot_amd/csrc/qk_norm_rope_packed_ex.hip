@@ -283,17 +283,15 @@ __global__ void __launch_bounds__(512) qk_norm_rope_packed_ex_token_kernel(
                                            num_heads_q, nh, valid, eps);
 }
 
-// kExTokensPerBlock tokens of one wave each per block.  The block's first
-// wave reads their positions and requests their rotary rows (up to 64 floats
-// each: 16 lanes of 16 bytes per token) before its own head loads, writes
+// P tokens of one wave each per block (P = 2 or 4).  The block's first wave
+// reads their positions and requests their rotary rows (up to 64 floats
+// each, 64/P lanes of 16 bytes per token) before its own head loads, writes
 // them to LDS, and the block meets at one barrier.  Tokens past the last one
 // re-read the last token (in bounds) and store nothing.
-constexpr int kExTokensPerBlock = 4;
-constexpr int kExTokenRowLanes = 64 / kExTokensPerBlock;  // lanes per token row
-constexpr int kExTokensMaxRotary = 4 * kExTokenRowLanes;  // floats per row
+constexpr int kExTokensMaxRotary = 64;  // floats per row
 
-template <int D, bool FP16, bool NEOX, int U>
-__global__ void __launch_bounds__(kExTokensPerBlock * 64) qk_norm_rope_packed_ex_tokens_kernel(
+template <int D, bool FP16, bool NEOX, int U, int P>
+__global__ void __launch_bounds__(P * 64) qk_norm_rope_packed_ex_tokens_kernel(
     uint16_t* __restrict__ qkv, const float* __restrict__ cos_sin,
     const int64_t* __restrict__ position_ids, int32_t num_heads_q,
     int32_t num_heads_k, int32_t row_elems, int32_t rotary_dim, int32_t num_tokens,
@@ -301,8 +299,9 @@ __global__ void __launch_bounds__(kExTokensPerBlock * 64) qk_norm_rope_packed_ex
     int64_t max_position, float eps) {
   constexpr int LPH = D / 8;
   constexpr int HPW = 64 / LPH;
-  constexpr int P = kExTokensPerBlock;
-  __shared__ f32x4_t cs_lds[P][kExTokenRowLanes];
+  constexpr int RL = 64 / P;  // lanes per token row
+  static_assert(RL * 4 >= kExTokensMaxRotary, "a row must fit its lanes");
+  __shared__ f32x4_t cs_lds[P][RL];
   __shared__ int32_t valid_lds[P];
   const int lane = lane_id();
   const int wave = wave_id();
@@ -315,8 +314,8 @@ __global__ void __launch_bounds__(kExTokensPerBlock * 64) qk_norm_rope_packed_ex
   uint16_t* base =
       qkv + static_cast<int64_t>(real ? t : num_tokens - 1) * row_elems + lh * 8;
 
-  // the first wave: lanes 16p .. 16p+15 fetch token t0 + p's row
-  const int rp = lane / kExTokenRowLanes, rl = lane % kExTokenRowLanes;
+  // the first wave: lanes RL*p .. RL*p + RL-1 fetch token t0 + p's row
+  const int rp = lane / RL, rl = lane % RL;
   f32x4_t row_v = {0.f, 0.f, 0.f, 0.f};
   bool valid0 = false;
   if (wave == 0) {
@@ -389,10 +388,15 @@ constexpr int64_t kExCapMinWaves = 131072;
 //   6144 / 8192 tokens 9.18 / 8.38, 11.42 / 10.10 and 13.80 / 11.72; D=64
 //   R=64 fp16 at 5120 / 6144 tokens 10.00 / 9.48 and 11.50 / 10.28; 8/2/2
 //   heads, D=128 R=64 at 4096 / 8192 tokens 8.76 / 8.20 and 12.60 / 11.24;
-//   never more than 2% slower below the limit.  With interleaved pairs it was mixed (D=64
-//   fp16: 3-7% faster at 8192 tokens, 2-7% slower at 4096-5120), so
-//   interleaved one-wave tokens keep one-wave blocks.  Two tokens per block
-//   gained less.
+//   never more than 2% slower below the limit.
+//   two tokens per block, interleaved pairs in bf16 (three runs each):
+//   16/8/8 heads, D=64 R=64 at 2048 / 6144 / 8192 tokens 6.80-7.16 /
+//   6.62-6.64, 10.92-11.00 / 10.14-10.36 and 13.18-13.30 / 12.60-12.72; D=64
+//   R=32 at 6144 tokens 10.72-10.94 / 9.94-10.10; 8/2/2 heads, D=128 R=64 at
+//   6144 tokens 10.18-10.44 / 9.52-9.56; never more than 0.6% slower.  Four
+//   per block was better at 8192 tokens but up to 3% slower at 2048-4096.
+//   With interleaved pairs in fp16 both were mixed (D=64 R=64: 4% slower to
+//   5% faster), so those tokens keep one-wave blocks.
 constexpr int kExMaxBlockWaves = 8;
 constexpr int64_t kExTokenBlockMaxWaves = 8192;
 
@@ -407,26 +411,33 @@ int launch_ex(const PackedExArgs& a, hipStream_t stream) {
   const int64_t waves = static_cast<int64_t>(a.num_tokens) * waves_per_token;
   if (waves > 0x7FFFFFFF) return FP8KV_ERR_SHAPE;
   hipError_t err;
-  if (NEOX && waves_per_token == 1 && waves <= kExTokenBlockMaxWaves &&
-      a.rotary_dim <= kExTokensMaxRotary) {
-    int32_t num_tokens = a.num_tokens;
-    const int64_t blocks = (waves + kExTokensPerBlock - 1) / kExTokensPerBlock;
-    void* args[] = {const_cast<uint16_t**>(&a.qkv),
-                    const_cast<const float**>(&a.cos_sin),
-                    const_cast<const int64_t**>(&a.position_ids),
-                    const_cast<int32_t*>(&a.num_heads_q),
-                    const_cast<int32_t*>(&a.num_heads_k),
-                    const_cast<int32_t*>(&a.row_elems),
-                    const_cast<int32_t*>(&a.rotary_dim), &num_tokens,
-                    const_cast<const uint16_t**>(&a.q_weight),
-                    const_cast<const uint16_t**>(&a.k_weight),
-                    const_cast<int64_t*>(&a.max_position),
-                    const_cast<float*>(&a.eps)};
-    err = hipLaunchKernel(
-        reinterpret_cast<const void*>(
-            &qk_norm_rope_packed_ex_tokens_kernel<D, FP16, NEOX, kExUnroll>),
-        dim3(static_cast<uint32_t>(blocks)), dim3(kExTokensPerBlock * 64), args, 0, stream);
-  } else if (waves_per_token >= 2 && waves <= kExTokenBlockMaxWaves) {
+  // one-wave tokens per block: four with NeoX pairs, two with interleaved
+  // pairs in bf16, none with interleaved pairs in fp16
+  constexpr int kTokensPerBlock = NEOX ? 4 : (FP16 ? 1 : 2);
+  if constexpr (kTokensPerBlock > 1) {
+    if (waves_per_token == 1 && waves <= kExTokenBlockMaxWaves &&
+        a.rotary_dim <= kExTokensMaxRotary) {
+      int32_t num_tokens = a.num_tokens;
+      const int64_t blocks = (waves + kTokensPerBlock - 1) / kTokensPerBlock;
+      void* args[] = {const_cast<uint16_t**>(&a.qkv),
+                      const_cast<const float**>(&a.cos_sin),
+                      const_cast<const int64_t**>(&a.position_ids),
+                      const_cast<int32_t*>(&a.num_heads_q),
+                      const_cast<int32_t*>(&a.num_heads_k),
+                      const_cast<int32_t*>(&a.row_elems),
+                      const_cast<int32_t*>(&a.rotary_dim), &num_tokens,
+                      const_cast<const uint16_t**>(&a.q_weight),
+                      const_cast<const uint16_t**>(&a.k_weight),
+                      const_cast<int64_t*>(&a.max_position),
+                      const_cast<float*>(&a.eps)};
+      err = hipLaunchKernel(
+          reinterpret_cast<const void*>(
+              &qk_norm_rope_packed_ex_tokens_kernel<D, FP16, NEOX, kExUnroll, kTokensPerBlock>),
+          dim3(static_cast<uint32_t>(blocks)), dim3(kTokensPerBlock * 64), args, 0, stream);
+      return err == hipSuccess ? FP8KV_OK : FP8KV_ERR_LAUNCH;
+    }
+  }
+  if (waves_per_token >= 2 && waves <= kExTokenBlockMaxWaves) {
     int32_t blocks_per_token = (waves_per_token + kExMaxBlockWaves - 1) / kExMaxBlockWaves;
     int32_t waves_per_block = (waves_per_token + blocks_per_token - 1) / blocks_per_token;
     const int64_t blocks = static_cast<int64_t>(a.num_tokens) * blocks_per_token;

@@ -217,8 +217,9 @@ def test_rejects_and_out_of_range_positions():
 # limit; 100/8/4 heads of 256 are 18 waves, three blocks of six per token.
 BOUNDARY = [(128, (16, 8, 8), 4096), (256, (16, 8, 8), 2048), (64, (40, 8, 8), 4096),
             (256, (100, 8, 4), 455),
-            # one-wave tokens: four to a block below the limit (rotary rows of
-            # up to 64 floats), one-wave blocks above it
+            # one-wave tokens below the limit (rotary rows of up to 64
+            # floats): four to a block with NeoX pairs, two with interleaved
+            # pairs in bf16, one-wave blocks with interleaved pairs in fp16
             (64, (16, 8, 8), 8192), (128, (8, 2, 2), 8192)]
 
 
@@ -227,7 +228,8 @@ BOUNDARY = [(128, (16, 8, 8), 4096), (256, (16, 8, 8), 2048), (64, (40, 8, 8), 4
 def test_both_forms_at_the_token_block_limit(D, heads, T):
     hq, hk, hv = heads
     for n in (T, T + 1):
-        for neox, dtype in ((True, torch.bfloat16), (False, torch.float16)):
+        for neox, dtype in ((True, torch.bfloat16), (False, torch.float16),
+                            (False, torch.bfloat16)):
             R = D // 2
             qkv, qw, kw, cs, pos = _make(n, hq, hk, hv, D, R, dtype, seed=D + n + neox)
             pos[n // 2] = cs.shape[0]       # one token out of range: left as it was
