@@ -66,7 +66,7 @@ inline int validate_packed(const void* qkv, int64_t num_tokens,
                            int32_t forced_token_heads_per_warp,
                            int64_t max_position) {
   if (num_tokens < 0 || num_heads_q < 0 || num_heads_k < 0 ||
-      num_heads_v < 0 || num_heads_q + num_heads_k < 1 || max_position < 1)
+      num_heads_v < 0 || int64_t{num_heads_q} + num_heads_k < 1 || max_position < 1)
     return FP8KV_ERR_SHAPE;
   if (head_dim != kPackedHeadDim || is_neox != 1 ||
       forced_token_heads_per_warp != -1)
@@ -95,7 +95,7 @@ inline int validate_packed_ex(const void* qkv, int64_t num_tokens,
                               const int64_t* position_ids, int32_t rotary_dim,
                               int32_t dtype, int64_t max_position) {
   if (num_tokens < 0 || num_heads_q < 0 || num_heads_k < 0 ||
-      num_heads_v < 0 || num_heads_q + num_heads_k < 1 ||
+      num_heads_v < 0 || int64_t{num_heads_q} + num_heads_k < 1 ||
       (rotary_dim > 0 && max_position < 1))  // R = 0 indexes no table
     return FP8KV_ERR_SHAPE;
   if ((head_dim != 64 && head_dim != 128 && head_dim != 256) ||
