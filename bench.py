@@ -14,7 +14,8 @@ Prints ONE JSON line:
                of the same 512 MiB, both reported with their own ratios;
                beside them its in-place 16 B/lane read-modify-write over 2 GiB
   roofline     dominant kernel: algorithmic bytes per launch / mean launch
-               duration (HIP events on the launch stream) against 8 TB/s
+               duration (one pair of HIP events on the launch stream around
+               the timed launches) against 8 TB/s
   cpu_baseline the CPU oracle timed on a bounded token slice of the same
                workload, single-threaded (cpu_baseline_all_cores: the same
                oracle over disjoint token slices on every core of the share)
@@ -141,36 +142,30 @@ def main():
     dst = torch.empty_like(src)
     for _ in range(3):
         dst.copy_(src)
-    times = []
-    for _ in range(20):
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        dst.copy_(src)
-        e1.record(stream)
-        e1.synchronize()
-        times.append(e0.elapsed_time(e1) / 1e3)
-    d2d_gbps = 2 * n / statistics.median(times) / 1e9
-    log(f"hipMemcpyAsync D2D copy {d2d_gbps:.1f} GB/s")
-
-    def median_launch(fn, iters=20, warmup=3):
+    def back_to_back(fn, iters=20, warmup=3):
+        """Mean seconds per call of `iters` back-to-back calls, from one pair
+        of events on the launch stream around all of them (an event pair
+        around every call adds its own few microseconds to each)."""
         for _ in range(warmup):
             fn()
-        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for _ in range(iters)]
-        for a, b in ev:
-            a.record(stream)
-            fn()
-            b.record(stream)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
-        return statistics.median(a.elapsed_time(b) / 1e3 for a, b in ev)
+        a.record(stream)
+        for _ in range(iters):
+            fn()
+        b.record(stream)
+        b.synchronize()
+        return a.elapsed_time(b) / 1e3 / iters
 
     # the same 512 MiB through the library's hand-written 16 B/lane copy, and
     # an in-place 16 B/lane read-modify-write over 2 GiB (the size and access
     # pattern of the prefill Q heads, without the arithmetic)
-    copy_gbps = 2 * n / median_launch(lambda: K.stream_copy(dst, src)) / 1e9
+    d2d_gbps = 2 * n / back_to_back(lambda: dst.copy_(src)) / 1e9
+    log(f"hipMemcpyAsync D2D copy {d2d_gbps:.1f} GB/s")
+    copy_gbps = 2 * n / back_to_back(lambda: K.stream_copy(dst, src)) / 1e9
     del src, dst
     rbuf = torch.zeros(2 ** 31, dtype=torch.uint8, device=dev)
-    rmw_gbps = 2 * rbuf.numel() / median_launch(lambda: K.stream_rmw(rbuf, 0)) / 1e9
+    rmw_gbps = 2 * rbuf.numel() / back_to_back(lambda: K.stream_rmw(rbuf, 0)) / 1e9
     del rbuf
     log(f"16 B/lane copy kernel {copy_gbps:.1f} GB/s, in-place RMW {rmw_gbps:.1f} GB/s")
     # The D2D-copy ceiling of the metric: the faster of the two measured
@@ -315,33 +310,33 @@ def main():
         return A.dsv4_bytes(w.num_tokens, w.num_heads, written)
 
     def time_launches(fn, steps, warmup):
-        """Run warmup untimed launches, then `steps` launches bracketed by a
-        synchronize on both sides; each launch between its own pair of events
-        on the launch stream.  Returns (total seconds, per-launch seconds)."""
+        """Run warmup untimed launches, then `steps` back-to-back launches
+        bracketed by a synchronize on both sides and by one pair of events on
+        the launch stream.  Returns (total wall seconds, mean seconds per
+        launch from the events).  An event pair around every launch would
+        add about 7 us to each 680 us step and 2-3 us to each launch's own
+        interval, so the events bracket the whole timed region instead."""
         for _ in range(warmup):
             fn()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
-        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for _ in range(steps)]
         t0 = time.perf_counter()
-        for a, b in ev:
-            a.record(stream)
+        a.record(stream)
+        for _ in range(steps):
             fn()
-            b.record(stream)
+        b.record(stream)
         torch.cuda.synchronize()
         total = time.perf_counter() - t0
-        per = [a.elapsed_time(b) / 1e3 for a, b in ev]
-        return total, per
+        return total, a.elapsed_time(b) / 1e3 / steps
 
     # ---- headline: prefill 32768 x 64 ---------------------------------------
     w = I.DSV4_WORKLOADS["prefill"]
     x = I.make_dsv4(w, dev)
     q, cache, scale = x["q"].clone(), x["kv_cache"].clone(), x["kv_scale"].clone()
     nbytes = workload_bytes(w, x)
-    total, per = time_launches(lambda: call(x, q, cache, scale), args.steps,
-                               args.warmup)
+    total, mean_launch = time_launches(lambda: call(x, q, cache, scale), args.steps,
+                                       args.warmup)
     value = nbytes * args.steps / total / 1e9
-    mean_launch = sum(per) / len(per)
     achieved = nbytes / mean_launch / 1e9
     log(f"prefill: {value:.1f} GB/s whole-job, kernel {achieved:.1f} GB/s "
         f"({mean_launch * 1e6:.1f} us/launch), {value / ceiling_gbps:.3f} of the "
@@ -392,7 +387,8 @@ def main():
             "traffic": traffic,
             "kernel": "dsv4_prologue_kernel<{}, {}, false>".format(*K.get_tiling()),
             "mean_launch_us": round(mean_launch * 1e6, 2),
-            "median_launch_us": round(statistics.median(per) * 1e6, 2),
+            "timing": "one pair of HIP events on the launch stream around the "
+                      "timed back-to-back launches; mean = their interval / steps",
         },
     }
     # ---- the same call as five separate launches (the unfused baseline) ----
