@@ -214,8 +214,9 @@ int launch(const PrologueArgs& a, hipStream_t stream) {
 // Instantiated (waves per block, Q heads per wave) shapes.  (1, 1) is the
 // small-batch kernel: one head per 64-lane block.
 int launch_prologue(const PrologueArgs& a, int waves, int qs, hipStream_t stream) {
-  // The scalar-scale cache convention is built for the small-batch shape and
-  // the default tiled shape only.
+  // The scalar-scale cache convention is built in two shapes only: one head
+  // per one-wave block (the small-batch and default tiled shape), and 4 waves
+  // x 2 heads, which every other tiling selects.
   if (a.scalar) {
     if (waves == 1 && qs == 1) return launch<1, 1, true>(a, stream);
     return launch<4, 2, true>(a, stream);

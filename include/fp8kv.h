@@ -374,8 +374,9 @@ int64_t fp8kv_get_dispatch_threshold(void);
  * Tiling of the tiled prologue kernel: waves (of 64 lanes) per block and
  * Q slots per wave.  The built-in default (1, 1) is the measured best on
  * MI355X and equals the small-batch shape; the other instantiated shapes
- * exist for measurement.  (0, 0) restores the
- * default.  Returns FP8KV_ERR_UNSUPPORTED, and changes nothing, for a shape
+ * exist for measurement (the scalar-scale prologue is built in two shapes:
+ * (1, 1), and (4, 2), which it runs under any other tiling).  (0, 0) restores
+ * the default.  Returns FP8KV_ERR_UNSUPPORTED, and changes nothing, for a shape
  * that is not built.  Process-wide.
  */
 int fp8kv_set_tiling(int32_t waves_per_block, int32_t slots_per_wave);
