@@ -22,9 +22,12 @@ from oracle import build as obuild
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 SRC = os.path.join(ROOT, "oracle", "oracle.cpp")
+# test_oracle_sanitized.py builds the tree's own oracle source, not a mutant,
+# so it is not one of the pins run against each mutant.
 PIN_FILES = sorted(os.path.relpath(p, ROOT) for p in
                    glob.glob(os.path.join(ROOT, "tests", "test_oracle_*.py"))
-                   if not p.endswith("test_oracle_mutations.py"))
+                   if not p.endswith(("test_oracle_mutations.py",
+                                      "test_oracle_sanitized.py")))
 
 # (name, text in oracle.cpp, replacement); each text occurs exactly once.
 MUTATIONS = [
@@ -229,6 +232,50 @@ MUTATIONS = [
      "        double b = oracle_bf16_to_double(xh[i + half]);",
      "        double a = oracle_bf16_to_double(xh[2 * i]);\n"
      "        double b = oracle_bf16_to_double(xh[2 * i + 1]);"),
+    ("q_not_rotated",
+     "      for (int i = 0; i < kRopeDim / 2; ++i)\n"
+     "        rotate_pair(&y[kRopeStart + 2 * i], &y[kRopeStart + 2 * i + 1],\n"
+     "                    cosv[i], sinv[i]);\n"
+     "      for (int d = 0; d < kHeadDim; ++d) qh[d] = oracle_bf16_rne(y[d]);\n"
+     "    }\n\n    // KV",
+     "      for (int i = 0; i < 0; ++i)\n"
+     "        rotate_pair(&y[kRopeStart + 2 * i], &y[kRopeStart + 2 * i + 1],\n"
+     "                    cosv[i], sinv[i]);\n"
+     "      for (int d = 0; d < kHeadDim; ++d) qh[d] = oracle_bf16_rne(y[d]);\n"
+     "    }\n\n    // KV"),
+    ("skipped_token_skips_q",
+     "    const float* sinv = row + kRopeDim / 2;\n\n    // Q:",
+     "    const float* sinv = row + kRopeDim / 2;\n    if (slot_mapping[t] < 0) continue;\n\n    // Q:"),
+    ("packed_normalises_v",
+     "    for (int32_t h = 0; h < num_heads_q + num_heads_k; ++h) {\n"
+     "      uint16_t* xh = qkv + t * row_elems + static_cast<int64_t>(h) * head_dim;\n"
+     "      const uint16_t* w = h < num_heads_q ? q_weight : k_weight;\n"
+     "      rms_norm(xh, w, head_dim, eps, y);",
+     "    for (int32_t h = 0; h < num_heads_q + num_heads_k + num_heads_v; ++h) {\n"
+     "      uint16_t* xh = qkv + t * row_elems + static_cast<int64_t>(h) * head_dim;\n"
+     "      const uint16_t* w = h < num_heads_q ? q_weight : k_weight;\n"
+     "      rms_norm(xh, w, head_dim, eps, y);"),
+    ("packed_ex_normalises_v",
+     "    for (int32_t h = 0; h < num_heads_q + num_heads_k; ++h) {\n"
+     "      uint16_t* xh = qkv + t * row_elems + static_cast<int64_t>(h) * head_dim;\n"
+     "      const uint16_t* w = h < num_heads_q ? q_weight : k_weight;\n"
+     "      // RMSNorm over the whole head",
+     "    for (int32_t h = 0; h < num_heads_q + num_heads_k + num_heads_v; ++h) {\n"
+     "      uint16_t* xh = qkv + t * row_elems + static_cast<int64_t>(h) * head_dim;\n"
+     "      const uint16_t* w = h < num_heads_q ? q_weight : k_weight;\n"
+     "      // RMSNorm over the whole head"),
+    ("packed_ex_fp16_output_as_bf16",
+     "    return is_fp16 ? oracle_fp16_rne(v) : oracle_bf16_rne(v);",
+     "    return oracle_bf16_rne(v);"),
+    ("dequant_invalid_row_kept",
+     "    for (int d = 0; d < kHeadDim; ++d) dst[d] = 0;\n    return;",
+     "    return;"),
+    ("scalar_dequant_invalid_row_kept",
+     "      for (int d = 0; d < kHeadDim; ++d) dst[d] = 0;\n      continue;",
+     "      continue;"),
+    ("paged_invalid_page_row_skipped",
+     "      row_fn(slot, row);",
+     "      if (slot >= 0) row_fn(slot, row);"),
     ("quant_insert_stage_bound",
      "    if (slot < 0 || slot >= num_slots) continue;\n    for (int d = 0; d < kHeadDim; ++d) y[d]",
      "    if (slot < 0 || slot >= num_slots - 1) continue;\n    for (int d = 0; d < kHeadDim; ++d) y[d]"),
