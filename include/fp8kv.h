@@ -97,10 +97,11 @@ enum fp8kv_status {
  *                  and >= 0 (FP8KV_ERR_VALUE otherwise).  With eps = 0 an
  *                  all-zero head is 0/0 and its outputs are NaN.
  * The elements of q, kv, the weights and the table rows are finite
- * (precondition, not checked).  A NaN or an infinity makes the outputs of its
- * head unspecified (NaN, or zero where an infinite mean square scales finite
- * elements to 0), and in the KV head also its exponents and codes; no other
- * head or token is affected.
+ * (precondition, not checked).  A NaN or an infinity in q or kv makes the
+ * outputs of its own head unspecified (NaN, or zero where an infinite mean
+ * square scales finite elements to 0), and in the KV head also its exponents
+ * and codes; no other head or token is affected.  One in a weight or a table
+ * row does the same to every head that uses it.
  *
  * Per token t, for each Q head and then for the KV head x (with its weight w):
  *   y_d = x_d / sqrt(mean_d(x_d^2) + eps) * w_d            (fp32)
@@ -171,8 +172,9 @@ int qnorm_rope_kv_quant_insert_scalar_scale(
  *   out_i = n_i cos_i - n_{i+D/2} sin_i,  out_{i+D/2} = n_{i+D/2} cos_i + n_i sin_i
  * so the partner element enters the rotation with its own weight (the page's
  * paired-weight rule).  Outputs are rounded to bf16 (nearest even).  Inputs
- * are finite (precondition, as for the prologue: a non-finite element makes
- * only its own head's outputs unspecified).
+ * are finite (precondition, as for the prologue: a non-finite element of qkv
+ * makes only its own head's outputs unspecified; V elements are never read,
+ * whatever their values).
  */
 int qk_norm_rope_packed(
     void* qkv, int64_t num_tokens, int32_t num_heads_q, int32_t num_heads_k,
