@@ -184,6 +184,21 @@ def test_ragged_heads_every_tiling(heads):
     K.set_tiling(0, 0)
 
 
+@pytest.mark.parametrize("heads,T", [(1, 300), (1000, 3), (4099, 2)])
+def test_many_heads(heads, T):
+    # a token spread over thousands of Q waves (and blocks), or over one
+    w = I.custom_dsv4(T, heads, seed=3200 + heads, max_position=8192)
+    x = I.make_dsv4(w, DEV)
+    h = _host(x)
+    ref = _oracle(h)
+    for wv, qs in [(1, 1), (4, 2), (16, 2), (8, 4)]:
+        _say(f"H={heads} T={T} tiling {wv}x{qs}")
+        K.set_tiling(wv, qs)
+        _compare_full(h, ref, _run(x, TILED), f"H={heads} tiling {wv}x{qs}")
+    K.set_tiling(0, 0)
+    _compare_full(h, ref, _run(x, SMALL), f"H={heads} small-batch")
+
+
 def _oracle_threads():
     return max(1, min(16, len(os.sched_getaffinity(0))))
 
