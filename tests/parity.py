@@ -5,10 +5,12 @@ bit-exact):
   * bf16 outputs (q, the rotary part of the cache, packed Q/K):
         |got - ref| <= 2^-7 |ref| + 1e-3
     and at most ``MAX_MISMATCH`` of the elements may differ in their bits at
-    all (fp32 kernel arithmetic vs double oracle only flips a rounding when the
-    value sits next to a bf16 midpoint; a wrong rounding mode would flip ~50%).
+    all (``MIN_MISMATCH`` elements are allowed whatever the size) (fp32 kernel
+    arithmetic vs double oracle only flips a rounding when the value sits next
+    to a bf16 midpoint; a wrong rounding mode would flip ~50%).
   * E4M3 codes: at most one step apart on the signed integer line
-    (sign-magnitude, +0 == -0), and at most ``MAX_MISMATCH`` differ.
+    (sign-magnitude, +0 == -0), and at most ``MAX_MISMATCH`` differ
+    (``MIN_MISMATCH`` whatever the size).
   * UE8M0 exponent bytes: bit-exact, except in a block whose oracle maximum A
     lies within 2^-18 of an exponent boundary (A / (448 2^e) > 1 - 2^-18 or
     < (1 + 2^-18) / 2): there the two exponents may differ by one and the
@@ -27,7 +29,17 @@ import numpy as np
 import oracle as O
 
 MAX_MISMATCH = 1e-3
+# The cap is a fraction meant to catch a systematic error (a wrong rounding
+# mode flips about half of the values).  Below 1 / MAX_MISMATCH values it would
+# refuse a single value whose last bit flipped within the tolerance, so an
+# array of any size may hold MIN_MISMATCH differing values.
+MIN_MISMATCH = 2
 BAND = 2.0 ** -18
+
+
+def within_cap(n_diff, n):
+    """Whether n_diff differing values of n stay under the mismatch cap."""
+    return n_diff <= max(MAX_MISMATCH * n, MIN_MISMATCH)
 
 _E4M3 = np.array([O.e4m3_decode(c) for c in range(256)], np.float64)
 
@@ -79,7 +91,8 @@ def check_bf16(got, ref, what="", stats=None):
         stats["max_steps"] = max(stats.get("max_steps", 0), int(steps.max(initial=0)))
         stats["max_abs"] = max(stats.get("max_abs", 0.0),
                                float(np.abs(g - r).max(initial=0.0)))
-    assert frac <= MAX_MISMATCH, f"{what}: {frac:.2e} of bf16 values differ in bits"
+    assert within_cap(idx.size, gr.size), (
+        f"{what}: {idx.size} of {gr.size} bf16 values ({frac:.2e}) differ in bits")
     return frac
 
 
@@ -100,8 +113,10 @@ def check_fp16(got, ref, what=""):
         raise AssertionError(
             f"{what}: {bad.sum()} fp16 values out of tolerance, e.g. at {i}: "
             f"got {g.ravel()[i]} ref {r.ravel()[i]}")
-    frac = float(np.mean(got != ref)) if got.size else 0.0
-    assert frac <= MAX_MISMATCH, f"{what}: {frac:.2e} of fp16 values differ in bits"
+    n_diff = int(np.count_nonzero(got != ref))
+    frac = n_diff / got.size if got.size else 0.0
+    assert within_cap(n_diff, got.size), (
+        f"{what}: {n_diff} of {got.size} fp16 values ({frac:.2e}) differ in bits")
     return frac
 
 
@@ -156,9 +171,7 @@ def check_cache(got_cache, got_scale, ref_cache, ref_scale, slots, y_ref,
     n_same = int(same_e.sum()) * 64
     n_diff = int(((d != 0) & same_e[:, :, None]).sum())
     stats["code_diff"] = n_diff
-    if n_same:
-        assert n_diff / n_same <= MAX_MISMATCH, (
-            f"{what}: {n_diff}/{n_same} codes differ")
+    assert within_cap(n_diff, n_same), f"{what}: {n_diff}/{n_same} codes differ"
     # blocks in the band: dequantised values against the unrounded oracle
     for (i, b) in np.argwhere(diff_e):
         deq = _E4M3[codes_g[i, b]] * 2.0 ** e_g[i, b]
@@ -173,8 +186,9 @@ def check_codes(got, ref, what=""):
     step apart on the signed line and at most MAX_MISMATCH differing."""
     d = np.abs(_signed_code(got) - _signed_code(ref))
     assert d.max(initial=0) <= 1, f"{what}: codes more than one step apart"
-    frac = float(np.mean(d != 0)) if d.size else 0.0
-    assert frac <= MAX_MISMATCH, f"{what}: {frac:.2e} of codes differ"
+    n_diff = int(np.count_nonzero(d))
+    frac = n_diff / d.size if d.size else 0.0
+    assert within_cap(n_diff, d.size), f"{what}: {n_diff} of {d.size} codes differ"
     return frac
 
 

@@ -116,3 +116,37 @@ def test_bf16_rule_statistics_and_nan():
     nan_got[3] = 0xFFC0
     with pytest.raises(AssertionError):
         P.check_bf16(nan_got, ref, "t")
+
+
+def test_mismatch_cap_on_small_arrays():
+    # A last-bit flip within the tolerance is what fp32 arithmetic against a
+    # double oracle produces near a rounding midpoint: one among 640 values
+    # (ten cache rows of rotary dims) passes, as do two; a systematic error on
+    # a small array (a third of its values flipped) still fails, and so does a
+    # 0.2% rate on a large one.
+    rng = np.random.default_rng(5)
+
+    def bf16(v):
+        return I.bits(torch.from_numpy(v.astype(np.float32)).to(torch.bfloat16)).copy()
+
+    ref = bf16(rng.normal(size=640) + 3.0)
+    for flips in (1, 2):
+        got = ref.copy()
+        got[rng.choice(640, flips, replace=False)] ^= 1
+        P.check_bf16(got, ref, "small")
+    got = ref.copy()
+    got[::3] ^= 1
+    with pytest.raises(AssertionError):
+        P.check_bf16(got, ref, "small, systematic")
+    big = bf16(rng.normal(size=100000) + 3.0)
+    got = big.copy()
+    got[::500] ^= 1
+    with pytest.raises(AssertionError):
+        P.check_bf16(got, big, "large, 0.2%")
+    codes = rng.integers(0, 0x70, 448).astype(np.uint8)
+    g = codes.copy()
+    g[[3, 200]] += 1
+    P.check_codes(g, codes, "two codes one step apart")
+    g[::4] = codes[::4] + 1
+    with pytest.raises(AssertionError):
+        P.check_codes(g, codes, "a quarter of the codes")
