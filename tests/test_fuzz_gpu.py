@@ -103,6 +103,11 @@ def test_packed_random_case(case):
     if hq + hk == 0:
         hq = 1
     T = int(rng.integers(1, 300))
+    # one case in eight launches just over 8192 waves, where the variants
+    # kernel leaves its block-sharing forms for one-wave blocks
+    if rng.random() < 0.125:
+        waves_per_token = max(1, -(-(hq + hk) // (3 * (512 // D))))
+        T = -(-8193 // waves_per_token) + int(rng.integers(0, 64))
     guarded = dtype == torch.bfloat16 and D == 128 and R == 128 and neox
     _say(f"case {case}: T={T} heads={hq},{hk},{hv} D={D} R={R} neox={neox} "
          f"{dtype} guarded={guarded}")
