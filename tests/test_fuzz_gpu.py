@@ -1,7 +1,8 @@
 """Seeded random cases against the oracle: each case draws its own sizes and
 knobs (token and head counts, cache pages, skipped and out-of-range slots,
 eps, the built tiling and the dispatch side for the fused prologue; head
-width, rotary width, pairing, dtype and head mix for the packed forms), so
+width, rotary width, pairing, dtype and head mix for the packed forms; the
+cache, slots, block tables and output layout for the read sides), so
 combinations no hand-written case names get checked too.  Every case is
 deterministic in its seed and small enough for the oracle to finish in well
 under a second.  Needs an MI355X.  FP8KV_FUZZ_CASES sets the number of
@@ -171,3 +172,63 @@ def test_packed_guarded_random_case(case):
                           I.bits(x["k_weight"]), I.bits(x["cos_sin_cache"]),
                           I.bits(pos)[keep].copy())
     P.check_bf16(got[keep][:, :n], ref[:, :n], f"guarded case {case}")
+
+
+@pytest.mark.parametrize("case", range(CASES))
+def test_read_side_random_case(case):
+    # The four read sides (slot list or block tables, blockwise or scalar
+    # scale) on random caches of 0 to 39 pages: slots and page ids past either
+    # end, sequences longer than their table row or of negative length,
+    # disjoint output ranges with gaps and rows past the output.
+    rng = np.random.default_rng(9000 + case)
+    pages = int(rng.integers(0, 40))
+    scalar = bool(rng.integers(2))
+    paged = bool(rng.integers(2))
+    s = float(rng.choice([2.0 ** -8, 0.37, 3.0, 2.0 ** 10]))
+    cache = rng.integers(0, 256, (pages, 64, 576), dtype=np.uint8)
+    codes = cache[..., :448]
+    codes[(codes & 0x7F) == 0x7F] ^= 0x01     # the writer never stores NaN codes
+    scale = rng.integers(127 - 60, 127 + 10, (pages, 64, 8), dtype=np.uint8)
+    sc = torch.tensor([s], dtype=torch.float32, device=DEV)
+
+    def d(a):
+        return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+
+    if not paged:
+        rows = int(rng.integers(1, 3000))
+        slots = rng.integers(-3, pages * 64 + 3, rows).astype(np.int64)
+        _say(f"read case {case}: pages={pages} scalar={scalar} slot list of {rows}")
+        if scalar:
+            out = K.kv_cache_gather_dequant_scalar_scale(d(cache), sc, d(slots))
+            ref = O.kv_cache_gather_dequant_scalar(cache, s, slots)
+        else:
+            out = K.kv_cache_gather_dequant(d(cache), d(scale), d(slots))
+            ref = O.kv_cache_gather_dequant(cache, scale, slots)
+    else:
+        S, M = int(rng.integers(1, 12)), int(rng.integers(1, 6))
+        table = rng.integers(-2, pages + 2, (S, M)).astype(np.int32)
+        lens = rng.integers(-1, M * 64 + 20, S).astype(np.int32)
+        gaps = np.maximum(lens, 0) + rng.integers(0, 7, S)
+        offs = (int(rng.integers(0, 5)) +
+                np.concatenate([[0], np.cumsum(gaps)[:-1]])).astype(np.int64)
+        N = max(1, int(offs[-1]) + max(int(lens[-1]), 0) - int(rng.integers(0, 3)))
+        _say(f"read case {case}: pages={pages} scalar={scalar} tables {S}x{M} N={N}")
+        ref = np.full((N, 512), 0x7777, np.uint16)
+        out = torch.full((N, 512), 0x7777, dtype=torch.int16, device=DEV).view(torch.bfloat16)
+        if scalar:
+            K.kv_cache_gather_dequant_paged_scalar_scale(d(cache), sc, d(table), d(lens),
+                                                         d(offs), out)
+            O.kv_cache_gather_dequant_paged_scalar(cache, s, table, lens, offs, ref)
+        else:
+            K.kv_cache_gather_dequant_paged(d(cache), d(scale), d(table), d(lens),
+                                            d(offs), out)
+            O.kv_cache_gather_dequant_paged(cache, scale, table, lens, offs, ref)
+    torch.cuda.synchronize()
+    got = I.bits(out)
+    if scalar:
+        # rotary bytes are copied (random here, NaN patterns included); the
+        # codes' fp32 product rounds to bf16 against one rounding from double
+        np.testing.assert_array_equal(got[:, 448:], ref[:, 448:])
+        P.check_bf16(got[:, :448], ref[:, :448], f"read case {case}")
+    else:
+        np.testing.assert_array_equal(got, ref, err_msg=f"read case {case}")
