@@ -38,14 +38,17 @@ rms_norm_heads_kernel(const uint16_t* __restrict__ x, int64_t x_token_stride,
   const int lane = lane_id();
   const int row = lane >> 4;
   const int l16 = lane & 15;
-  const int32_t g0 = static_cast<int32_t>(blockIdx.x) * 4 * U;  // < total
+  // Head indices in 32-bit unsigned arithmetic: the last block's padding can
+  // pass 2^31 - 1 when the heads in all come close to it.
+  const uint32_t total = static_cast<uint32_t>(num_heads_total);
+  const uint32_t g0 = blockIdx.x * 4u * U;  // < total
   u32x4_t v[U];
-  int32_t gh[U];
+  uint32_t gh[U];
 #pragma unroll
   for (int u = 0; u < U; ++u) {
-    gh[u] = g0 + 4 * u + row;
+    gh[u] = g0 + 4u * u + row;
     // heads past the last re-read the block's first head and are not stored
-    const uint32_t g = static_cast<uint32_t>(gh[u] < num_heads_total ? gh[u] : g0);
+    const uint32_t g = gh[u] < total ? gh[u] : g0;
     const uint32_t t = g / static_cast<uint32_t>(heads_per_token);
     const uint32_t h = g - t * static_cast<uint32_t>(heads_per_token);
     v[u] = load16<true>(x + static_cast<int64_t>(t) * x_token_stride +
@@ -62,7 +65,7 @@ rms_norm_heads_kernel(const uint16_t* __restrict__ x, int64_t x_token_stride,
     float y[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) y[j] = f[j] * r * w[j];
-    if (gh[u] < num_heads_total)
+    if (gh[u] < total)
       store16<true>(out + static_cast<int64_t>(gh[u]) * kHeadElems + l16 * 8,
                     u32x4_t{pack_bf16(y[0], y[1]), pack_bf16(y[2], y[3]),
                             pack_bf16(y[4], y[5]), pack_bf16(y[6], y[7])});
@@ -78,14 +81,15 @@ rope_neox_heads_kernel(uint16_t* __restrict__ x, const float* __restrict__ cos_s
   const int lane = lane_id();
   const int row = lane >> 4;
   const int l16 = lane & 15;
-  const int32_t g0 = static_cast<int32_t>(blockIdx.x) * 4 * U;
+  const uint32_t total = static_cast<uint32_t>(num_heads_total);
+  const uint32_t g0 = blockIdx.x * 4u * U;  // < total
   u32x4_t v[U];
-  int32_t gh[U];
+  uint32_t gh[U];
   uint32_t tok[U];
 #pragma unroll
   for (int u = 0; u < U; ++u) {
-    gh[u] = g0 + 4 * u + row;
-    const uint32_t g = static_cast<uint32_t>(gh[u] < num_heads_total ? gh[u] : g0);
+    gh[u] = g0 + 4u * u + row;
+    const uint32_t g = gh[u] < total ? gh[u] : g0;
     tok[u] = g / static_cast<uint32_t>(heads_per_token);
     v[u] = load16<true>(x + static_cast<int64_t>(g) * kHeadElems + l16 * 8);
   }
@@ -116,7 +120,7 @@ rope_neox_heads_kernel(uint16_t* __restrict__ x, const float* __restrict__ cos_s
       const float p = dpp<kDppRowRor8>(n[j]);  // partner element i +- 64
       o[j] = n[j] * c[j] + p * s[j];
     }
-    if (ok && gh[u] < num_heads_total)
+    if (ok && gh[u] < total)
       store16<true>(x + static_cast<int64_t>(gh[u]) * kHeadElems + l16 * 8,
                     u32x4_t{pack_bf16(o[0], o[1]), pack_bf16(o[2], o[3]),
                             pack_bf16(o[4], o[5]), pack_bf16(o[6], o[7])});
