@@ -130,7 +130,7 @@ __global__ void __launch_bounds__(64) kv_cache_gather_dequant_kernel(
 #pragma unroll
     for (int r = 0; r < RS; ++r) {
       const int32_t i = grp * RS + r;
-      if (i < num_rows) store16<true>(out + static_cast<int64_t>(i) * 512 + lane * 8, z);
+      if (i < num_rows) store16_nt_sc1(out + static_cast<int64_t>(i) * 512 + lane * 8, z);
     }
     return;
   }
@@ -160,7 +160,7 @@ __global__ void __launch_bounds__(64) kv_cache_gather_dequant_kernel(
     const u32x4_t o = slot_valid(s[r], num_cache_slots)
                           ? dequant_vector<SCALAR>(d.v[r], d.ev[r], fs, lane)
                           : z;
-    store16<true>(out + static_cast<int64_t>(i) * 512 + lane * 8, o);
+    store16_nt_sc1(out + static_cast<int64_t>(i) * 512 + lane * 8, o);
   }
 }
 
@@ -207,7 +207,7 @@ __global__ void __launch_bounds__(WAVES * 64) kv_cache_gather_dequant_paged_kern
     for (int r = 0; r < PRS; ++r) {
       const int64_t i = first + r;
       if (j0 + r < len && i >= 0 && i < num_rows)
-        store16<true>(out + i * 512 + lane * 8, z);
+        store16_nt_sc1(out + i * 512 + lane * 8, z);
     }
     return;
   }
@@ -226,7 +226,7 @@ __global__ void __launch_bounds__(WAVES * 64) kv_cache_gather_dequant_paged_kern
     const int64_t i = first + r;
     if (j0 + r >= len || i < 0 || i >= num_rows) continue;
     const u32x4_t o = page_ok ? dequant_vector<SCALAR>(d.v[r], d.ev[r], fs, lane) : z;
-    store16<true>(out + i * 512 + lane * 8, o);
+    store16_nt_sc1(out + i * 512 + lane * 8, o);
   }
 }
 

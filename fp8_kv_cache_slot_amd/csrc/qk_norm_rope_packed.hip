@@ -137,7 +137,7 @@ __global__ void __launch_bounds__(kMaxBlockWaves * 64) qk_norm_rope_packed_kerne
     if (valid && h < nh) {
       u32x4_t v = {pack_bf16(o[0], o[1]), pack_bf16(o[2], o[3]),
                    pack_bf16(o[4], o[5]), pack_bf16(o[6], o[7])};
-      store16<true>(base + h * 128, v);
+      store16_nt_sc1(base + h * 128, v);
     }
   }
 }

@@ -164,7 +164,7 @@ __device__ __forceinline__ void normalise_rotate_store(
     if (valid && h < nh) {
       u32x4_t v = {pack2_any<FP16>(o[0], o[1]), pack2_any<FP16>(o[2], o[3]),
                    pack2_any<FP16>(o[4], o[5]), pack2_any<FP16>(o[6], o[7])};
-      store16<true>(base + static_cast<int64_t>(h) * D, v);
+      store16_nt_sc1(base + static_cast<int64_t>(h) * D, v);
     }
   }
 }

@@ -1,7 +1,8 @@
 // Reference streaming kernels for the bandwidth ceiling the prologue is
 // measured against.  Both move 16 bytes per lane, one vector per lane, in
-// 64-lane (one-wave) blocks, with the same non-temporal load/store policy as
-// the prologue's q stream:
+// 64-lane (one-wave) blocks, with the same load and store policy as the
+// prologue's q stream (non-temporal loads, "nt sc1" stores: 1.1-1.2% faster
+// than "nt" stores for both kernels on MI355X, so the ceilings use them too):
 //   stream_copy  dst[i] = src[i]                       (read n + write n bytes)
 //   stream_rmw   buf[i] = buf[i] ^ mask, in place      (read n + write n bytes)
 // The in-place form is the access pattern of the prologue's Q heads, which
@@ -32,6 +33,8 @@ constexpr int kThreads = 64;
 // gained 1-2% from 128 MiB up, but launched back to back, as the copy
 // ceiling of the benchmark is, it lost 2-3% (6.42-6.43 against 6.59-6.63
 // TB/s over 512 MiB each way).
+// (These were measured with "nt" stores; with "nt sc1" stores the capped
+// RMW moved 6.97-6.99 TB/s back to back over 2 GiB.)
 constexpr int kCapBlocksPerCu = 25;
 constexpr int64_t kCapMinBytes = int64_t{128} << 20;
 
@@ -43,13 +46,13 @@ unsigned cap_lds(int64_t bytes) {
 __global__ void __launch_bounds__(kThreads) stream_copy_kernel(
     u32x4_t* __restrict__ dst, const u32x4_t* __restrict__ src, int64_t n16) {
   const int64_t i = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
-  if (i < n16) store16<true>(dst + i, load16<true>(src + i));
+  if (i < n16) store16_nt_sc1(dst + i, load16<true>(src + i));
 }
 
 __global__ void __launch_bounds__(kThreads) stream_rmw_kernel(
     u32x4_t* __restrict__ buf, int64_t n16, uint32_t mask) {
   const int64_t i = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
-  if (i < n16) store16<true>(buf + i, load16<true>(buf + i) ^ mask);
+  if (i < n16) store16_nt_sc1(buf + i, load16<true>(buf + i) ^ mask);
 }
 
 int grid_for(int64_t n16, uint32_t* blocks) {

@@ -110,6 +110,31 @@ __device__ __forceinline__ void store16(void* p, u32x4_t v) {
     *static_cast<u32x4_t*>(p) = v;
 }
 
+// Non-temporal 16-byte store with device scope (gfx950 cache policy "nt sc1"),
+// for the streams that write each line once.  The compiler's non-temporal
+// store builtin sets only "nt", and no builtin reaches the scope bits of a
+// global store, hence the asm (a vector store: no result, so nothing waits
+// on it; the "memory" clobber keeps its place among the other memory
+// operations).  The hardware reads a 16-byte store's data registers after
+// the store issues, so a VALU write to them must come some wait states later.
+// The compiler inserts those after its own stores (two, here), but it cannot
+// see a store inside an asm statement: without the s_nop a kernel with
+// several stores per wave overwrote a store's data before it was read (a
+// seeded packed case stored wrong values).  The s_nop 4 gives five wait
+// states in the same statement.  Measured on MI355X against "nt" alone, each
+// launch after a cache-flushing read, two runs: the prologue 673.3 -> 657.3-
+// 658.4 us at 32768 x 64 and 2703 -> 2635 us at 131072 x 64 (2.3-3.6% faster
+// from 1024 tokens up), the read sides 1-2%, the packed op 0.3-1.3% and its
+// variants 1.3-5% faster, the in-place RMW and copy references 1.1-1.2%
+// faster; "nt sc0 sc1" measured the same as "nt sc1", and "sc1" without "nt"
+// was mixed.  The prologue's KV row stores (8-byte codes, 16-byte rotary
+// part) measured 0.5-1% slower with it and keep "nt"; so do the separate-
+// launch baselines, which were 2-5% slower with it.
+__device__ __forceinline__ void store16_nt_sc1(void* p, u32x4_t v) {
+  __asm__ volatile("global_store_dwordx4 %0, %1, off nt sc1\n\ts_nop 4"
+                   : : "v"(p), "v"(v) : "memory");
+}
+
 __device__ __forceinline__ f32x4_t load16f(const float* p) {
   return *reinterpret_cast<const f32x4_t*>(p);
 }
