@@ -126,8 +126,8 @@ __device__ __forceinline__ void store16(void* p, u32x4_t v) {
 // 658.4 us at 32768 x 64 and 2703 -> 2635 us at 131072 x 64 (2.3-3.6% faster
 // from 1024 tokens up), the read sides 1-2%, the packed op 0.3-1.3% and its
 // variants 1.3-5% faster, the in-place RMW and copy references 1.1-1.2%
-// faster; "nt sc0 sc1" measured the same as "nt sc1", and "sc1" without "nt"
-// was mixed.  The prologue's KV row stores (8-byte codes, 16-byte rotary
+// faster; "nt sc0 sc1" measured the same as "nt sc1", "nt sc0" the same as
+// "nt", and "sc1" without "nt" was mixed.  The prologue's KV row stores (8-byte codes, 16-byte rotary
 // part) measured 0.5-1% slower with it and keep "nt"; so do the separate-
 // launch baselines, which were 2-5% slower with it.
 __device__ __forceinline__ void store16_nt_sc1(void* p, u32x4_t v) {
