@@ -397,7 +397,8 @@ void fp8kv_get_tiling(int32_t* waves_per_block, int32_t* slots_per_wave);
  * the rate of a plain copy on the same device; FlagGems PR #5449
  * "Performance" reports its kernel as a share of a measured copy peak).
  * Both move one 16-byte vector per lane, one 64-lane wave per block, with
- * non-temporal loads and stores; neither is part of the prologue.  From
+ * non-temporal loads and stores (the stores with device scope, as the
+ * prologue's q stores); neither is part of the prologue.  From
  * 128 MiB up the read-modify-write runs at most 25 blocks per CU (a request
  * for LDS it never uses), which measured 1-2.5% faster on MI355X; the copy
  * is never capped.
